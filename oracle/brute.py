@@ -1,0 +1,125 @@
+"""Brute-force MoE forward for tiny inputs (T <= 8), pure Python loops.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/moe_oracle.py``): used to pin the
+vectorised oracle. It imports nothing from the HIP library nor from the
+vectorised oracle.
+
+Differences from the vectorised oracle, on purpose:
+  * every dot product is an explicit Python loop over scalars;
+  * the top-k set is found by enumerating all C(E,k) expert subsets and keeping
+    the one of largest total probability (the set maximising sum g_i is the
+    top-k set of P2's ``TopK(g)`` equation); among equal totals the
+    lexicographically smallest index tuple wins, which is the lower-index tie
+    rule;
+  * expert choice enumerates all C-subsets of tokens per expert the same way.
+
+Pages cited by title as in ``oracle/moe_oracle.py``.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+
+def _dot_col(row, M, col):
+    acc = 0.0
+    for i in range(len(row)):
+        acc += float(row[i]) * float(M[i][col])
+    return acc
+
+
+def _vecmat(row, M):
+    return [_dot_col(row, M, j) for j in range(len(M[0]))]
+
+
+def _softmax(v):
+    m = max(v)
+    ex = [math.exp(a - m) for a in v]
+    s = 0.0
+    for a in ex:
+        s += a
+    return [a / s for a in ex]
+
+
+def _silu(z):
+    # z / (1 + e^-z), written to avoid overflow for very negative z
+    if z >= 0:
+        return z / (1.0 + math.exp(-z))
+    ez = math.exp(z)
+    return z * ez / (ez + 1.0)
+
+
+def expert(xrow, Wgate, Wup, Wdown):
+    """(silu(x W_gate) * (x W_up)) W_down, P1 ``Expert.forward``."""
+    g = _vecmat(xrow, Wgate)
+    u = _vecmat(xrow, Wup)
+    h = [_silu(g[i]) * u[i] for i in range(len(g))]
+    return _vecmat(h, Wdown)
+
+
+def _best_subset(values, size):
+    """Subset of ``size`` positions maximising the sum of ``values``; the sum is
+    taken over the values in ascending order so that equal multisets give equal
+    sums; ties go to the lexicographically smallest position tuple."""
+    best, best_sum = None, -math.inf
+    for comb in itertools.combinations(range(len(values)), size):
+        s = 0.0
+        for v in sorted(values[i] for i in comb):
+            s += v
+        if s > best_sum:
+            best, best_sum = comb, s
+    return list(best)
+
+
+def forward_tc(x, Wg, b, Wgate, Wup, Wdown, k, renormalize=True):
+    """Token-choice forward by literal loops. Returns dict(y, idx, w, probs)."""
+    T, E = len(x), len(Wg[0])
+    ys, idxs, ws, ps = [], [], [], []
+    for t in range(T):
+        s = _vecmat(x[t], Wg)
+        if b is not None:
+            s = [s[e] + float(b[e]) for e in range(E)]
+        p = _softmax(s)
+        chosen = _best_subset(p, k)
+        # slot order: descending probability, lower index first on ties
+        chosen.sort(key=lambda e: (-p[e], e))
+        wsel = [p[e] for e in chosen]
+        if renormalize:
+            tot = 0.0
+            for v in wsel:
+                tot += v
+            wsel = [v / tot for v in wsel]
+        y = [0.0] * len(Wdown[0][0])
+        for j, e in enumerate(chosen):
+            out = expert(x[t], Wgate[e], Wup[e], Wdown[e])
+            for c in range(len(y)):
+                y[c] += wsel[j] * out[c]
+        ys.append(y)
+        idxs.append(chosen)
+        ws.append(wsel)
+        ps.append(p)
+    return {"y": ys, "idx": idxs, "w": ws, "probs": ps}
+
+
+def forward_ec(x, Wg, b, Wgate, Wup, Wdown, cf):
+    """Expert-choice forward by literal loops. Returns dict(y, idx, w)."""
+    T, E = len(x), len(Wg[0])
+    C = int(T * cf / E)
+    logits = []
+    for t in range(T):
+        s = _vecmat(x[t], Wg)
+        if b is not None:
+            s = [s[e] + float(b[e]) for e in range(E)]
+        logits.append(s)
+    idx, score = [], []
+    ys = [[0.0] * len(Wdown[0][0]) for _ in range(T)]
+    for e in range(E):
+        col = _softmax([logits[t][e] for t in range(T)])
+        chosen = sorted(_best_subset(col, C))
+        idx.append(chosen)
+        score.append([col[t] for t in chosen])
+        for t in chosen:
+            out = expert(x[t], Wgate[e], Wup[e], Wdown[e])
+            for c in range(len(out)):
+                ys[t][c] += col[t] * out[c]
+    return {"y": ys, "idx": idx, "w": score}

@@ -1,0 +1,258 @@
+"""fp64 CPU oracle for the sparse Mixture-of-Experts layer forward.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker, not the product: only
+``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import or call it. It shares no code with the HIP library and
+imports nothing from it.
+
+Every function is the plain definition written out in NumPy float64, one step
+per statement, in the order the pages give the steps. Inputs are the exact
+values the device sees (bf16 or fp32 values widened to float64; nothing is
+re-rounded). Library routines used as steps: ``@`` (matmul), ``np.exp``,
+``np.argsort(kind="stable")``.
+
+Pages cited (by title):
+  P1 "Mixture of Experts（MoE）の理論と実装 — 条件付き計算でLLMを効率化する"
+     (classes ``Expert`` and ``MoELayer``: ``route``, ``forward``,
+     ``load_balancing_loss``)
+  P2 "MoE" primer on qiita (section "ゲート / ルーターって何者？", the four
+     router equations s = W_g x, g = softmax(s), TopK(g), y = sum g_i E_i(x))
+  P3 "Sparse Mixture of Experts(MoE) 아키텍처 심층 분석" (``SwiGLUExpert``,
+     ``TopKGating``, ``ExpertChoiceGating``, ``compute_load_balancing_loss``,
+     ``MoELayerWithAuxLoss``)
+  P5 "机器学习基础系列——混合专家模型" (``GatingNetwork`` with bias,
+     ``MixtureOfExperts`` dense mixture, ``SparseMoE``)
+
+Readings where the pages leave a step open or disagree:
+  * renormalisation: P1/P3 code renormalise the selected weights, P2's
+    equations do not; both are provided (``renormalize`` flag).
+  * ties: experts with equal probability are ordered by lower index; in
+    expert-choice mode tokens with equal score are ordered by lower token index.
+  * slot order: descending probability (P1 ``route``, P3 ``TopKGating``).
+  * f = count/T so that sum(f) = k (P1 ``load_balancing_loss``); the loss is
+    E * sum((f/k) * p), which is P3's scale (sum(f/k) = 1) and equals 1 under
+    uniform routing.
+  * expert choice: softmax over tokens of each expert's logit column, top-C
+    tokens per expert with C = floor(T*cf/E), outputs combined with the
+    selected scores and no renormalisation; a token no expert picks gets 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=F64)
+
+
+# --------------------------------------------------------------------------
+# Router (token choice)
+# --------------------------------------------------------------------------
+
+def router_logits(x, Wg, b=None):
+    """s = x W_g (+ b). P2 first router equation (written as x @ W in P1
+    ``MoELayer.route``); the optional bias is P5 ``GatingNetwork.forward``."""
+    s = _f64(x) @ _f64(Wg)
+    if b is not None:
+        s = s + _f64(b)[None, :]
+    return s
+
+
+def softmax_rows(s):
+    """g = softmax(s) over the experts of each token, shifted by the row max
+    (P1 ``MoELayer.route``; P2 second router equation)."""
+    s = _f64(s)
+    z = s - s.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk_experts(p, k):
+    """TopK(g): the k experts of largest probability per token, listed by
+    descending probability, lower expert index first among equals (P1
+    ``route``, P3 ``TopKGating``; tie order is this implementation's reading)."""
+    p = _f64(p)
+    order = np.argsort(-p, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def gate_weights(p, idx, renormalize=True):
+    """Weights of the selected experts: g_i (P2 fourth equation) or g_i divided
+    by the sum over the selected set (P1 ``route``, P3 ``TopKGating``)."""
+    sel = np.take_along_axis(_f64(p), idx, axis=1)
+    if renormalize:
+        sel = sel / sel.sum(axis=1, keepdims=True)
+    return sel
+
+
+def route_tc(x, Wg, b, k, renormalize=True):
+    """Token-choice routing: returns (idx [T,k], w [T,k], probs [T,E], logits [T,E])."""
+    s = router_logits(x, Wg, b)
+    p = softmax_rows(s)
+    idx = topk_experts(p, k)
+    w = gate_weights(p, idx, renormalize)
+    return idx, w, p, s
+
+
+def topk_margin(p, k):
+    """p_(k) - p_(k+1) per token (descending order); +inf when k equals E."""
+    p = _f64(p)
+    E = p.shape[1]
+    if k >= E:
+        return np.full(p.shape[0], np.inf)
+    ps = -np.sort(-p, axis=1)
+    return ps[:, k - 1] - ps[:, k]
+
+
+# --------------------------------------------------------------------------
+# Experts
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """silu(z) = z / (1 + exp(-z)) (P1 ``Expert.forward``)."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(X, Wgate, Wup, Wdown):
+    """E_i(x) = (silu(x W_gate) * (x W_up)) W_down for the rows of X (P1
+    ``Expert.forward`` with W1 = W_up and W2 = W_down; P3 ``SwiGLUExpert``)."""
+    X = _f64(X)
+    g = silu(X @ _f64(Wgate))
+    u = X @ _f64(Wup)
+    return (g * u) @ _f64(Wdown)
+
+
+def mix(x, idx, w, Wgate, Wup, Wdown):
+    """y_t = sum_j w[t,j] * E_{idx[t,j]}(x_t) (P2 fourth equation; P1
+    ``MoELayer.forward``). Rows of each expert are gathered and run through
+    that expert once; expert weights are widened to float64 one expert at a
+    time so that large stacks need not be held in float64 all at once."""
+    x = _f64(x)
+    idx = np.asarray(idx)
+    w = _f64(w)
+    T = x.shape[0]
+    d_out = Wdown.shape[2]
+    y = np.zeros((T, d_out), dtype=F64)
+    for e in np.unique(idx):
+        tt, jj = np.nonzero(idx == e)
+        out = expert_ffn(x[tt], Wgate[e], Wup[e], Wdown[e])
+        np.add.at(y, tt, w[tt, jj][:, None] * out)
+    return y
+
+
+def forward_tc(x, Wg, b, Wgate, Wup, Wdown, k, renormalize=True):
+    """Token-choice layer forward. Returns dict with y, idx, w, probs, logits."""
+    idx, w, p, s = route_tc(x, Wg, b, k, renormalize)
+    y = mix(x, idx, w, Wgate, Wup, Wdown)
+    return {"y": y, "idx": idx, "w": w, "probs": p, "logits": s}
+
+
+# --------------------------------------------------------------------------
+# Load-balancing statistics
+# --------------------------------------------------------------------------
+
+def expert_counts(idx, E):
+    """Number of (token, slot) assignments per expert (P1 ``load_balancing_loss``
+    dispatch count; P3 ``tokens_per_expert``)."""
+    return np.bincount(np.asarray(idx).ravel(), minlength=E).astype(np.int64)
+
+
+def aux_stats(probs, idx, E, k):
+    """f_e = count_e / T (sum f = k, P1), p_e = mean_t probs[t,e] (P1, P3),
+    loss = E * sum_e (f_e / k) * p_e (P3 ``compute_load_balancing_loss`` scale).
+    Returns (f, p, loss, counts)."""
+    probs = _f64(probs)
+    T = probs.shape[0]
+    c = expert_counts(idx, E)
+    f = c.astype(F64) / T
+    p = probs.mean(axis=0)
+    loss = E * np.sum((f / k) * p)
+    return f, p, float(loss), c
+
+
+# --------------------------------------------------------------------------
+# Expert choice
+# --------------------------------------------------------------------------
+
+def capacity(T, E, cf):
+    """C = int(T * cf / E) (P3 ``ExpertChoiceGating``)."""
+    return int(T * cf / E)
+
+
+def softmax_cols(s):
+    """Each expert's softmax over the tokens of its logit column (P3
+    ``ExpertChoiceGating``: softmax of the transposed logits)."""
+    s = _f64(s)
+    z = s - s.max(axis=0, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def route_ec(x, Wg, b, cf):
+    """Expert-choice routing (P3 ``ExpertChoiceGating``): expert e takes the C
+    tokens of largest column-softmax score, lower token first among equals;
+    idx [E,C] lists each expert's tokens in ascending token order and score
+    [E,C] their scores. Returns (idx, score, S [T,E], logits [T,E])."""
+    s = router_logits(x, Wg, b)
+    S = softmax_cols(s)
+    T, E = S.shape
+    C = capacity(T, E, cf)
+    idx = np.empty((E, C), dtype=np.int64)
+    score = np.empty((E, C), dtype=F64)
+    for e in range(E):
+        chosen = np.argsort(-S[:, e], kind="stable")[:C]
+        chosen = np.sort(chosen)
+        idx[e] = chosen
+        score[e] = S[chosen, e]
+    return idx, score, S, s
+
+
+def ec_margin(logits, C):
+    """Per expert, l_(C) - l_(C+1) on its descending logit column; +inf when C = T."""
+    s = _f64(logits)
+    T = s.shape[0]
+    if C >= T:
+        return np.full(s.shape[1], np.inf)
+    ss = -np.sort(-s, axis=0)
+    return ss[C - 1, :] - ss[C, :]
+
+
+def mix_ec(x, idx, score, Wgate, Wup, Wdown):
+    """y_t = sum over experts e that chose t of score[e,t] * E_e(x_t); tokens no
+    expert chose get y_t = 0 (the dispatch mask of P3 ``ExpertChoiceGating``
+    applied to the expert outputs)."""
+    x = _f64(x)
+    T = x.shape[0]
+    E = idx.shape[0]
+    y = np.zeros((T, Wdown.shape[2]), dtype=F64)
+    for e in range(E):
+        tt = np.asarray(idx[e])
+        out = expert_ffn(x[tt], Wgate[e], Wup[e], Wdown[e])
+        y[tt] += _f64(score[e])[:, None] * out
+    return y
+
+
+def forward_ec(x, Wg, b, Wgate, Wup, Wdown, cf):
+    """Expert-choice layer forward. Returns dict with y, idx, score, probs, logits."""
+    idx, score, S, s = route_ec(x, Wg, b, cf)
+    y = mix_ec(x, idx, score, Wgate, Wup, Wdown)
+    return {"y": y, "idx": idx, "w": score, "probs": S, "logits": s}
+
+
+# --------------------------------------------------------------------------
+# Dense mixture (used as an independent pin)
+# --------------------------------------------------------------------------
+
+def dense_mixture(x, Wg, b, Wgate, Wup, Wdown):
+    """All experts run on every token, y = sum_e g_e E_e(x) (P5
+    ``MixtureOfExperts.forward``)."""
+    g = softmax_rows(router_logits(x, Wg, b))
+    x = _f64(x)
+    y = np.zeros((x.shape[0], Wdown.shape[2]), dtype=F64)
+    for e in range(g.shape[1]):
+        y += g[:, e:e + 1] * expert_ffn(x, Wgate[e], Wup[e], Wdown[e])
+    return y

@@ -1,0 +1,64 @@
+"""Each plausible mistake planted in a copy of the oracle makes some pin fail.
+
+The mistakes are planted on the CPU, in a private copy of the oracle's source
+(text replacement, then exec into a fresh module); the real oracle is untouched.
+"""
+import inspect
+import types
+
+import pytest
+
+from oracle import moe_oracle
+from tests.pins import PINS
+
+SRC = inspect.getsource(moe_oracle)
+
+MUTANTS = {
+    "no_renormalise": ("sel = sel / sel.sum(axis=1, keepdims=True)", "sel = sel"),
+    "renormalise_always": ("if renormalize:\n        sel = sel / sel",
+                           "if True:\n        sel = sel / sel"),
+    "softmax_no_shift_wrong_axis": ("return e / e.sum(axis=1, keepdims=True)",
+                                    "return e / e.sum(axis=0, keepdims=True)"),
+    "topk_ascending": ("order = np.argsort(-p, axis=1, kind=\"stable\")",
+                       "order = np.argsort(p, axis=1, kind=\"stable\")"),
+    "ties_to_higher_index": ("order = np.argsort(-p, axis=1, kind=\"stable\")",
+                             "order = (p.shape[1] - 1) - np.argsort(-p[:, ::-1], axis=1, kind=\"stable\")"),
+    "silu_sign": ("return z / (1.0 + np.exp(-z))", "return z / (1.0 + np.exp(z))"),
+    "silu_is_sigmoid": ("return z / (1.0 + np.exp(-z))", "return 1.0 / (1.0 + np.exp(-z))"),
+    "gate_up_swapped": ("g = silu(X @ _f64(Wgate))\n    u = X @ _f64(Wup)",
+                        "g = silu(X @ _f64(Wup))\n    u = X @ _f64(Wgate)"),
+    "silu_on_up": ("return (g * u) @ _f64(Wdown)", "return (g * silu(u)) @ _f64(Wdown)"),
+    "bias_dropped": ("s = s + _f64(b)[None, :]", "s = s"),
+    "weight_wrong_slot": ("w[tt, jj][:, None] * out", "w[tt, 0][:, None] * out"),
+    "f_over_Tk": ("f = c.astype(F64) / T", "f = c.astype(F64) / (T * k)"),
+    "loss_missing_k": ("loss = E * np.sum((f / k) * p)", "loss = E * np.sum(f * p)"),
+    "p_is_sum": ("p = probs.mean(axis=0)", "p = probs.sum(axis=0)"),
+    "capacity_rounds_up": ("return int(T * cf / E)", "return -(-int(T * cf) // E)"),
+    "ec_softmax_rows": ("z = s - s.max(axis=0, keepdims=True)\n    e = np.exp(z)\n    return e / e.sum(axis=0, keepdims=True)",
+                        "z = s - s.max(axis=1, keepdims=True)\n    e = np.exp(z)\n    return e / e.sum(axis=1, keepdims=True)"),
+    "ec_smallest_scores": ("chosen = np.argsort(-S[:, e], kind=\"stable\")[:C]",
+                           "chosen = np.argsort(S[:, e], kind=\"stable\")[:C]"),
+    "ec_unsorted_tokens": ("chosen = np.sort(chosen)\n", "\n"),
+    "ec_score_unweighted": ("y[tt] += _f64(score[e])[:, None] * out", "y[tt] += out"),
+    "margin_off_by_one": ("return ps[:, k - 1] - ps[:, k]", "return ps[:, k] - ps[:, k + 1 if k + 1 < E else k]"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(SRC.replace(old, new, 1), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    M = _mutant(name)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(M)
+        except Exception:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
