@@ -1,0 +1,191 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer (pages cited by title):
+ *   - router: s = x W_g (+ b), g = softmax(s), TopK(g), y = sum_{i in TopK} g_i E_i(x)
+ *     ("MoE" primer on qiita, section "ゲート / ルーターって何者？", the four router
+ *     equations; bias as in "机器学习基础系列——混合专家模型", GatingNetwork);
+ *     the selected weights renormalised to sum to 1 as in
+ *     "Mixture of Experts（MoE）の理論と実装", MoELayer.route, and
+ *     "Sparse Mixture of Experts(MoE) 아키텍처 심층 분석", TopKGating;
+ *   - experts: E_i(x) = (silu(x W_gate) * (x W_up)) W_down, silu(z) = z / (1 + e^-z)
+ *     ("Mixture of Experts（MoE）の理論と実装", Expert.forward; the Korean page's
+ *     SwiGLUExpert);
+ *   - load-balancing statistics f_i, p_i and loss = E * sum_i (f_i / k) p_i
+ *     ("Mixture of Experts（MoE）の理論と実装", load_balancing_loss; the Korean page's
+ *     compute_load_balancing_loss);
+ *   - expert-choice routing with capacity C = floor(T * cf / E): each expert takes the
+ *     C tokens of largest softmax-over-tokens score (the Korean page's
+ *     ExpertChoiceGating).
+ *
+ * Conventions for every entry point:
+ *   - All tensors are row-major and live in device memory (HBM) unless stated; the
+ *     caller allocates every buffer, including the workspace. The library never
+ *     allocates, frees, synchronises or keeps a pointer after it returns.
+ *   - Work is enqueued on `stream` in order; results are valid once the caller
+ *     synchronises that stream.
+ *   - Activations and weights have the type `shape->dtype` (fp32 or bf16). Router
+ *     logits, probabilities, gate weights, the output y and the statistics are fp32.
+ *     bf16 products accumulate in fp32.
+ *   - Every argument is checked on the host before any HIP call; a failed check
+ *     returns a status and enqueues nothing. MOE_ERR_HIP reports a launch failure.
+ *   - Token-choice slots list experts by descending probability, lower index first on
+ *     ties. Expert-choice lists each expert's tokens in ascending token order; ties at
+ *     the capacity boundary go to the lower token index.
+ *   - Results are deterministic: the same inputs give bitwise the same outputs.
+ *   - Entry points are reentrant; calls on different streams may overlap if their
+ *     workspaces differ.
+ *
+ * Limits: 1 <= E <= 64; token choice 1 <= k <= min(E, 8); d_model and d_ff multiples
+ * of 64; 0 <= T and T * max(k, 1) < 2^31; expert choice needs 1 <= C <= T. x, weights,
+ * y and the workspace must be 16-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  MOE_ERR_BAD_SHAPE = 2,           /* sizes out of range or inconsistent */
+  MOE_ERR_UNSUPPORTED = 3,         /* valid request this library does not provide */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < moe_workspace_size() */
+  MOE_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned */
+  MOE_ERR_HIP = 6                  /* a HIP launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_mode { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 } moe_mode;
+
+/* Shape of one layer call. */
+typedef struct moe_shape {
+  int64_t T;             /* tokens (rows of x) */
+  int64_t d_model;       /* width of x and y */
+  int64_t d_ff;          /* hidden width of each expert */
+  int32_t E;             /* experts */
+  int32_t k;             /* token choice: experts per token; ignored in expert choice */
+  int32_t mode;          /* moe_mode */
+  int32_t dtype;         /* moe_dtype of x, W_g, W_gate, W_up, W_down */
+  int32_t renormalize;   /* token choice: 1 = selected weights divided by their sum
+                            (Mixture of Experts（MoE）の理論と実装, MoELayer.route);
+                            0 = raw probabilities (the qiita router equations) */
+  float capacity_factor; /* expert choice: C = floor(T * capacity_factor / E) */
+} moe_shape;
+
+/* Human-readable name of a status code. Never NULL; the string is static. */
+const char* moe_status_string(int32_t status);
+
+/* Expert-choice capacity C = floor(T * cf / E) (the Korean page's ExpertChoiceGating,
+ * expert_capacity). Host only. Returns MOE_ERR_BAD_SHAPE when mode is not expert
+ * choice or C falls outside [1, T]. */
+moe_status moe_capacity(const moe_shape* shape, int64_t* capacity);
+
+/* Bytes of device workspace moe_route / moe_forward / moe_aux_loss need for `shape`.
+ * Host only; the same size serves all three entry points. */
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/* Byte offset, inside the workspace, of an intermediate buffer of moe_forward, for
+ * tests and debugging. After a moe_forward call has completed on the stream the
+ * buffer holds that call's values until the workspace is used again. Host only.
+ *   MOE_WS_OFFSETS [E+1] int32   first row of each expert's group; [E] = R
+ *   MOE_WS_POS     [T, k] int32  token choice: row of each (token, slot)
+ *   MOE_WS_SRC     [R] int32     token of each row
+ *   MOE_WS_XPERM   [R, d_model]  dtype, x rows in expert-contiguous order
+ *   MOE_WS_H       [R, d_ff]     dtype, silu(x W_gate) * (x W_up) per row
+ *   MOE_WS_O       [R, d_model]  fp32, expert output per row (before weighting)
+ * R = T*k (token choice) or E*C (expert choice). MOE_WS_POS is MOE_ERR_UNSUPPORTED in
+ * expert choice. */
+enum {
+  MOE_WS_OFFSETS = 0,
+  MOE_WS_POS = 1,
+  MOE_WS_SRC = 2,
+  MOE_WS_XPERM = 3,
+  MOE_WS_H = 4,
+  MOE_WS_O = 5
+};
+moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* offset);
+
+/* Router (the qiita router equations; Mixture of Experts（MoE）の理論と実装,
+ * MoELayer.route; the Korean page's TopKGating and ExpertChoiceGating).
+ *   x      [T, d_model]   dtype
+ *   W_g    [d_model, E]   dtype (the x @ W layout of MoELayer.__init__)
+ *   b_g    [E] fp32 router bias added to the logits, or NULL for none
+ * Token choice outputs:
+ *   idx    [T, k] int32   selected experts, descending probability
+ *   w      [T, k] fp32    gate weights of the selected experts
+ * Expert choice outputs (C = moe_capacity):
+ *   idx    [E, C] int32   tokens chosen by each expert, ascending token index
+ *   w      [E, C] fp32    their scores (column-softmax values)
+ * Optional outputs (NULL to skip):
+ *   probs  [T, E] fp32    softmax probabilities (expert choice: over tokens, per column)
+ *   counts [E] int32      assignments per expert (expert choice: C each)
+ * idx and w are required. */
+moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
+                     int32_t* idx, float* w, float* probs, int32_t* counts, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer forward: router, dispatch (histogram, prefix sum, stable permutation of
+ * token rows into expert-contiguous order), grouped SwiGLU gate/up GEMM, grouped down
+ * GEMM, weighted combine, and (token choice) the load-balancing statistics.
+ *   x, W_g, b_g   as in moe_route
+ *   W_gate, W_up  [E, d_model, d_ff] dtype, expert e's matrix at offset e*d_model*d_ff
+ *   W_down        [E, d_ff, d_model] dtype
+ *   y             [T, d_model] fp32   y_t = sum over the token's experts of
+ *                 weight * E_e(x_t); in expert choice a token no expert takes gets 0
+ * Optional outputs (NULL to skip): idx, w, probs, counts as in moe_route, and, token
+ * choice only:
+ *   f     [E] fp32   counts / T (sums to k)
+ *   p     [E] fp32   mean over tokens of probs
+ *   loss  [1] fp32   E * sum_e (f_e / k) * p_e (1 under uniform routing)
+ * Passing f, p or loss in expert-choice mode returns MOE_ERR_UNSUPPORTED: the pages
+ * define these statistics for token choice only. */
+moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
+                       const void* W_gate, const void* W_up, const void* W_down, float* y,
+                       int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
+                       float* loss, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Load-balancing statistics from router outputs (Mixture of Experts（MoE）の理論と実装,
+ * load_balancing_loss; the Korean page's compute_load_balancing_loss), token choice:
+ *   probs [T, E] fp32, idx [T, k] int32 (values in [0, E)) ->
+ *   f [E] = counts / T, p [E] = mean_t probs, loss [1] = E * sum (f / k) p,
+ *   counts [E] int32 (optional, NULL to skip).
+ * Expert-choice shapes return MOE_ERR_UNSUPPORTED. With T = 0, f, p, loss and counts
+ * are zero. */
+moe_status moe_aux_loss(const moe_shape* shape, const float* probs, const int32_t* idx, float* f,
+                        float* p, float* loss, int32_t* counts, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Stage timing. While enabled, every moe_route / moe_forward / moe_aux_loss call
+ * records a hipEvent pair around each stage's kernel launch on the caller's stream.
+ * moe_profile_read waits for the recorded events, returns per-stage totals
+ * (milliseconds, and the number of timed launches) for stages 0..n-1 and clears them.
+ * Not thread-safe: one profiling caller per process. */
+enum {
+  MOE_STAGE_ROUTER = 0,
+  MOE_STAGE_SCAN = 1,
+  MOE_STAGE_PERMUTE = 2,
+  MOE_STAGE_GEMM_GATE_UP = 3,
+  MOE_STAGE_GEMM_DOWN = 4,
+  MOE_STAGE_COMBINE = 5,
+  MOE_STAGE_AUX = 6,
+  MOE_STAGE_EC_SELECT = 7,
+  MOE_NUM_STAGES = 8
+};
+moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_read(double* total_ms, int64_t* launches, int32_t n);
+const char* moe_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

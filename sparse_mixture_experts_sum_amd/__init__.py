@@ -1,0 +1,288 @@
+"""MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+
+A thin ctypes binding over the C ABI in ``include/moe.h`` (``libmoe_hip.so``, built
+in-tree by ``python -m sparse_mixture_experts_sum_amd.build``). Every step of the
+layer runs in the library's HIP kernels; this module only checks tensor
+metadata, allocates outputs and the workspace with torch (device memory), and
+passes pointers and the current HIP stream. There is no fallback: if the library
+is missing, importing the binding's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "moe_route", "moe_forward", "moe_aux_loss", "make_shape", "workspace_size", "capacity",
+    "workspace_offset", "profile_enable", "profile_read", "stage_names", "SparseMoE",
+    "MoEError", "load_library", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
+
+MOE_FP32, MOE_BF16 = 0, 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
+NUM_STAGES = 8
+WS_OFFSETS, WS_POS, WS_SRC, WS_XPERM, WS_H, WS_O = range(6)
+
+# every symbol include/moe.h declares
+EXPORTS = (
+    "moe_status_string", "moe_capacity", "moe_workspace_size", "moe_workspace_offset",
+    "moe_route", "moe_forward", "moe_aux_loss", "moe_profile_enable", "moe_profile_read",
+    "moe_stage_name",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d_model", ctypes.c_int64),
+        ("d_ff", ctypes.c_int64),
+        ("E", ctypes.c_int32),
+        ("k", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe_hip.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} not found: build it with `python -m sparse_mixture_experts_sum_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, S, I32, I64, F = ctypes.c_void_p, ctypes.POINTER(MoeShape), ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [I32]
+    lib.moe_stage_name.restype = ctypes.c_char_p
+    lib.moe_stage_name.argtypes = [I32]
+    lib.moe_capacity.argtypes = [S, ctypes.POINTER(I64)]
+    lib.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_workspace_offset.argtypes = [S, I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_route.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_aux_loss.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_profile_enable.argtypes = [I32]
+    lib.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
+    for name in ("moe_capacity", "moe_workspace_size", "moe_workspace_offset", "moe_route",
+                 "moe_forward", "moe_aux_loss", "moe_profile_enable", "moe_profile_read"):
+        getattr(lib, name).restype = I32
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        msg = load_library().moe_status_string(st).decode()
+        raise MoEError(fn, st, msg)
+
+
+def make_shape(T, d_model, d_ff, E, k=2, mode="tc", dtype="bf16", renormalize=True,
+               capacity_factor=1.0) -> MoeShape:
+    return MoeShape(T=int(T), d_model=int(d_model), d_ff=int(d_ff), E=int(E), k=int(k),
+                    mode=MOE_TOKEN_CHOICE if mode == "tc" else MOE_EXPERT_CHOICE,
+                    dtype=MOE_BF16 if dtype in ("bf16", torch.bfloat16) else MOE_FP32,
+                    renormalize=1 if renormalize else 0,
+                    capacity_factor=float(capacity_factor))
+
+
+def workspace_size(shape: MoeShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", load_library().moe_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_offset(shape: MoeShape, which: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_offset",
+           load_library().moe_workspace_offset(ctypes.byref(shape), int(which), ctypes.byref(n)))
+    return n.value
+
+
+def capacity(shape: MoeShape) -> int:
+    c = ctypes.c_int64(0)
+    _check("moe_capacity", load_library().moe_capacity(ctypes.byref(shape), ctypes.byref(c)))
+    return c.value
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_name(t: torch.Tensor) -> str:
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "fp32"
+    raise TypeError(f"unsupported dtype {t.dtype}: x and weights must be bfloat16 or float32")
+
+
+def _need(t, name, dtype=None, dev=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    n = workspace_size(shape)
+    if workspace is not None and workspace.numel() * workspace.element_size() >= n:
+        return workspace
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+
+
+def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormalize=True,
+              want_probs=True, want_counts=True, workspace=None) -> dict:
+    """Router only. Token choice returns idx/w [T,k]; expert choice idx/w [E,C]."""
+    dev = x.device
+    dt = x.dtype
+    _need(x, "x", dev=dev)
+    _need(W_g, "W_g", dt, dev)
+    _need(b_g, "b_g", torch.float32, dev)
+    T, d = x.shape
+    E = W_g.shape[1]
+    shape = make_shape(T, d, 64, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
+    ws = _workspace(shape, dev, workspace)
+    if mode == "tc":
+        idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    else:
+        C = capacity(shape)
+        idx = torch.empty(E, C, dtype=torch.int32, device=dev)
+        w = torch.empty(E, C, dtype=torch.float32, device=dev)
+    probs = torch.empty(T, E, dtype=torch.float32, device=dev) if want_probs else None
+    counts = torch.empty(E, dtype=torch.int32, device=dev) if want_counts else None
+    _check("moe_route", load_library().moe_route(
+        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(idx), _ptr(w), _ptr(probs),
+        _ptr(counts), _ptr(ws), ws.numel(), _stream(dev)))
+    return {"idx": idx, "w": w, "probs": probs, "counts": counts}
+
+
+def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_factor=1.0,
+                renormalize=True, want_routing=True, want_probs=True, want_stats=True,
+                workspace=None, y=None) -> dict:
+    """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
+    counts and (token choice) f, p, loss."""
+    dev = x.device
+    dt = x.dtype
+    _need(x, "x", dev=dev)
+    for t, nm in ((W_g, "W_g"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down, "W_down")):
+        _need(t, nm, dt, dev)
+    _need(b_g, "b_g", torch.float32, dev)
+    T, d = x.shape
+    E, _, f = W_gate.shape
+    if W_g.shape != (d, E) or W_up.shape != (E, d, f) or W_down.shape != (E, f, d):
+        raise ValueError("inconsistent weight shapes")
+    shape = make_shape(T, d, f, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
+    ws = _workspace(shape, dev, workspace)
+    if y is None:
+        y = torch.empty(T, d, dtype=torch.float32, device=dev)
+    else:
+        _need(y, "y", torch.float32, dev)
+    idx = w = probs = counts = fo = po = lo = None
+    if want_routing:
+        if mode == "tc":
+            idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+            w = torch.empty(T, k, dtype=torch.float32, device=dev)
+        else:
+            C = capacity(shape)
+            idx = torch.empty(E, C, dtype=torch.int32, device=dev)
+            w = torch.empty(E, C, dtype=torch.float32, device=dev)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if want_probs:
+        probs = torch.empty(T, E, dtype=torch.float32, device=dev)
+    if want_stats and mode == "tc":
+        fo = torch.empty(E, dtype=torch.float32, device=dev)
+        po = torch.empty(E, dtype=torch.float32, device=dev)
+        lo = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("moe_forward", load_library().moe_forward(
+        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+        _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo), _ptr(po), _ptr(lo),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return {"y": y, "idx": idx, "w": w, "probs": probs, "counts": counts, "f": fo, "p": po,
+            "loss": lo, "workspace": ws, "shape": shape}
+
+
+def moe_aux_loss(probs, idx, *, workspace=None) -> dict:
+    """f, p, loss and counts from router outputs probs [T,E] and idx [T,k] (token choice)."""
+    dev = probs.device
+    _need(probs, "probs", torch.float32, dev)
+    _need(idx, "idx", torch.int32, dev)
+    T, E = probs.shape
+    k = idx.shape[1]
+    shape = make_shape(T, 64, 64, E, k, "tc", "fp32")
+    ws = _workspace(shape, dev, workspace)
+    f = torch.empty(E, dtype=torch.float32, device=dev)
+    p = torch.empty(E, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    _check("moe_aux_loss", load_library().moe_aux_loss(
+        ctypes.byref(shape), _ptr(probs), _ptr(idx), _ptr(f), _ptr(p), _ptr(loss), _ptr(counts),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return {"f": f, "p": p, "loss": loss, "counts": counts}
+
+
+def profile_enable(on: bool = True):
+    _check("moe_profile_enable", load_library().moe_profile_enable(1 if on else 0))
+
+
+def stage_names():
+    lib = load_library()
+    return [lib.moe_stage_name(i).decode() for i in range(NUM_STAGES)]
+
+
+def profile_read() -> dict:
+    """Per-stage totals since the last read: {stage: (total_ms, launches)}."""
+    ms = (ctypes.c_double * NUM_STAGES)()
+    n = (ctypes.c_int64 * NUM_STAGES)()
+    _check("moe_profile_read", load_library().moe_profile_read(ms, n, NUM_STAGES))
+    return {nm: (ms[i], n[i]) for i, nm in enumerate(stage_names())}
+
+
+class SparseMoE:
+    """One sparse MoE layer with its weights held as device tensors.
+
+    ``layer(x)`` runs ``moe_forward`` and returns the fp32 output y; the workspace is
+    allocated once per token count and reused."""
+
+    def __init__(self, W_g, W_gate, W_up, W_down, b_g=None, *, k=2, mode="tc",
+                 capacity_factor=1.0, renormalize=True):
+        self.W_g, self.W_gate, self.W_up, self.W_down, self.b_g = W_g, W_gate, W_up, W_down, b_g
+        self.k, self.mode, self.cf, self.renormalize = k, mode, capacity_factor, renormalize
+        self._ws = None
+        self.last = None
+
+    def __call__(self, x, **kw):
+        out = moe_forward(x, self.W_g, self.b_g, self.W_gate, self.W_up, self.W_down, k=self.k,
+                          mode=self.mode, capacity_factor=self.cf, renormalize=self.renormalize,
+                          workspace=self._ws, **kw)
+        self._ws = out["workspace"]
+        self.last = out
+        return out["y"]

@@ -1,0 +1,188 @@
+// Weighted un-permute and combine, and the load-balancing statistics.
+//
+// Combine: y_t = sum over the token's experts of weight * E_e(x_t) (qiita primer,
+// fourth router equation; "Mixture of Experts（MoE）の理論と実装", MoELayer.forward).
+// Expert outputs o sit in expert-contiguous rows; token t reads its k rows through
+// pos[t, :] and sums them in slot order in fp32, so the result does not depend on
+// scheduling. Expert choice (the Korean page's ExpertChoiceGating dispatch mask):
+// token t finds, per expert, whether that expert chose it by binary search in the
+// expert's ascending token list, and sums the chosen rows in ascending expert order.
+//
+// Statistics ("Mixture of Experts（MoE）の理論と実装", load_balancing_loss; the Korean
+// page's compute_load_balancing_loss): f_e = count_e / T, p_e = mean_t probs[t, e],
+// loss = E * sum_e (f_e / k) * p_e, from per-block partials in a fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// one wave per token, 4 tokens per workgroup; k <= 8
+__global__ __launch_bounds__(256) void combine_tc_kernel(const float* __restrict__ o,
+                                                         const int32_t* __restrict__ pos,
+                                                         const float* __restrict__ w, int T, int d,
+                                                         int k, float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int pj = 0;
+  float wj = 0.f;
+  if (lane < k) {
+    pj = pos[(size_t)t * k + lane];
+    wj = w[(size_t)t * k + lane];
+  }
+  int prow[8];
+  float pw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    prow[j] = __shfl(pj, j);
+    pw[j] = __shfl(wj, j);
+  }
+  const int nch = d / 4;
+  float* yr = y + (size_t)t * d;
+  for (int c = lane; c < nch; c += 64) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = (j < k && prow[j] >= 0) ? *reinterpret_cast<const f32x4*>(o + (size_t)prow[j] * d + 4 * c)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) acc += pw[j] * v[j];
+    *reinterpret_cast<f32x4*>(yr + 4 * c) = acc;
+  }
+}
+
+// one wave per token; lane e < E searches expert e's token list
+__global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict__ o,
+                                                         const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ score, int T,
+                                                         int d, int E, int C,
+                                                         float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int row = -1;
+  float sc = 0.f;
+  if (lane < E) {
+    const int32_t* list = idx + (size_t)lane * C;
+    int lo = 0, hi = C;  // first position with list[pos] >= t
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (list[mid] < t) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo < C && list[lo] == t) {
+      row = lane * C + lo;
+      sc = score[(size_t)lane * C + lo];
+    }
+  }
+  const uint64_t found = __ballot(row >= 0);
+  const int nch = d / 4;
+  float* yr = y + (size_t)t * d;
+  for (int c = lane; c < nch; c += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    uint64_t m = found;
+    while (m) {
+      const int e = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      const int r = __shfl(row, e);
+      const float s = __shfl(sc, e);
+      acc += s * *reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c);
+    }
+    *reinterpret_cast<f32x4*>(yr + 4 * c) = acc;
+  }
+}
+
+// per block of kRouterTokens tokens: slot counts per expert and probability sums
+__global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restrict__ probs,
+                                                           const int32_t* __restrict__ idx, int T,
+                                                           int E, int k, int32_t* blk_counts,
+                                                           float* blk_psum) {
+  __shared__ int cnt[64];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int ntok = min(kRouterTokens, T - t0);
+  if (tid < 64) cnt[tid] = 0;
+  __syncthreads();
+  for (int q = tid; q < ntok * k; q += 256) {
+    const int e = idx[(size_t)t0 * k + q];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  if (tid < E) {
+    float s = 0.f;
+    for (int q = 0; q < ntok; ++q) s += probs[(size_t)(t0 + q) * E + tid];
+    blk_psum[(size_t)blockIdx.x * E + tid] = s;
+  }
+  __syncthreads();
+  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(64) void aux_final_kernel(const int32_t* __restrict__ blk_counts,
+                                                       const float* __restrict__ blk_psum, int nblk,
+                                                       int T, int E, int k, float* f, float* p,
+                                                       float* loss, int32_t* counts) {
+  __shared__ double term[64];
+  const int e = threadIdx.x;
+  if (e < E) {
+    long long c = 0;
+    double ps = 0.0;
+    for (int b = 0; b < nblk; ++b) {
+      c += blk_counts[(size_t)b * E + e];
+      ps += (double)blk_psum[(size_t)b * E + e];
+    }
+    const float fe = (float)((double)c / (double)T);
+    const float pe = (float)(ps / (double)T);
+    if (f) f[e] = fe;
+    if (p) p[e] = pe;
+    if (counts) counts[e] = (int32_t)c;
+    term[e] = ((double)fe / (double)k) * (double)pe;
+  }
+  __syncthreads();
+  if (e == 0 && loss) {
+    double s = 0.0;
+    for (int i = 0; i < E; ++i) s += term[i];
+    *loss = (float)((double)E * s);
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,
+                             int k, float* y, hipStream_t s) {
+  combine_tc_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, pos, w, T, d, k, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
+                             int E, int C, float* y, hipStream_t s) {
+  combine_ec_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, idx, score, T, d, E, C, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,
+                               int32_t* blk_counts, float* blk_psum, hipStream_t s) {
+  const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
+  aux_partials_kernel<<<nblk, 256, 0, s>>>(probs, idx, T, E, k, blk_counts, blk_psum);
+  return hipGetLastError();
+}
+
+hipError_t launch_aux_final(const int32_t* blk_counts, const float* blk_psum, int nblk, int T,
+                            int E, int k, float* f, float* p, float* loss, int32_t* counts,
+                            hipStream_t s) {
+  aux_final_kernel<<<1, 64, 0, s>>>(blk_counts, blk_psum, nblk, T, E, k, f, p, loss, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)min((size_t)1024, (n + 255) / 256);
+  fill_zero_kernel<<<grid, 256, 0, s>>>(static_cast<uint32_t*>(ptr), n);
+  return hipGetLastError();
+}

@@ -1,0 +1,67 @@
+// Internal helpers shared by the gfx950 kernels of the MoE library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+// Tokens per router workgroup; the per-block dispatch tables are indexed by it.
+constexpr int kRouterTokens = 64;
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Order-preserving map of a float to uint32 (larger float -> larger key), with -0
+// folded onto +0 so that the two zeros tie as they do in float comparison.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64, at
+// most 1024). `sh` must hold 17 ints. Returns the exclusive prefix; *total gets the
+// sum over the block. All threads must call it.
+__device__ inline int block_exclusive_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int s = lane < nw ? sh[lane] : 0;
+    int si = s;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int u = __shfl_up(si, o);
+      if (lane >= o) si += u;
+    }
+    if (lane < nw) sh[lane] = si - s;  // exclusive base of each wave
+    if (lane == nw - 1) sh[16] = si;   // block total
+  }
+  __syncthreads();
+  const int base = sh[wid];
+  *total = sh[16];
+  __syncthreads();  // sh may be reused by the caller right after
+  return base + incl - v;
+}

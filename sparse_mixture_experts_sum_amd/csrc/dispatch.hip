@@ -1,0 +1,139 @@
+// Dispatch: prefix sum over the router's per-block expert histogram and the stable
+// permutation of token rows into expert-contiguous order.
+//
+// The expert-parallel dispatch of "Sparse Mixture of Experts(MoE) 아키텍처 심층 분석"
+// (ExpertParallelRouter.dispatch) counts tokens per destination and sorts the token
+// rows by expert before sending them; here the same grouping feeds the grouped GEMMs
+// of one GPU. Row order inside an expert's group is the flattened (token, slot)
+// order, so the permutation is stable and deterministic without atomics.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+// One workgroup. Entry (e, b) of the expert-major sequence q = e*nblk + b holds
+// blk_counts[b, e]; its exclusive prefix is the first row of block b's slots for
+// expert e, and the prefix at (e, 0) is the start of expert e's group.
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    const int32_t* __restrict__ blk_counts, int nblk, int E, int32_t* counts, int32_t* offsets,
+    int32_t* base, int32_t* user_counts) {
+  __shared__ int sh[17];
+  __shared__ int off_sh[65];
+  const long n = (long)nblk * E;
+  const int tid = threadIdx.x;
+  const long per = (n + kScanThreads - 1) / kScanThreads;
+  const long qb = min(n, (long)tid * per), qe = min(n, qb + per);
+  int local = 0;
+  for (long q = qb; q < qe; ++q) {
+    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
+    local += blk_counts[(size_t)b * E + e];
+  }
+  int total;
+  int run = block_exclusive_scan(local, sh, &total);
+  for (long q = qb; q < qe; ++q) {
+    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
+    if (b == 0) off_sh[e] = run;
+    base[(size_t)b * E + e] = run;
+    run += blk_counts[(size_t)b * E + e];
+  }
+  if (tid == 0) off_sh[E] = total;
+  __syncthreads();
+  if (tid <= E) offsets[tid] = off_sh[tid];
+  if (tid < E) {
+    const int c = off_sh[tid + 1] - off_sh[tid];
+    counts[tid] = c;
+    if (user_counts) user_counts[tid] = c;
+  }
+}
+
+// One wave per token: slots first (pos, src), then the row copy to every slot's row.
+template <int EB>
+__global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict__ x, int T, int d,
+                                                         int E, int k, const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ lrank,
+                                                         const int32_t* __restrict__ base,
+                                                         int32_t* pos, int32_t* src,
+                                                         char* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int R = T * k;
+  int p = -1;
+  if (lane < k) {
+    const int e = idx[(size_t)t * k + lane];
+    p = base[(size_t)(t / kRouterTokens) * E + e] + lrank[(size_t)t * k + lane];
+    if (p < 0 || p >= R) p = -1;  // unreachable for consistent tables; never write outside
+    pos[(size_t)t * k + lane] = p;
+    if (p >= 0) src[p] = t;
+  }
+  const size_t row_bytes = (size_t)d * EB;
+  const int nch = (int)(row_bytes / 16);
+  const char* xr = x + (size_t)t * row_bytes;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * 64 + lane;
+      if (c < nch) v[u] = ld16(xr + 16 * (size_t)c);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int pj = __shfl(p, j);
+      if (pj < 0) continue;
+      char* dst = x_perm + (size_t)pj * row_bytes;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < nch) st16(dst + 16 * (size_t)c, v[u]);
+      }
+    }
+  }
+}
+
+// One wave per routed row of expert choice: row e*C + c takes token idx[e, c].
+__global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict__ x, size_t row_bytes,
+                                                         int R, const int32_t* __restrict__ idx,
+                                                         int32_t* src, char* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int t = idx[r];
+  if (lane == 0) src[r] = t;
+  const int nch = (int)(row_bytes / 16);
+  const char* xr = x + (size_t)t * row_bytes;
+  char* dst = x_perm + (size_t)r * row_bytes;
+  for (int c = lane; c < nch; c += 64) st16(dst + 16 * (size_t)c, ld16(xr + 16 * (size_t)c));
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int32_t* counts,
+                                int32_t* offsets, int32_t* base, int32_t* user_counts,
+                                hipStream_t s) {
+  dispatch_scan_kernel<<<1, kScanThreads, 0, s>>>(blk_counts, nblk, E, counts, offsets, base,
+                                                  user_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
+                             const int32_t* idx, const int32_t* lrank, const int32_t* base,
+                             int32_t* pos, int32_t* src, void* x_perm, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (elt_bytes == 2)
+    permute_tc_kernel<2><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
+                                                base, pos, src, static_cast<char*>(x_perm));
+  else
+    permute_tc_kernel<4><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
+                                                base, pos, src, static_cast<char*>(x_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
+                             const int32_t* idx, int32_t* src, void* x_perm, hipStream_t s) {
+  const int R = E * C;
+  dim3 grid((R + 3) / 4), block(256);
+  permute_ec_kernel<<<grid, block, 0, s>>>(static_cast<const char*>(x), (size_t)d * elt_bytes, R, idx,
+                                           src, static_cast<char*>(x_perm));
+  return hipGetLastError();
+}

@@ -1,0 +1,73 @@
+// Launch wrappers for the gfx950 kernels (internal; the public ABI is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+struct RouterArgs {
+  const void* x;        // [T, d] dtype
+  const void* Wg;       // [d, E] dtype
+  const float* bias;    // [E] or nullptr
+  int T, d, E, k, renorm;
+  // token choice outputs
+  int32_t* idx;         // [T, k]
+  float* w;             // [T, k]
+  float* probs;         // [T, E] or nullptr
+  int32_t* lrank;       // [T, k] rank of the slot among equal experts within its block
+  int32_t* blk_counts;  // [nblk, E]
+  float* blk_psum;      // [nblk, E] column sums of probs over the block's tokens
+  // expert choice output
+  float* logitsT;       // [E, T] (expert choice only)
+};
+
+// Token-choice router (logits, softmax, top-k, weights, per-block histogram and
+// slot ranks, per-block probability sums) or, with ec = 1, expert-choice logits.
+hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
+
+// Expert choice: per expert, softmax over tokens, top-C tokens (ascending token
+// order) and scores. Also writes offsets[e] = e*C and counts (optional).
+hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
+                            float* probs, int32_t* offsets, int32_t* counts, hipStream_t s);
+
+// Dispatch prefix sum over per-block counts: counts[E], offsets[E+1],
+// base[nblk, E] (first row of each (block, expert) pair), optional user counts.
+hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int32_t* counts,
+                                int32_t* offsets, int32_t* base, int32_t* user_counts,
+                                hipStream_t s);
+
+// Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t].
+hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
+                             const int32_t* idx, const int32_t* lrank, const int32_t* base,
+                             int32_t* pos, int32_t* src, void* x_perm, hipStream_t s);
+
+// Expert choice: row e*C + c takes token idx[e, c].
+hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
+                             const int32_t* idx, int32_t* src, void* x_perm, hipStream_t s);
+
+// Grouped GEMMs over expert-contiguous rows (group e = rows [offsets[e], offsets[e+1])).
+//   gate/up: h[r] = silu(x_perm[r] W_gate[e]) * (x_perm[r] W_up[e])  -> h [R, f]
+//   down:    o[r] = h[r] W_down[e]                                   -> o [R, d] fp32
+// R_max bounds the number of routed rows (sizes the grid).
+hipError_t launch_gemm_gateup(int bf16, const void* xp, const void* Wgate, const void* Wup,
+                              const int32_t* offsets, int E, int R_max, int d, int f, void* h,
+                              hipStream_t s);
+hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
+                            int E, int R_max, int f, int d, float* o, hipStream_t s);
+
+// y[t] = sum_j w[t,j] * o[pos[t,j]]  (j in slot order)
+hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,
+                             int k, float* y, hipStream_t s);
+// y[t] = sum over experts e (ascending) that chose t of score[e,c] * o[e*C + c]; else 0
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
+                             int E, int C, float* y, hipStream_t s);
+
+// Per-block counts and probability sums from router outputs (standalone aux loss).
+hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,
+                               int32_t* blk_counts, float* blk_psum, hipStream_t s);
+// f, p, loss (and optional counts) from per-block partials.
+hipError_t launch_aux_final(const int32_t* blk_counts, const float* blk_psum, int nblk, int T,
+                            int E, int k, float* f, float* p, float* loss, int32_t* counts,
+                            hipStream_t s);
+// Zero-fill helper (device memory), used for empty inputs.
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);

@@ -1,0 +1,380 @@
+// Host side of the C ABI (include/moe.h): argument checks, workspace layout and the
+// launch sequence on the caller's stream. No allocation, no synchronisation.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+  int64_t R = 0, C = 0;
+  int nblk = 0;
+  size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
+         offsets = 0, counts = 0, logitsT = 0, x_perm = 0, h = 0, o = 0, total = 0;
+};
+
+int64_t ec_capacity(const moe_shape& s) {
+  const double c = floor((double)s.T * (double)s.capacity_factor / (double)s.E);
+  if (!(c >= 0.0) || c > 9.0e18) return -1;
+  return (int64_t)c;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_NULL_ARG;
+  if (s->dtype != MOE_FP32 && s->dtype != MOE_BF16) return MOE_ERR_BAD_SHAPE;
+  if (s->mode != MOE_TOKEN_CHOICE && s->mode != MOE_EXPERT_CHOICE) return MOE_ERR_BAD_SHAPE;
+  if (s->T < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->E < 1) return MOE_ERR_BAD_SHAPE;
+  if (s->d_model % 64 || s->d_ff % 64) return MOE_ERR_BAD_SHAPE;
+  if (s->d_model > (1 << 20) || s->d_ff > (1 << 20)) return MOE_ERR_BAD_SHAPE;
+  if (s->E > 64) return MOE_ERR_UNSUPPORTED;
+  if (s->mode == MOE_TOKEN_CHOICE) {
+    if (s->k < 1 || s->k > s->E) return MOE_ERR_BAD_SHAPE;
+    if (s->k > 8) return MOE_ERR_UNSUPPORTED;
+    if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_BAD_SHAPE;
+    if (s->T * (int64_t)s->k >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  } else {
+    if (!(s->capacity_factor > 0.0f) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
+    const int64_t C = ec_capacity(*s);
+    if (C < 1 || C > s->T) return MOE_ERR_BAD_SHAPE;
+    if (C * (int64_t)s->E >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+  }
+  return MOE_OK;
+}
+
+Layout make_layout(const moe_shape& s) {
+  Layout L;
+  const size_t eb = s.dtype == MOE_BF16 ? 2 : 4;
+  const int64_t T = s.T, E = s.E, d = s.d_model, f = s.d_ff;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  L.nblk = (int)((T + 63) / 64);
+  if (s.mode == MOE_TOKEN_CHOICE) {
+    const int64_t k = s.k;
+    L.R = T * k;
+    L.idx = take(T * k * 4);
+    L.w = take(T * k * 4);
+    L.lrank = take(T * k * 4);
+    L.pos = take(T * k * 4);
+    L.blk_counts = take((size_t)L.nblk * E * 4);
+    L.blk_psum = take((size_t)L.nblk * E * 4);
+    L.base = take((size_t)L.nblk * E * 4);
+  } else {
+    L.C = ec_capacity(s);
+    L.R = E * L.C;
+    L.logitsT = take(E * T * 4);
+    L.idx = take(L.R * 4);
+    L.w = take(L.R * 4);
+  }
+  L.offsets = take((E + 1) * 4);
+  L.counts = take(E * 4);
+  L.src = take(L.R * 4);
+  L.x_perm = take((size_t)L.R * d * eb);
+  L.h = take((size_t)L.R * f * eb);
+  L.o = take((size_t)L.R * d * 4);
+  L.total = cur;
+  return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- stage timing ----------------------------------------------------------------
+struct ProfRec {
+  int stage;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t prof_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct StageTimer {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(int st, hipStream_t str) : stage(st), s(str) {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (!g_prof_on) return;
+    a = prof_event();
+    b = prof_event();
+    if (a && b && hipEventRecord(a, s) != hipSuccess) drop();
+  }
+  void drop() {
+    if (a) g_event_pool.push_back(a);
+    if (b) g_event_pool.push_back(b);
+    a = b = nullptr;
+  }
+  void done() {
+    if (!a || !b) return;
+    const bool ok = hipEventRecord(b, s) == hipSuccess;
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    if (ok) g_prof_recs.push_back({stage, a, b});
+    else drop();
+    a = b = nullptr;
+  }
+};
+
+#define MOE_LAUNCH(stage, call)              \
+  do {                                       \
+    StageTimer _t((stage), stream);          \
+    hipError_t _e = (call);                  \
+    _t.done();                               \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, hipStream_t stream) {
+  if (f) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(f, (size_t)E * 4, stream));
+  if (p) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(p, (size_t)E * 4, stream));
+  if (loss) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(loss, 4, stream));
+  if (counts) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(counts, (size_t)E * 4, stream));
+  return MOE_OK;
+}
+
+// Router stage shared by moe_route and moe_forward. Token choice writes idx/w and the
+// dispatch tables; expert choice writes idx/score and the group offsets.
+moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
+                      const float* b_g, int32_t* idx, float* w, float* probs,
+                      int32_t* user_counts, void* ws, hipStream_t stream) {
+  const int bf = s.dtype == MOE_BF16;
+  RouterArgs a{};
+  a.x = x;
+  a.Wg = W_g;
+  a.bias = b_g;
+  a.T = (int)s.T;
+  a.d = (int)s.d_model;
+  a.E = s.E;
+  a.k = s.k;
+  a.renorm = s.renormalize;
+  if (s.mode == MOE_TOKEN_CHOICE) {
+    a.idx = idx;
+    a.w = w;
+    a.probs = probs;
+    a.lrank = at<int32_t>(ws, L.lrank);
+    a.blk_counts = at<int32_t>(ws, L.blk_counts);
+    a.blk_psum = at<float>(ws, L.blk_psum);
+    MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 0, stream));
+    MOE_LAUNCH(MOE_STAGE_SCAN,
+               launch_dispatch_scan(at<int32_t>(ws, L.blk_counts), L.nblk, s.E,
+                                    at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                                    at<int32_t>(ws, L.base), user_counts, stream));
+  } else {
+    a.logitsT = at<float>(ws, L.logitsT);
+    MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
+    MOE_LAUNCH(MOE_STAGE_EC_SELECT,
+               launch_ec_select(at<float>(ws, L.logitsT), (int)s.T, s.E, (int)L.C, idx, w, probs,
+                                at<int32_t>(ws, L.offsets), user_counts, stream));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "sizes out of range or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "request not supported by this library";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than moe_workspace_size()";
+    case MOE_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_capacity(const moe_shape* shape, int64_t* capacity) {
+  if (!shape || !capacity) return MOE_ERR_NULL_ARG;
+  if (shape->mode != MOE_EXPERT_CHOICE) return MOE_ERR_BAD_SHAPE;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  *capacity = ec_capacity(*shape);
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL_ARG;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  *bytes = make_layout(*shape).total;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* offset) {
+  if (!offset) return MOE_ERR_NULL_ARG;
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const Layout L = make_layout(*shape);
+  switch (which) {
+    case MOE_WS_OFFSETS: *offset = L.offsets; return MOE_OK;
+    case MOE_WS_POS:
+      if (shape->mode != MOE_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+      *offset = L.pos;
+      return MOE_OK;
+    case MOE_WS_SRC: *offset = L.src; return MOE_OK;
+    case MOE_WS_XPERM: *offset = L.x_perm; return MOE_OK;
+    case MOE_WS_H: *offset = L.h; return MOE_OK;
+    case MOE_WS_O: *offset = L.o; return MOE_OK;
+    default: return MOE_ERR_BAD_SHAPE;
+  }
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
+                     int32_t* idx, float* w, float* probs, int32_t* counts, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (!idx || !w) return MOE_ERR_NULL_ARG;
+  if (s.T > 0 && (!x || !W_g || !ws)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(W_g) || !aligned16(ws)) return MOE_ERR_MISALIGNED;
+  const Layout L = make_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, stream);
+  return run_router(s, L, x, W_g, b_g, idx, w, probs, counts, ws, stream);
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
+                       const void* W_gate, const void* W_up, const void* W_down, float* y,
+                       int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
+                       float* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.mode == MOE_EXPERT_CHOICE && (f || p || loss)) return MOE_ERR_UNSUPPORTED;
+  if (s.T > 0 && (!x || !W_g || !W_gate || !W_up || !W_down || !y || !ws)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(x) || !aligned16(W_g) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down) || !aligned16(y) || !aligned16(ws))
+    return MOE_ERR_MISALIGNED;
+  const Layout L = make_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, stream);
+
+  const int bf = s.dtype == MOE_BF16;
+  const int eb = bf ? 2 : 4;
+  const int T = (int)s.T, d = (int)s.d_model, ff = (int)s.d_ff, E = s.E;
+  const int R = (int)L.R;
+  int32_t* idx_b = idx ? idx : at<int32_t>(ws, L.idx);
+  float* w_b = w ? w : at<float>(ws, L.w);
+  const int32_t* offsets = at<int32_t>(ws, L.offsets);
+
+  st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, ws, stream);
+  if (st != MOE_OK) return st;
+  if (s.mode == MOE_TOKEN_CHOICE) {
+    MOE_LAUNCH(MOE_STAGE_PERMUTE,
+               launch_permute_tc(x, eb, T, d, E, s.k, idx_b, at<int32_t>(ws, L.lrank),
+                                 at<int32_t>(ws, L.base), at<int32_t>(ws, L.pos),
+                                 at<int32_t>(ws, L.src), at<void>(ws, L.x_perm), stream));
+  } else {
+    MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
+                                                    at<int32_t>(ws, L.src),
+                                                    at<void>(ws, L.x_perm), stream));
+  }
+  MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
+             launch_gemm_gateup(bf, at<void>(ws, L.x_perm), W_gate, W_up, offsets, E, R, d, ff,
+                                at<void>(ws, L.h), stream));
+  MOE_LAUNCH(MOE_STAGE_GEMM_DOWN, launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, E, R,
+                                                   ff, d, at<float>(ws, L.o), stream));
+  if (s.mode == MOE_TOKEN_CHOICE) {
+    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
+                                                    w_b, T, d, s.k, y, stream));
+    if (f || p || loss)
+      MOE_LAUNCH(MOE_STAGE_AUX,
+                 launch_aux_final(at<int32_t>(ws, L.blk_counts), at<float>(ws, L.blk_psum),
+                                  L.nblk, T, E, s.k, f, p, loss, nullptr, stream));
+  } else {
+    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, T, d, E,
+                                                    (int)L.C, y, stream));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_aux_loss(const moe_shape* shape, const float* probs, const int32_t* idx, float* f,
+                        float* p, float* loss, int32_t* counts, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.mode != MOE_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+  if (!f || !p || !loss) return MOE_ERR_NULL_ARG;
+  if (s.T > 0 && (!probs || !idx || !ws)) return MOE_ERR_NULL_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  const Layout L = make_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, stream);
+  MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_partials(probs, idx, (int)s.T, s.E, s.k,
+                                                at<int32_t>(ws, L.blk_counts),
+                                                at<float>(ws, L.blk_psum), stream));
+  MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(at<int32_t>(ws, L.blk_counts), at<float>(ws, L.blk_psum),
+                                             L.nblk, (int)s.T, s.E, s.k, f, p, loss, counts, stream));
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  g_prof_on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(double* total_ms, int64_t* launches, int32_t n) {
+  if (n < 0) return MOE_ERR_BAD_SHAPE;
+  if (n > 0 && (!total_ms || !launches)) return MOE_ERR_NULL_ARG;
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  moe_status st = MOE_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = MOE_ERR_HIP;
+    if (r.stage >= 0 && r.stage < n) {
+      total_ms[r.stage] += ms;
+      launches[r.stage] += 1;
+    }
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  return st;
+}
+
+const char* moe_stage_name(int32_t stage) {
+  static const char* names[MOE_NUM_STAGES] = {"router", "dispatch_scan", "permute",
+                                               "gemm_gate_up", "gemm_down", "combine",
+                                               "aux", "ec_select"};
+  if (stage < 0 || stage >= MOE_NUM_STAGES) return "unknown";
+  return names[stage];
+}
+
+}  // extern "C"

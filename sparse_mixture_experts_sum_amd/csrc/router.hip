@@ -1,0 +1,384 @@
+// Router kernels for gfx950.
+//
+// Token choice (qiita primer, router equations s = W_g x, g = softmax(s), TopK(g);
+// "Mixture of Experts（MoE）の理論と実装", MoELayer.route; the Korean page's
+// TopKGating): one workgroup takes 64 tokens. The skinny GEMM x W_g runs on
+// 16x16 MFMA tiles (x rows streamed from HBM straight into registers as the A
+// operand, W_g staged transposed in LDS as the B operand), then four threads per
+// token do the max-shifted softmax, top-k by (logit desc, index asc) and the
+// weights. The same workgroup counts its slots per expert, ranks each slot among
+// the block's slots of the same expert (flattened token-major order) and sums the
+// block's probabilities per expert, so dispatch and the aux statistics need no
+// second pass over the routing.
+//
+// Expert choice (the Korean page's ExpertChoiceGating): the same GEMM writes the
+// logits transposed, [E, T]; a second kernel takes one expert per workgroup.
+#include <float.h>
+#include <limits.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+template <typename TI>
+struct RouterMma;
+
+template <>
+struct RouterMma<bf16> {
+  static constexpr int VEC = 8;  // elements per 16-byte chunk
+  __device__ static void step(f32x4& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct RouterMma<float> {
+  static constexpr int VEC = 4;
+  __device__ static void step(f32x4& acc, u32x4 a, u32x4 b) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[q]), __uint_as_float(b[q]),
+                                                 acc, 0, 0, 0);
+  }
+};
+
+constexpr int kRT = kRouterTokens;  // tokens per workgroup (4 waves x 16)
+
+template <typename TI, int EP>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
+  using M = RouterMma<TI>;
+  constexpr int VEC = M::VEC;
+  constexpr int ITK = 16 * VEC;                          // k per iteration (4 groups x 4 chunks)
+  constexpr int KC = 32768 / (EP * (int)sizeof(TI));     // k per LDS stage of W_g
+  constexpr int LDW = KC + 16 / (int)sizeof(TI);         // padded row (16 bytes)
+  constexpr int LSP = EP + 1;
+  static_assert(KC % ITK == 0, "stage must hold whole iterations");
+
+  __shared__ __attribute__((aligned(16))) TI Wl[EP * LDW];
+  __shared__ float Ls[kRT * LSP];
+  __shared__ int sel[kRT * 8];
+  __shared__ int running[64];
+
+  const TI* __restrict__ x = static_cast<const TI*>(a.x);
+  const TI* __restrict__ Wg = static_cast<const TI*>(a.Wg);
+  const int T = a.T, d = a.d, E = a.E;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int t0 = blockIdx.x * kRT;
+  const int trow = t0 + wave * 16 + (lane & 15);
+  const TI* xrow = x + (size_t)min(trow, T - 1) * d;
+
+  f32x4 acc[EP / 16];
+#pragma unroll
+  for (int nb = 0; nb < EP / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kc = 0; kc < d; kc += KC) {
+    const int kn = min(KC, d - kc);
+    __syncthreads();
+    // zero the stage (rows >= E and columns >= kn stay zero)
+    for (int i = tid; i < EP * LDW * (int)sizeof(TI) / 16; i += 256)
+      st16(reinterpret_cast<char*>(Wl) + 16 * i, u32x4{0u, 0u, 0u, 0u});
+    __syncthreads();
+    // W_g[kc : kc+kn, :] is contiguous: read it in 16-byte chunks, scatter transposed
+    const TI* src = Wg + (size_t)kc * E;
+    const int nchunk = kn * E / VEC;
+    for (int c = tid; c < nchunk; c += 256) {
+      u32x4 v = ld16(src + (size_t)c * VEC);
+      const TI* ve = reinterpret_cast<const TI*>(&v);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) {
+        const int flat = c * VEC + q;
+        const int kk = flat / E, n = flat - kk * E;
+        Wl[n * LDW + kk] = ve[q];
+      }
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kn; kk += ITK) {
+      u32x4 av[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kx = kk + (4 * u + g) * VEC;
+        av[u] = kx < kn ? ld16(xrow + kc + kx) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kx = kk + (4 * u + g) * VEC;
+#pragma unroll
+        for (int nb = 0; nb < EP / 16; ++nb) {
+          u32x4 bv = ld16(&Wl[(nb * 16 + (lane & 15)) * LDW + kx]);
+          M::step(acc[nb], av[u], bv);
+        }
+      }
+    }
+  }
+
+  // acc[nb][r] = logit of token (wave*16 + 4g + r), expert (nb*16 + lane%16)
+  if (ec) {
+#pragma unroll
+    for (int nb = 0; nb < EP / 16; ++nb) {
+      const int e = nb * 16 + (lane & 15);
+      if (e >= E) continue;
+      const float bz = a.bias ? a.bias[e] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wave * 16 + 4 * g + r;
+        if (t < T) a.logitsT[(size_t)e * T + t] = acc[nb][r] + bz;
+      }
+    }
+    return;
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < EP / 16; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ls[(wave * 16 + 4 * g + r) * LSP + nb * 16 + (lane & 15)] = acc[nb][r];
+  if (tid < 64) running[tid] = 0;
+  __syncthreads();
+
+  // ---- softmax and top-k: four threads per token, thread `part` owns experts part+4i
+  constexpr int PER = EP / 4;
+  const int tok = tid >> 2, part = tid & 3;
+  const int t = t0 + tok;
+  const bool valid = t < T;
+  const int k = a.k;
+  float lv[PER];
+  float lmax = -FLT_MAX;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = part + 4 * i;
+    lv[i] = -FLT_MAX;
+    if (e < E) {
+      lv[i] = Ls[tok * LSP + e] + (a.bias ? a.bias[e] : 0.f);
+      lmax = fmaxf(lmax, lv[i]);
+    }
+  }
+  lmax = fmaxf(lmax, __shfl_xor(lmax, 1));
+  lmax = fmaxf(lmax, __shfl_xor(lmax, 2));
+  float ex[PER];
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = part + 4 * i;
+    ex[i] = e < E ? expf(lv[i] - lmax) : 0.f;
+    lsum += ex[i];
+  }
+  lsum += __shfl_xor(lsum, 1);
+  lsum += __shfl_xor(lsum, 2);
+
+  // top-k by (logit desc, expert asc); every thread of the token ends with the same picks
+  uint32_t taken = 0;
+  float selp[8];
+  int sele[8];
+  for (int j = 0; j < k; ++j) {
+    float bv = -FLT_MAX;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = part + 4 * i;
+      if (e < E && !((taken >> i) & 1u) && (be == INT_MAX || lv[i] > bv)) {
+        bv = lv[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o <= 2; o <<= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      if (oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be))) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 3) == part) taken |= 1u << (be >> 2);
+    sele[j] = be;
+    selp[j] = expf(bv - lmax) / lsum;
+  }
+  if (valid) {
+    float den = 0.f;
+    if (a.renorm)
+      for (int j = 0; j < k; ++j) den += selp[j];
+    for (int j = part; j < k; j += 4) {
+      a.idx[(size_t)t * k + j] = sele[j];
+      a.w[(size_t)t * k + j] = a.renorm ? selp[j] / den : selp[j];
+    }
+    if (part == 0)
+      for (int j = 0; j < k; ++j) sel[tok * k + j] = sele[j];
+  }
+  // probabilities: to HBM (optional) and into the tile for the block sums
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = part + 4 * i;
+    if (e < E) {
+      const float pe = ex[i] / lsum;
+      if (valid && a.probs) a.probs[(size_t)t * E + e] = pe;
+      Ls[tok * LSP + e] = valid ? pe : 0.f;
+    }
+  }
+  __syncthreads();
+
+  const int nvalid = min(kRT, T - t0);
+  // per-block probability sums, fixed token order
+  if (tid < E) {
+    float s = 0.f;
+    for (int q = 0; q < kRT; ++q) s += Ls[q * LSP + tid];
+    a.blk_psum[(size_t)blockIdx.x * E + tid] = s;
+  }
+  // slot ranks within the block: wave 0 walks the slots in flattened order, 64 at a time
+  if (wave == 0) {
+    const int nent = nvalid * k;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int c0 = 0; c0 < nent; c0 += 64) {
+      const int q = c0 + lane;
+      const bool act = q < nent;
+      const int e = act ? sel[q] : 0;
+      uint64_t m = __ballot(act);
+#pragma unroll
+      for (int b = 0; b < 6; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(act && bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int before = __popcll(m & below);
+      const int r = act ? running[e] + before : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (act && before == 0) running[e] += __popcll(m);
+      if (act) a.lrank[(size_t)t0 * k + q] = r;
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  if (tid < E) a.blk_counts[(size_t)blockIdx.x * E + tid] = running[tid];
+}
+
+// ---------------------------------------------------------------------------------
+// Expert choice: one workgroup (1024 threads) per expert.
+//   column max and sum of exp over the expert's T logits (fixed-order reductions),
+//   radix select (4 x 8 bits, most significant first) of the C-th largest logit key,
+//   then a stable compaction in token order: every key above the threshold plus the
+//   first (C - above) keys equal to it.
+// ---------------------------------------------------------------------------------
+constexpr int kEcThreads = 1024;
+
+__global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __restrict__ logitsT,
+                                                               int T, int E, int C, int32_t* idx,
+                                                               float* score, float* probs,
+                                                               int32_t* offsets, int32_t* counts) {
+  __shared__ float redf[kEcThreads / 64];
+  __shared__ int hist[256];
+  __shared__ int scan_sh[17];
+  __shared__ int sel_digit, sel_need;
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const float* col = logitsT + (size_t)e * T;
+
+  // contiguous token range of this thread
+  const int per = (T + kEcThreads - 1) / kEcThreads;
+  const int tb = min(T, tid * per), te = min(T, tb + per);
+
+  float m = -FLT_MAX;
+  for (int t = tb; t < te; ++t) m = fmaxf(m, col[t]);
+  m = warp_max(m);
+  if (lane == 0) redf[wid] = m;
+  __syncthreads();
+  m = redf[0];
+  for (int i = 1; i < kEcThreads / 64; ++i) m = fmaxf(m, redf[i]);
+  __syncthreads();
+  float s = 0.f;
+  for (int t = tb; t < te; ++t) s += expf(col[t] - m);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+  if (lane == 0) redf[wid] = s;
+  __syncthreads();
+  float sum = 0.f;
+  for (int i = 0; i < kEcThreads / 64; ++i) sum += redf[i];
+
+  // radix select of the C-th largest key
+  uint32_t prefix = 0, mask = 0;
+  int need = C;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kEcThreads) hist[i] = 0;
+    __syncthreads();
+    for (int t = tb; t < te; ++t) {
+      const uint32_t key = float_key(col[t]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, b = 255;
+      for (; b > 0; --b) {
+        if (cum + hist[b] >= need) break;
+        cum += hist[b];
+      }
+      sel_digit = b;
+      sel_need = need - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel_digit << shift;
+    mask |= 255u << shift;
+    need = sel_need;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;  // key of the C-th largest logit
+  // `need` = how many keys equal to thr are taken (lowest token indices first)
+  int neq = 0;
+  for (int t = tb; t < te; ++t) neq += float_key(col[t]) == thr;
+  int tot;
+  int eq_base = block_exclusive_scan(neq, scan_sh, &tot);
+  int ntake = 0;
+  {
+    int eqr = eq_base;
+    for (int t = tb; t < te; ++t) {
+      const uint32_t key = float_key(col[t]);
+      if (key > thr) ++ntake;
+      else if (key == thr) ntake += (eqr++ < need);
+    }
+  }
+  int out = block_exclusive_scan(ntake, scan_sh, &tot);
+  {
+    int eqr = eq_base;
+    for (int t = tb; t < te; ++t) {
+      const float l = col[t];
+      const uint32_t key = float_key(l);
+      bool take = false;
+      if (key > thr) take = true;
+      else if (key == thr) take = (eqr++ < need);
+      const float sc = expf(l - m) / sum;
+      if (take && out < C) {
+        idx[(size_t)e * C + out] = t;
+        score[(size_t)e * C + out] = sc;
+        ++out;
+      }
+      if (probs) probs[(size_t)t * E + e] = sc;
+    }
+  }
+  if (tid == 0) {
+    offsets[e] = e * C;
+    if (e == E - 1) offsets[E] = E * C;
+    if (counts) counts[e] = C;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s) {
+  const int nblk = (a.T + kRT - 1) / kRT;
+  const int ep = a.E <= 16 ? 16 : (a.E <= 32 ? 32 : 64);
+  dim3 grid(nblk), block(256);
+  if (bf16in) {
+    if (ep == 16) router_kernel<bf16, 16><<<grid, block, 0, s>>>(a, ec);
+    else if (ep == 32) router_kernel<bf16, 32><<<grid, block, 0, s>>>(a, ec);
+    else router_kernel<bf16, 64><<<grid, block, 0, s>>>(a, ec);
+  } else {
+    if (ep == 16) router_kernel<float, 16><<<grid, block, 0, s>>>(a, ec);
+    else if (ep == 32) router_kernel<float, 32><<<grid, block, 0, s>>>(a, ec);
+    else router_kernel<float, 64><<<grid, block, 0, s>>>(a, ec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
+                            float* probs, int32_t* offsets, int32_t* counts, hipStream_t s) {
+  ec_select_kernel<<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets, counts);
+  return hipGetLastError();
+}

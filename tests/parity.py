@@ -1,0 +1,119 @@
+"""Helpers that compare the HIP library's outputs with the fp64 oracle.
+
+Rules (fixed before any kernel was written):
+  * routing: tokens whose oracle top-k margin p_(k) - p_(k+1) exceeds 1e-5 must pick
+    exactly the oracle's experts, in the oracle's order wherever neighbouring
+    selected probabilities differ by more than 1e-5 (ties go to the lower index).
+    Tokens with a smaller margin have several right answers: the device's choice
+    must be a valid top-k within 1e-5, and their output is checked against the
+    oracle evaluated with the device's experts. Per-expert counts over the
+    non-exempt tokens are bit-exact.
+  * fp32 layers: max|y - y_ref| / max|y_ref| <= 1e-4.
+  * bf16 layers (fp32 accumulation): max|y - y_ref| / rms(y_ref) <= 2e-2.
+  * expert choice: per expert, where the oracle's C-th vs (C+1)-th logit margin
+    exceeds 1e-5, the chosen token list is bit-exact; counts are C each.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+MARGIN = 1e-5
+TOL_FP32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def to_dev(a, dtype, dev="cuda"):
+    """float32 NumPy array (values exact in dtype) -> device tensor of dtype."""
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def device_inputs(inp, w, dev="cuda"):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {k: to_dev(inp[k], dt, dev) for k in ("x", "Wg", "Wgate", "Wup", "Wdown") if k in inp}
+    out["b"] = to_dev(inp["b"], torch.float32, dev) if inp.get("b") is not None else None
+    return out
+
+
+def check_tc_routing(idx_dev, w_dev, probs_ref, k, renormalize, w_atol=1e-5):
+    """Returns the boolean mask of exempt (near-tie) tokens after asserting the rules."""
+    idx_dev = np.asarray(idx_dev)
+    T, E = probs_ref.shape
+    idx_ref = O.topk_experts(probs_ref, k)
+    margin = O.topk_margin(probs_ref, k)
+    exempt = margin <= MARGIN
+    ok = ~exempt
+    # same set on non-exempt tokens
+    assert np.array_equal(np.sort(idx_dev[ok], axis=1), np.sort(idx_ref[ok], axis=1)), \
+        f"expert sets differ on {np.sum(np.any(np.sort(idx_dev[ok], 1) != np.sort(idx_ref[ok], 1), 1))} tokens"
+    # same order where neighbouring selected probabilities are distinct enough
+    psel = np.take_along_axis(probs_ref, idx_ref, axis=1)
+    if k > 1:
+        strict = np.all(psel[:, :-1] - psel[:, 1:] > MARGIN, axis=1) & ok
+        assert np.array_equal(idx_dev[strict], idx_ref[strict]), "slot order differs"
+    # exempt tokens: a valid top-k within the margin
+    if exempt.any():
+        pk = -np.sort(-probs_ref, axis=1)[:, k - 1]
+        pd = np.take_along_axis(probs_ref, idx_dev.astype(np.int64), axis=1)
+        assert np.all(pd[exempt] >= pk[exempt, None] - MARGIN), "near-tie token picked a non-top expert"
+        assert np.all(np.sort(idx_dev[exempt], 1)[:, 1:] != np.sort(idx_dev[exempt], 1)[:, :-1]) if k > 1 else True
+    # weights of the device's chosen experts
+    wref = O.gate_weights(probs_ref, idx_dev.astype(np.int64), renormalize)
+    err = np.max(np.abs(np.asarray(w_dev, dtype=np.float64) - wref)) if T else 0.0
+    assert err <= w_atol, f"gate weights differ by {err}"
+    return exempt
+
+
+def check_counts(counts_dev, idx_dev, idx_ref, exempt, E):
+    ok = ~exempt
+    c_dev = O.expert_counts(np.asarray(idx_dev)[ok], E)
+    c_ref = O.expert_counts(idx_ref[ok], E)
+    assert np.array_equal(c_dev, c_ref), (c_dev, c_ref)
+    if not exempt.any():
+        assert np.array_equal(np.asarray(counts_dev), c_ref)
+    else:
+        assert np.array_equal(np.asarray(counts_dev), O.expert_counts(np.asarray(idx_dev), E))
+
+
+def y_error(y_dev, y_ref, dtype):
+    y_dev = np.asarray(y_dev, dtype=np.float64)
+    diff = np.max(np.abs(y_dev - y_ref)) if y_ref.size else 0.0
+    if dtype == "fp32":
+        scale = np.max(np.abs(y_ref)) if y_ref.size else 1.0
+        return diff / max(scale, 1e-300), TOL_FP32
+    rms = np.sqrt(np.mean(y_ref ** 2)) if y_ref.size else 1.0
+    return diff / max(rms, 1e-300), TOL_BF16
+
+
+def check_y(y_dev, y_ref, dtype, what="y"):
+    err, tol = y_error(y_dev, y_ref, dtype)
+    assert err <= tol, f"{what}: normalised error {err:.3e} > {tol:.1e}"
+    return err
+
+
+def check_ec_routing(idx_dev, score_dev, ref, C):
+    """``ref`` is the oracle's forward_ec result (idx, w = scores, logits)."""
+    idx_dev = np.asarray(idx_dev)
+    logits = ref["logits"]
+    S = ref["probs"]
+    E = logits.shape[1]
+    assert idx_dev.shape == (E, C)
+    margin = O.ec_margin(logits, C)
+    for e in range(E):
+        chosen_ref = ref["idx"][e]
+        if margin[e] > MARGIN:
+            assert np.array_equal(idx_dev[e], chosen_ref), f"expert {e}: token list differs"
+        else:
+            # everything above the boundary tie group must match
+            thr = -np.sort(-logits[:, e])[C - 1]
+            sure = chosen_ref[logits[chosen_ref, e] > thr + MARGIN]
+            assert np.all(np.isin(sure, idx_dev[e])), f"expert {e}: clear picks missing"
+        assert np.all(np.diff(idx_dev[e]) > 0), f"expert {e}: tokens not ascending"
+    sref = np.take_along_axis(S.T, idx_dev.astype(np.int64), axis=1)
+    np.testing.assert_allclose(np.asarray(score_dev, dtype=np.float64), sref, rtol=1e-4, atol=1e-9)
+    return margin

@@ -1,0 +1,131 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/moe.h declares, and validates arguments on the host (these calls return
+before any HIP call, so they run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_mixture_experts_sum_amd as M
+    if not os.path.exists(M.LIB_PATH):
+        from sparse_mixture_experts_sum_amd import build
+        build.build()
+    M.load_library()
+    return M
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("moe_route", "moe_forward", "moe_aux_loss", "moe_workspace_size", "moe_capacity"):
+        assert must in names
+
+
+def test_exports_every_declared_symbol(M):
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+    assert set(declared_functions()) == set(M.EXPORTS)
+
+
+def test_status_strings(M):
+    lib = M.load_library()
+    for st in range(7):
+        assert lib.moe_status_string(st)
+    assert lib.moe_status_string(99) == b"unknown status"
+    assert lib.moe_stage_name(3) == b"gemm_gate_up"
+
+
+def _status(M, fn, *args):
+    return getattr(M.load_library(), fn)(*args)
+
+
+def test_shape_validation(M):
+    ok = M.make_shape(64, 128, 256, 8, 2)
+    assert M.workspace_size(ok) > 0
+    bad = [
+        dict(T=-1), dict(d_model=100), dict(d_ff=96), dict(E=0), dict(k=0), dict(k=9),
+    ]
+    for b in bad:
+        kw = dict(T=64, d_model=128, d_ff=256, E=8, k=2)
+        kw.update(b)
+        s = M.make_shape(**kw)
+        with pytest.raises(M.MoEError) as ei:
+            M.workspace_size(s)
+        assert ei.value.status in (2, 3)
+    s = M.make_shape(64, 128, 256, 65, 2)
+    with pytest.raises(M.MoEError) as ei:
+        M.workspace_size(s)
+    assert ei.value.status == 3  # E > 64 unsupported
+    s = M.make_shape(64, 128, 256, 16, 9)
+    with pytest.raises(M.MoEError) as ei:
+        M.workspace_size(s)
+    assert ei.value.status == 3  # k > 8 unsupported
+
+
+def test_capacity(M):
+    assert M.capacity(M.make_shape(8192, 1024, 4096, 16, mode="ec", capacity_factor=1.0)) == 512
+    assert M.capacity(M.make_shape(100, 64, 64, 8, mode="ec", capacity_factor=1.25)) == 15
+    with pytest.raises(M.MoEError):
+        M.capacity(M.make_shape(4, 64, 64, 8, mode="ec", capacity_factor=1.0))  # C = 0
+    with pytest.raises(M.MoEError):
+        M.capacity(M.make_shape(64, 64, 64, 8, mode="tc"))
+
+
+def test_workspace_offsets_are_inside(M):
+    for mode in ("tc", "ec"):
+        s = M.make_shape(1000, 256, 512, 8, 2, mode=mode)
+        n = M.workspace_size(s)
+        for which in (M.WS_OFFSETS, M.WS_SRC, M.WS_XPERM, M.WS_H, M.WS_O):
+            off = M.workspace_offset(s, which)
+            assert 0 <= off < n and off % 256 == 0
+    with pytest.raises(M.MoEError):
+        M.workspace_offset(M.make_shape(1000, 256, 512, 8, 2, mode="ec"), M.WS_POS)
+
+
+def test_forward_argument_errors_before_any_hip_call(M):
+    lib = M.load_library()
+    s = M.make_shape(64, 128, 256, 8, 2)
+    n = M.workspace_size(s)
+    P = ctypes.c_void_p
+    good = P(4096)  # never dereferenced: every call below fails validation first
+    args = dict(x=good, Wg=good, b=None, Wgate=good, Wup=good, Wdown=good, y=good)
+
+    def call(shape=s, ws=good, ws_bytes=n, **over):
+        a = dict(args)
+        a.update(over)
+        return lib.moe_forward(ctypes.byref(shape), a["x"], a["Wg"], a["b"], a["Wgate"], a["Wup"],
+                               a["Wdown"], a["y"], None, None, None, None, None, None, None, ws,
+                               ws_bytes, None)
+
+    assert call(x=None) == 1
+    assert call(Wdown=None) == 1
+    assert call(ws=None) == 1
+    assert call(y=P(4100)) == 5                      # misaligned
+    assert call(ws_bytes=n - 1) == 4                 # workspace too small
+    assert lib.moe_forward(None, *([None] * 15), 0, None) == 1
+    ec = M.make_shape(64, 128, 256, 8, mode="ec")
+    f = P(8192)
+    assert lib.moe_forward(ctypes.byref(ec), good, good, None, good, good, good, good, None, None,
+                           None, None, f, None, None, good, n, None) == 3
+    assert lib.moe_route(ctypes.byref(s), good, good, None, None, good, None, None, good, n, None) == 1
+    assert lib.moe_aux_loss(ctypes.byref(ec), good, good, good, good, good, None, good, n, None) == 3
+    assert lib.moe_aux_loss(ctypes.byref(s), good, good, None, good, good, None, good, n, None) == 1
+
+
+def test_profile_read_without_records(M):
+    M.profile_enable(False)
+    d = M.profile_read()
+    assert set(d) == set(M.stage_names()) and all(v == (0.0, 0) for v in d.values())

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every case is seeded and synthetic (workloads/), printed before it runs.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_oracle as O
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_mixture_experts_sum_amd as M
+    M.load_library()
+    return M
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def run_tc_case(M, w: W.Workload, inp=None, check_stats=True, sample=None):
+    """Run the token-choice layer on the device and check it against the oracle.
+
+    sample: if given, the number of tokens whose output the oracle evaluates
+    (routing is still checked on every token)."""
+    _say(w)
+    if inp is None:
+        inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    out = M.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        k=w.k, renormalize=w.renormalize)
+    torch.cuda.synchronize()
+    idx, wd, probs, counts = (_np(out[k]) for k in ("idx", "w", "probs", "counts"))
+    y = _np(out["y"])
+    idx_ref, w_ref, p_ref, s_ref = O.route_tc(inp["x"], inp["Wg"], inp["b"], w.k, w.renormalize)
+    np.testing.assert_allclose(probs, p_ref, rtol=0, atol=1e-5 if w.dtype == "bf16" else 1e-6)
+    exempt = PR.check_tc_routing(idx, wd, p_ref, w.k, w.renormalize)
+    PR.check_counts(counts, idx, idx_ref, exempt, w.E)
+    # reference routing: the oracle's, except near-tie tokens take the device's experts
+    idx_use = idx_ref.copy()
+    idx_use[exempt] = idx[exempt]
+    w_use = O.gate_weights(p_ref, idx_use, w.renormalize)
+    toks = np.arange(w.T)
+    if sample is not None and sample < w.T:
+        toks = np.sort(np.random.default_rng(7).choice(w.T, size=sample, replace=False))
+    y_ref = O.mix(inp["x"][toks], idx_use[toks], w_use[toks], inp["Wgate"], inp["Wup"], inp["Wdown"])
+    err = PR.check_y(y[toks], y_ref, w.dtype)
+    if check_stats:
+        f_ref, pm_ref, loss_ref, c_ref = O.aux_stats(p_ref, idx_use, w.E, w.k)
+        rt = 1e-5
+        np.testing.assert_allclose(_np(out["f"]), f_ref, rtol=1e-6, atol=0)
+        np.testing.assert_allclose(_np(out["p"]), pm_ref, rtol=rt, atol=1e-7)
+        np.testing.assert_allclose(_np(out["loss"])[0], loss_ref, rtol=rt)
+    _say(f"  ok: y err {err:.3e}, exempt tokens {int(exempt.sum())}")
+    return out, inp
+
+
+def run_ec_case(M, w: W.Workload, inp=None):
+    _say(w)
+    if inp is None:
+        inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    out = M.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        mode="ec", capacity_factor=w.cf, want_stats=False)
+    torch.cuda.synchronize()
+    ref = O.forward_ec(inp["x"], inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.cf)
+    C = w.capacity
+    margin = PR.check_ec_routing(_np(out["idx"]), _np(out["w"]), ref, C)
+    assert np.all(_np(out["counts"]) == C)
+    np.testing.assert_allclose(_np(out["probs"]), ref["probs"], rtol=1e-4, atol=1e-9)
+    if np.all(margin > PR.MARGIN):
+        y_ref = ref["y"]
+    else:  # near-tie boundary: evaluate the oracle with the device's choice
+        y_ref = O.mix_ec(inp["x"], _np(out["idx"]).astype(np.int64),
+                         np.take_along_axis(ref["probs"].T, _np(out["idx"]).astype(np.int64), 1),
+                         inp["Wgate"], inp["Wup"], inp["Wdown"])
+    err = PR.check_y(_np(out["y"]), y_ref, w.dtype)
+    _say(f"  ok: y err {err:.3e}")
+    return out, inp
+
+
+# ---------------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------------
+
+def test_config1_tiny_fp32(moe):
+    run_tc_case(moe, W.CONFIGS[1])
+
+
+def test_config2_mid_bf16(moe):
+    run_tc_case(moe, W.CONFIGS[2])
+
+
+def test_config4_fine_grained_e64_top4(moe):
+    run_tc_case(moe, W.CONFIGS[4])
+
+
+def test_config5_expert_choice(moe):
+    run_ec_case(moe, W.CONFIGS[5])
+
+
+# ---------------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 63, 65, 257, 1000])
+def test_ragged_tokens_bf16(moe, T):
+    run_tc_case(moe, W.custom(f"ragged_T{T}", T=T, d=128, f=192, E=6, k=2, seed=(42, 100 + T)))
+
+
+def test_fp32_general(moe):
+    run_tc_case(moe, W.custom("fp32_k3", dtype="fp32", T=300, d=128, f=256, E=6, k=3,
+                              x_std=0.5, wg_std=0.1, seed=(42, 201)))
+
+
+def test_all_tokens_one_expert_and_empty_experts(moe):
+    w = W.custom("collapsed", T=500, d=128, f=128, E=8, k=1, seed=(42, 202))
+    inp = W.make_inputs(w)
+    inp["b"] = np.zeros(8, dtype=np.float32)
+    inp["b"][3] = 50.0
+    out, _ = run_tc_case(moe, w, inp=inp)
+    assert _np(out["counts"]).tolist() == [0, 0, 0, 500, 0, 0, 0, 0]
+
+
+def test_single_expert(moe):
+    run_tc_case(moe, W.custom("E1k1", T=200, d=64, f=128, E=1, k=1, seed=(42, 203)))
+
+
+def test_k_equals_E_without_renormalisation_is_dense(moe):
+    w = W.custom("dense", T=128, d=64, f=64, E=4, k=4, renormalize=False, wg_std=0.5,
+                 seed=(42, 204))
+    out, inp = run_tc_case(moe, w)
+    y_dense = O.dense_mixture(inp["x"], inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"])
+    PR.check_y(_np(out["y"]), y_dense, "bf16", "dense mixture")
+
+
+def test_max_k_and_E(moe):
+    run_tc_case(moe, W.custom("E64k8", T=333, d=128, f=128, E=64, k=8, wg_std=0.2, seed=(42, 205)))
+
+
+def test_zero_input_uniform_routing(moe):
+    w = W.custom("zeros", T=70, d=64, f=64, E=8, k=3, seed=(42, 206))
+    inp = W.make_inputs(w)
+    inp["x"] = np.zeros_like(inp["x"])
+    out, _ = run_tc_case(moe, w, inp=inp)
+    assert np.all(_np(out["idx"]) == np.array([0, 1, 2]))
+    assert np.all(_np(out["y"]) == 0.0)
+    assert abs(float(_np(out["loss"])[0]) - 1.0) < 1e-6
+
+
+def test_empty_batch(moe):
+    _say("T=0")
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    Wg = torch.zeros(64, 4, dtype=torch.bfloat16, device="cuda")
+    Wgu = torch.zeros(4, 64, 64, dtype=torch.bfloat16, device="cuda")
+    out = moe.moe_forward(x, Wg, None, Wgu, Wgu.clone(), Wgu.clone(), k=2)
+    torch.cuda.synchronize()
+    assert out["y"].shape == (0, 64)
+    assert _np(out["counts"]).tolist() == [0, 0, 0, 0]
+    assert float(_np(out["loss"])[0]) == 0.0
+
+
+@pytest.mark.parametrize("T,E,cf", [(1024, 8, 1.0), (1000, 8, 1.25), (96, 1, 1.0), (512, 16, 0.5)])
+def test_expert_choice_shapes(moe, T, E, cf):
+    run_ec_case(moe, W.custom(f"ec_T{T}_E{E}_cf{cf}", T=T, d=128, f=128, E=E, mode="ec", cf=cf,
+                              k=1, seed=(42, 300 + T + E)))
+
+
+def test_determinism_bitwise(moe):
+    w = W.custom("det", T=777, d=256, f=256, E=8, k=2, seed=(42, 207))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    outs = [moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"], k=2)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for key in ("y", "idx", "w", "probs", "counts", "f", "p", "loss"):
+        assert torch.equal(outs[0][key], outs[1][key]), key
+
+
+def test_standalone_aux_loss_matches_fused(moe):
+    w = W.custom("aux", T=1500, d=128, f=64, E=16, k=4, seed=(42, 208))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    fw = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"], k=4)
+    aux = moe.moe_aux_loss(fw["probs"], fw["idx"])
+    torch.cuda.synchronize()
+    for key in ("f", "p", "loss", "counts"):
+        assert torch.equal(aux[key], fw[key]), key
+    f_ref, p_ref, loss_ref, c_ref = O.aux_stats(_np(fw["probs"]), _np(fw["idx"]), 16, 4)
+    assert _np(aux["counts"]).tolist() == c_ref.tolist()
+    np.testing.assert_allclose(_np(aux["loss"])[0], loss_ref, rtol=1e-6)
+
+
+def test_route_only_matches_forward(moe):
+    w = W.custom("route", T=640, d=192, f=64, E=12, k=3, bias_std=1.0, seed=(42, 209))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    r = moe.moe_route(dev["x"], dev["Wg"], dev["b"], k=3)
+    fw = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"], k=3)
+    torch.cuda.synchronize()
+    for key in ("idx", "w", "probs", "counts"):
+        assert torch.equal(r[key], fw[key]), key
+
+
+def test_dispatch_permutation_is_stable_bijection(moe):
+    w = W.custom("perm", T=900, d=64, f=64, E=5, k=3, seed=(42, 210))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    out = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"], k=3)
+    torch.cuda.synchronize()
+    ws, shape = out["workspace"], out["shape"]
+    R = w.T * w.k
+
+    def grab(which, n, dt):
+        off = moe.workspace_offset(shape, which)
+        nbytes = n * torch.empty(0, dtype=dt).element_size()
+        return ws[off: off + nbytes].view(dt).cpu()
+
+    pos = grab(moe.WS_POS, R, torch.int32).numpy().reshape(w.T, w.k)
+    src = grab(moe.WS_SRC, R, torch.int32).numpy()
+    offs = grab(moe.WS_OFFSETS, w.E + 1, torch.int32).numpy()
+    idx = _np(out["idx"])
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(R))            # bijection
+    assert np.array_equal(src[pos], np.repeat(np.arange(w.T)[:, None], w.k, 1))
+    for e in range(w.E):                                                # grouped + stable
+        rows = np.arange(offs[e], offs[e + 1])
+        flat = [(t * w.k + j) for t in range(w.T) for j in range(w.k) if idx[t, j] == e]
+        assert np.array_equal(pos.ravel()[flat], rows)
+    xperm = grab(moe.WS_XPERM, R * w.d, torch.bfloat16).view(R, w.d)
+    assert torch.equal(xperm, dev["x"].cpu()[torch.from_numpy(src).long()])
+
+
+# the full-size case runs last: it is the slowest
+def test_config3_mixtral_skewed_sampled(moe):
+    """Full-size Mixtral layer with a skewed router bias: routing, counts and
+    statistics on every token; outputs on a sample of tokens."""
+    w = W.CONFIGS[3]
+    out, inp = run_tc_case(moe, w, sample=96)
+    counts = _np(out["counts"])
+    assert counts.sum() == w.T * w.k
+    assert counts.max() > 1.3 * counts.mean()  # the bias skews the load
+    # dispatch invariants on the full size
+    ws = out["workspace"]
+    shape = out["shape"]
+    off = moe.workspace_offset(shape, moe.WS_OFFSETS)
+    offsets = ws[off: off + 4 * (w.E + 1)].view(torch.int32).cpu().numpy()
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))

@@ -25,6 +25,7 @@ fine-grained sub-experts with top-4 of "ç´°ç²’åº¦å°‚é–€å®¶åˆ†å‰²ãŒã‚‚ãŸã‚‰ã™è
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
@@ -115,17 +116,20 @@ def make_inputs(w: Workload, experts: bool = True) -> dict:
     kids = ss.spawn(6)
     rngs = [np.random.default_rng(s) for s in kids]
     bf = w.dtype == "bf16"
-    out = {
-        "x": _draw(rngs[0], (w.T, w.d), w.x_std, bf),
-        "Wg": _draw(rngs[1], (w.d, w.E), w.wg_std, bf),
-        "b": (rngs[2].standard_normal(w.E, dtype=np.float32) * np.float32(w.bias_std)
-              if w.bias_std is not None else None),
+    jobs = {
+        "x": lambda: _draw(rngs[0], (w.T, w.d), w.x_std, bf),
+        "Wg": lambda: _draw(rngs[1], (w.d, w.E), w.wg_std, bf),
+        "b": lambda: (rngs[2].standard_normal(w.E, dtype=np.float32) * np.float32(w.bias_std)
+                      if w.bias_std is not None else None),
     }
     if experts:
-        out["Wgate"] = _stack(rngs[3], w.E, (w.d, w.f), w.w_std, bf)
-        out["Wup"] = _stack(rngs[4], w.E, (w.d, w.f), w.w_std, bf)
-        out["Wdown"] = _stack(rngs[5], w.E, (w.f, w.d), w.w_std, bf)
-    return out
+        jobs["Wgate"] = lambda: _stack(rngs[3], w.E, (w.d, w.f), w.w_std, bf)
+        jobs["Wup"] = lambda: _stack(rngs[4], w.E, (w.d, w.f), w.w_std, bf)
+        jobs["Wdown"] = lambda: _stack(rngs[5], w.E, (w.f, w.d), w.w_std, bf)
+    # each tensor has its own stream, so drawing them concurrently changes nothing
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        futs = {k: ex.submit(fn) for k, fn in jobs.items()}
+        return {k: f.result() for k, f in futs.items()}
 
 
 def with_seed(w: Workload, seed) -> Workload:
