@@ -118,31 +118,49 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }
 
-__global__ __launch_bounds__(64) void aux_final_kernel(const int32_t* __restrict__ blk_counts,
-                                                       const float* __restrict__ blk_psum, int nblk,
-                                                       int T, int E, int k, float* f, float* p,
-                                                       float* loss, int32_t* counts) {
+// 1024 threads: thread (part, e) sums a contiguous range of blocks for expert e;
+// the 16 partial sums per expert are then added in part order (deterministic).
+constexpr int kAuxParts = 16;
+__global__ __launch_bounds__(1024) void aux_final_kernel(const int32_t* __restrict__ blk_counts,
+                                                         const float* __restrict__ blk_psum, int nblk,
+                                                         int T, int E, int k, float* f, float* p,
+                                                         float* loss, int32_t* counts) {
+  __shared__ long long csum[kAuxParts][64];
+  __shared__ double psum[kAuxParts][64];
   __shared__ double term[64];
-  const int e = threadIdx.x;
+  const int e = threadIdx.x & 63, part = threadIdx.x >> 6;
+  const int per = (nblk + kAuxParts - 1) / kAuxParts;
+  const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+  long long c = 0;
+  double ps = 0.0;
   if (e < E) {
-    long long c = 0;
-    double ps = 0.0;
-    for (int b = 0; b < nblk; ++b) {
+    for (int b = b0; b < b1; ++b) {
       c += blk_counts[(size_t)b * E + e];
       ps += (double)blk_psum[(size_t)b * E + e];
     }
-    const float fe = (float)((double)c / (double)T);
-    const float pe = (float)(ps / (double)T);
+  }
+  csum[part][e] = c;
+  psum[part][e] = ps;
+  __syncthreads();
+  if (part == 0 && e < E) {
+    long long ct = 0;
+    double pt = 0.0;
+    for (int i = 0; i < kAuxParts; ++i) {
+      ct += csum[i][e];
+      pt += psum[i][e];
+    }
+    const float fe = (float)((double)ct / (double)T);
+    const float pe = (float)(pt / (double)T);
     if (f) f[e] = fe;
     if (p) p[e] = pe;
-    if (counts) counts[e] = (int32_t)c;
+    if (counts) counts[e] = (int32_t)ct;
     term[e] = ((double)fe / (double)k) * (double)pe;
   }
   __syncthreads();
-  if (e == 0 && loss) {
-    double s = 0.0;
-    for (int i = 0; i < E; ++i) s += term[i];
-    *loss = (float)((double)E * s);
+  if (threadIdx.x == 0 && loss) {
+    double sacc = 0.0;
+    for (int i = 0; i < E; ++i) sacc += term[i];
+    *loss = (float)((double)E * sacc);
   }
 }
 
@@ -175,7 +193,7 @@ hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, in
 hipError_t launch_aux_final(const int32_t* blk_counts, const float* blk_psum, int nblk, int T,
                             int E, int k, float* f, float* p, float* loss, int32_t* counts,
                             hipStream_t s) {
-  aux_final_kernel<<<1, 64, 0, s>>>(blk_counts, blk_psum, nblk, T, E, k, f, p, loss, counts);
+  aux_final_kernel<<<1, 1024, 0, s>>>(blk_counts, blk_psum, nblk, T, E, k, f, p, loss, counts);
   return hipGetLastError();
 }
 

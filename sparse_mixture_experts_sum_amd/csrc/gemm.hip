@@ -27,26 +27,7 @@
 
 namespace {
 
-constexpr int BK = 64;
 constexpr int kGroupM = 4;  // M-tiles walked together per group of N-tiles
-
-// LDS tile rows are 64 bf16 = 8 chunks of 16 bytes; chunks are XOR-swizzled so that
-// the MFMA fragment reads (32 rows, same chunk) and the stores hit distinct banks.
-__device__ __forceinline__ int a_off(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }
-__device__ __forceinline__ int b_off(int n, int c) {
-  return n * 64 + ((c ^ ((n + (n >> 3)) & 7)) << 3);
-}
-
-// 8 rows (k) x 8 bf16 (n) in, 8 columns x 8 bf16 (k) out.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&c)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t lo = r[2 * m][j >> 1], hi = r[2 * m + 1][j >> 1];
-      c[j][m] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-}
 
 __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int E, int BM) {
   int mt = 0;
@@ -70,36 +51,179 @@ __device__ __forceinline__ void locate_mtile(const int32_t* offsets, int BM, int
   rows = min(BM, offsets[e + 1] - row0);
 }
 
-template <int BM, int BN, bool SWIGLU>
-struct Cfg {
-  static constexpr int NBL = SWIGLU ? 2 * BN : BN;  // weight columns staged per tile
-  static constexpr int WM = BM / 2, WN = BN / 2;    // per wave (2 x 2 waves)
-  static constexpr int MB = WM / 32, NB = WN / 32;  // 32x32 blocks per wave
-  static constexpr int NMAT = SWIGLU ? 2 : 1;
-  static constexpr int A_PER = BM * 8 / 256;        // 16-byte A chunks per thread per K step
-  static constexpr int B_PER = (NBL + 255) / 256;   // 8x8 weight blocks per thread per K step
-  static constexpr int LDS_A = BM * BK, LDS_B = NBL * BK;
-  static constexpr int STAGE = LDS_A + LDS_B;
-  static_assert(MB >= 1 && NB >= 1, "tile too small for 2x2 waves of 32x32 blocks");
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Tile geometry. BM rows x BNL staged weight columns per tile (SwiGLU: BNL/2 gate
+// columns then BNL/2 up columns, BNL/2 outputs), K staged in steps of 32 through a
+// ring of 4 LDS stages filled by direct global->LDS loads (each wave instruction
+// moves 64 lanes x 16 bytes into 1 KB of LDS, lane l into slot l).
+//
+// LDS layouts (per stage):
+//   A [BM][32] bf16, 64-byte rows, 16-byte chunk c stored at c ^ ((row >> 1) & 3)
+//   B [32][BNL] bf16 (k rows, n contiguous, as the weights sit in HBM), 16-byte slot
+//     s of row k stored at s ^ (2 * (k & 3))
+// MFMA operands: the A fragment is one 16-byte LDS read per lane (8 consecutive k of
+// one row); the B fragment is two ds_read_b64_tr_b16 per lane, each of which hands
+// every lane of a 16-lane group 4 consecutive k of one column: source lane i of the
+// group addresses row k0 + i/4, columns n0 + 4*(i%4) .. +3, and result lane j gets
+// element j%4 of source lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12.
+template <int BM, int BNL, bool SWIGLU, bool SPLIT>
+struct Geo {
+  static constexpr int BK = 32, STAGES = 4;
+  static constexpr int WM = BM / 2, WNL = BNL / 2;   // per wave (2 x 2 waves)
+  static constexpr int MB = WM / 32, NBW = WNL / 32; // 32x32 blocks per wave
+  static constexpr int BN_OUT = SWIGLU ? BNL / 2 : BNL;
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BNL * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int A_PW = A_BYTES / 1024 / 4;    // DMA instructions per wave per stage
+  static constexpr int B_PW = B_BYTES / 1024 / 4;
+  static constexpr int LPS = A_PW + B_PW;            // loads per wave per stage
+  static constexpr int B_ROW = BNL * 2;              // bytes per B row
+  static constexpr int B_SLOTS = BNL / 8;
+  static constexpr int B_RPI = 1024 / B_ROW;         // B rows per DMA instruction
+  static_assert(MB >= 1 && NBW >= 1 && (!SWIGLU || NBW % 2 == 0), "tile shape");
+  static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for 4-wave DMA");
+  static constexpr size_t LDS = (size_t)STAGES * STAGE_BYTES;
 };
 
-template <int BM, int BN, bool SWIGLU>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
-    const int32_t* __restrict__ offsets, int E, int K, int N, void* __restrict__ out) {
-  using C = Cfg<BM, BN, SWIGLU>;
-  extern __shared__ __attribute__((aligned(16))) bf16 lds[];
+// Direct loads of one K stage of the A and B tiles into a ring buffer.
+template <class G, bool SWIGLU, bool SPLIT>
+struct StageLoader {
+  const bf16* Ab;                 // A rows of this tile (h or x_perm)
+  const bf16* Ab2;                // second A half (SPLIT down projection)
+  const bf16* b_base[G::B_PW];    // weight matrix each B instruction reads
+  int a_src[G::A_PW];             // per-lane element offsets (row, chunk)
+  int b_src[G::B_PW];
+  int nk, N, wave;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __device__ __forceinline__ void issue(int kt, char* st) const {
+    const bool second = (SPLIT && !SWIGLU) && kt >= nk;
+    const int kk = (second ? kt - nk : kt) * G::BK;
+    const bf16* As = second ? Ab2 : Ab;
+#pragma unroll
+    for (int j = 0; j < G::A_PW; ++j)
+      __builtin_amdgcn_global_load_lds(As + kk + a_src[j],
+                                       (lds_void*)(st + (wave * G::A_PW + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < G::B_PW; ++j)
+      __builtin_amdgcn_global_load_lds(b_base[j] + (size_t)kk * N + b_src[j],
+                                       (lds_void*)(st + G::A_BYTES + (wave * G::B_PW + j) * 1024),
+                                       16, 0, 0);
+  }
+};
+
+// One K stage: wait for stage kt's loads, barrier, refill the ring three stages ahead,
+// then 2 x (fragment reads + MB x NBW MFMAs). J = kt % 4 is a template argument so
+// that every LDS access names one of the four stage arrays; FULL steps always refill,
+// so that the compiler sees the same number of loads in flight on every path.
+template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL>
+__device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ring)[4],
+                                          const StageLoader<G, SWIGLU, SPLIT>& ld,
+                                          const int (&a_frag)[G::MB][2],
+                                          const int (&b_frag)[G::NBW][2],
+                                          f32x16 (&acc)[G::NBW][G::MB]) {
+  // this wave's loads for stage kt have landed (later stages may still be in flight)
+  if constexpr (FULL) {
+    wait_vmcnt<2 * G::LPS>();
+  } else {
+    const int after = min(2, nk_total - 1 - kt);
+    if (after == 2) wait_vmcnt<2 * G::LPS>();
+    else if (after == 1) wait_vmcnt<G::LPS>();
+    else wait_vmcnt<0>();
+  }
+  // everyone's loads for stage kt have landed, and everyone is done with stage kt-1
+  __builtin_amdgcn_s_barrier();
+  if (FULL || kt + 3 < nk_total) ld.issue(kt + 3, ring[(J + 3) & 3]);  // stage kt-1's buffer
+  const char* st = ring[J];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    bf16x8 af[G::MB], bfr[G::NBW];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) af[mb] = *reinterpret_cast<const bf16x8*>(st + a_frag[mb][s]);
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb) {
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + b_frag[nb][s]));
+      const s16x4 hi4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + b_frag[nb][s] + 4 * G::B_ROW));
+      const s16x8 v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      bfr[nb] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+  }
+}
+
+template <int BM, int BNL, bool SWIGLU, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ A2, const bf16* __restrict__ B0,
+    const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N,
+    void* __restrict__ out, void* __restrict__ out2) {
+  using G = Geo<BM, BNL, SWIGLU, SPLIT>;
+  // one array per ring stage, so that the compiler can tell a stage's LDS reads from
+  // the direct loads still in flight into the other stages
+  __shared__ __attribute__((aligned(1024))) char lds0[G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds1[G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds2[G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds3[G::STAGE_BYTES];
+  char* const ring[4] = {lds0, lds1, lds2, lds3};
+  // the wave index is uniform: keep it scalar so LDS destinations stay plain offsets
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int MT = count_mtiles(offsets, E, BM);
-  const int NT = N / BN;
+  const int NT = N / G::BN_OUT;
   const int total = MT * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
   const int lo = (int)(((long long)total * xcd) >> 3);
   const int hi = (int)(((long long)total * (xcd + 1)) >> 3);
-  const int nk = K / BK;
+  const int nk = K / G::BK;
+  const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
+
+  // per-lane fragment offsets inside a stage (bytes)
+  int a_frag[G::MB][2];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int m = wm * G::WM + mb * 32 + (lane & 31);
+      const int c = (2 * s + (lane >> 5)) ^ ((m >> 1) & 3);
+      a_frag[mb][s] = m * 64 + c * 16;
+    }
+  int b_frag[G::NBW][2];
+  {
+    const int g = lane >> 4, i = lane & 15, c = i & 3, r = i >> 2;
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb) {
+      int nbase;
+      if constexpr (SWIGLU) {
+        constexpr int H = G::NBW / 2;
+        nbase = nb < H ? wn * (BNL / 4) + nb * 32 : BNL / 2 + wn * (BNL / 4) + (nb - H) * 32;
+      } else {
+        nbase = wn * G::WNL + nb * 32;
+      }
+      const int n = nbase + (g & 1) * 16 + 4 * c;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int k = 16 * s + (g >> 1) * 8 + r;
+        const int phys = (n >> 3) ^ (2 * r);
+        b_frag[nb][s] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
+      }
+    }
+  }
 
   for (int tile = lo + slot; tile < hi; tile += nslot) {
     const int grp = tile / (kGroupM * NT);
@@ -109,136 +233,115 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int nt = rem / gm, mt = m_first + rem % gm;
     int e, row0, rows;
     locate_mtile(offsets, BM, mt, e, row0, rows);
-    const int n0 = nt * BN;
+    const int n0 = nt * G::BN_OUT;
 
-    const bf16* Ab = A + (size_t)row0 * K;
+    StageLoader<G, SWIGLU, SPLIT> ld;
+    ld.Ab = A + (size_t)row0 * K;
+    ld.Ab2 = (SPLIT && !SWIGLU) ? A2 + (size_t)row0 * K : ld.Ab;
+    ld.nk = nk;
+    ld.N = N;
+    ld.wave = wave;
     const bf16* W0 = B0 + (size_t)e * K * N;
-    const bf16* W1 = SWIGLU ? B1 + (size_t)e * K * N : nullptr;
-
-    // global -> register staging
-    u32x4 ra[C::A_PER];
-    u32x4 rb[C::B_PER][8];
-    // element offsets from Ab (rows past the group's end re-read its last row)
-    int a_src[C::A_PER];
+    const bf16* W1 = SWIGLU ? B1 + (size_t)e * K * N : W0;
+    // per-lane DMA sources (element offsets, without the k step)
 #pragma unroll
-    for (int i = 0; i < C::A_PER; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      a_src[i] = min(r, rows - 1) * K + (tid & 7) * 8;
+    for (int j = 0; j < G::A_PW; ++j) {
+      const int row = (wave * G::A_PW + j) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      ld.a_src[j] = min(row, rows - 1) * K + c * 8;
     }
-    const bf16* b_src[C::B_PER];
-    int b_nl[C::B_PER], b_kg[C::B_PER];
 #pragma unroll
-    for (int j = 0; j < C::B_PER; ++j) {
-      const int bid = tid + 256 * j;
-      const int ng = bid % (C::NBL / 8), kg = bid / (C::NBL / 8);
-      const int nl = 8 * ng;
-      b_nl[j] = nl;
-      b_kg[j] = kg;
-      const bf16* W = (SWIGLU && nl >= BN) ? W1 : W0;
-      const int ncol = n0 + ((SWIGLU && nl >= BN) ? nl - BN : nl);
-      b_src[j] = W + (size_t)(8 * kg) * N + ncol;
-    }
-    auto gload = [&](int kt) {
-      const size_t koff = (size_t)kt * BK;
-#pragma unroll
-      for (int i = 0; i < C::A_PER; ++i) ra[i] = ld16(Ab + koff + a_src[i]);
-#pragma unroll
-      for (int j = 0; j < C::B_PER; ++j) {
-        if (tid + 256 * j < C::NBL) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) rb[j][q] = ld16(b_src[j] + (koff + q) * N);
-        }
+    for (int j = 0; j < G::B_PW; ++j) {
+      const int row = (wave * G::B_PW + j) * G::B_RPI + lane / G::B_SLOTS;
+      const int nl = ((lane % G::B_SLOTS) ^ (2 * (row & 3))) * 8;
+      if constexpr (SWIGLU) {
+        const bool up = nl >= BNL / 2;
+        ld.b_base[j] = up ? W1 : W0;
+        ld.b_src[j] = row * N + n0 + (up ? nl - BNL / 2 : nl);
+      } else {
+        ld.b_base[j] = W0;
+        ld.b_src[j] = row * N + n0 + nl;
       }
-    };
-    auto sstore = [&](int stage) {
-      bf16* As = lds + stage * C::STAGE;
-      bf16* Bs = As + C::LDS_A;
-#pragma unroll
-      for (int i = 0; i < C::A_PER; ++i) st16(As + a_off((tid >> 3) + 32 * i, tid & 7), ra[i]);
-#pragma unroll
-      for (int j = 0; j < C::B_PER; ++j) {
-        if (tid + 256 * j < C::NBL) {
-          u32x4 col[8];
-          transpose8x8(rb[j], col);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) st16(Bs + b_off(b_nl[j] + q, b_kg[j]), col[q]);
-        }
-      }
-    };
-
-    f32x16 acc[C::NMAT][C::NB][C::MB];
-#pragma unroll
-    for (int mt_ = 0; mt_ < C::NMAT; ++mt_)
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mt_][nb][mb][r] = 0.f;
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const bf16* As = lds + cur * C::STAGE;
-      const bf16* Bs = As + C::LDS_A;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int cc = 2 * s + (lane >> 5);
-        bf16x8 af[C::MB];
-        bf16x8 bfr[C::NMAT][C::NB];
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb) {
-          const int m = wm * C::WM + mb * 32 + (lane & 31);
-          af[mb] = __builtin_bit_cast(bf16x8, ld16(As + a_off(m, cc)));
-        }
-#pragma unroll
-        for (int mt_ = 0; mt_ < C::NMAT; ++mt_)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            const int n = mt_ * BN + wn * C::WN + nb * 32 + (lane & 31);
-            bfr[mt_][nb] = __builtin_bit_cast(bf16x8, ld16(Bs + b_off(n, cc)));
-          }
-#pragma unroll
-        for (int mt_ = 0; mt_ < C::NMAT; ++mt_)
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < C::MB; ++mb)
-              acc[mt_][nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  bfr[mt_][nb], af[mb], acc[mt_][nb][mb], 0, 0, 0);
-      }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
     }
 
-    // epilogue: acc[.][nb][mb][4q + i] = out[row = m][col = n0 + ncol0 + 8q + 4*(lane/32) + i]
+    f32x16 acc[G::NBW][G::MB];
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int nb = 0; nb < G::NBW; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        const int m = wm * C::WM + mb * 32 + (lane & 31);
-        if (m >= rows) continue;
-        const size_t rowoff = (size_t)(row0 + m) * N + n0;
+      for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ncol = wn * C::WN + nb * 32 + 8 * q + 4 * (lane >> 5);
-          if constexpr (SWIGLU) {
-            bf16x4 hv;
+        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+
+    int kt = 0;
+    if (nk_total >= 7) {
+      ld.issue(0, ring[0]);
+      ld.issue(1, ring[1]);
+      ld.issue(2, ring[2]);
+      for (; kt + 7 <= nk_total; kt += 4) {  // every step refills (kt + 6 < nk_total)
+        ring_step<G, SWIGLU, SPLIT, 0, true>(kt, nk_total, ring, ld, a_frag, b_frag, acc);
+        ring_step<G, SWIGLU, SPLIT, 1, true>(kt + 1, nk_total, ring, ld, a_frag, b_frag, acc);
+        ring_step<G, SWIGLU, SPLIT, 2, true>(kt + 2, nk_total, ring, ld, a_frag, b_frag, acc);
+        ring_step<G, SWIGLU, SPLIT, 3, true>(kt + 3, nk_total, ring, ld, a_frag, b_frag, acc);
+      }
+    } else {
+      ld.issue(0, ring[0]);
+      if (nk_total > 1) ld.issue(1, ring[1]);
+      if (nk_total > 2) ld.issue(2, ring[2]);
+    }
+    // at most 6 stages remain
+    if (kt < nk_total) ring_step<G, SWIGLU, SPLIT, 0, false>(kt, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (kt + 1 < nk_total) ring_step<G, SWIGLU, SPLIT, 1, false>(kt + 1, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (kt + 2 < nk_total) ring_step<G, SWIGLU, SPLIT, 2, false>(kt + 2, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (kt + 3 < nk_total) ring_step<G, SWIGLU, SPLIT, 3, false>(kt + 3, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (kt + 4 < nk_total) ring_step<G, SWIGLU, SPLIT, 0, false>(kt + 4, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (kt + 5 < nk_total) ring_step<G, SWIGLU, SPLIT, 1, false>(kt + 5, nk_total, ring, ld, a_frag, b_frag, acc);
+
+    // epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
+    // ncol = 8q + 4 * (lane / 32) inside 32-column block nb
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              hv[i] = (bf16)(silu(acc[0][nb][mb][4 * q + i]) * acc[1][nb][mb][4 * q + i]);
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = wm * G::WM + mb * 32 + (lane & 31);
+      if (m >= rows) continue;
+      const size_t rowoff = (size_t)(row0 + m) * N + n0;
+      if constexpr (SWIGLU) {
+        constexpr int H = G::NBW / 2;
+#pragma unroll
+        for (int nb = 0; nb < H; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ncol = wn * (BNL / 4) + nb * 32 + 8 * q + 4 * (lane >> 5);
+            bf16x4 hv, lv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float hf = silu(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
+              hv[i] = (bf16)hf;
+              if constexpr (SPLIT) lv[i] = (bf16)(hf - (float)hv[i]);
+            }
             *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + rowoff + ncol) =
                 __builtin_bit_cast(u32x2, hv);
-          } else {
-            f32x4 v = {acc[0][nb][mb][4 * q + 0], acc[0][nb][mb][4 * q + 1],
-                       acc[0][nb][mb][4 * q + 2], acc[0][nb][mb][4 * q + 3]};
+            if constexpr (SPLIT)
+              *reinterpret_cast<u32x2*>(static_cast<bf16*>(out2) + rowoff + ncol) =
+                  __builtin_bit_cast(u32x2, lv);
+            // one group of 4 outputs at a time: keeps the accumulator copies out of
+            // AGPRs from piling up in VGPRs
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (lane >> 5);
+            const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
+                             acc[nb][mb][4 * q + 3]};
             *reinterpret_cast<f32x4*>(static_cast<float*>(out) + rowoff + ncol) = v;
           }
-        }
       }
+    }
+    // stores retired and every wave past its last stage read before the next
+    // tile's loads refill the ring
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   }
 }
 
@@ -315,34 +418,43 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int BM, int BN, bool SWIGLU>
-hipError_t launch_bf16(const void* A, const void* B0, const void* B1, const int32_t* offsets, int E,
-                       int K, int N, void* out, hipStream_t s) {
-  using C = Cfg<BM, BN, SWIGLU>;
-  const size_t lds_bytes = 2 * C::STAGE * sizeof(bf16);
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_bf16_kernel<BM, BN, SWIGLU>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-    if (err != hipSuccess) return err;
-    attr_done = true;
-  }
+template <int BM, int BNL, bool SWIGLU, bool SPLIT>
+hipError_t launch_bf16(const void* A, const void* A2, const void* B0, const void* B1,
+                       const int32_t* offsets, int E, int K, int N, void* out, void* out2,
+                       hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
-  gemm_bf16_kernel<BM, BN, SWIGLU><<<grid, 256, lds_bytes, s>>>(
-      static_cast<const bf16*>(A), static_cast<const bf16*>(B0), static_cast<const bf16*>(B1),
-      offsets, E, K, N, out);
+  gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT><<<grid, 256, 0, s>>>(
+      static_cast<const bf16*>(A), static_cast<const bf16*>(A2), static_cast<const bf16*>(B0),
+      static_cast<const bf16*>(B1), offsets, E, K, N, out, out2);
   return hipGetLastError();
+}
+
+template <bool SPLIT>
+hipError_t gateup_bf16(const void* xp, const void* Wgate, const void* Wup, const int32_t* offsets,
+                       int E, int d, int f, void* h, void* h_lo, hipStream_t s) {
+  if (f % 128 == 0)
+    return launch_bf16<256, 256, true, SPLIT>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+  return launch_bf16<256, 128, true, SPLIT>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+}
+
+template <bool SPLIT>
+hipError_t down_bf16(const void* h, const void* h_lo, const void* Wdown, const int32_t* offsets,
+                     int E, int f, int d, float* o, hipStream_t s) {
+  if (d % 256 == 0)
+    return launch_bf16<256, 256, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+  if (d % 128 == 0)
+    return launch_bf16<256, 128, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+  return launch_bf16<256, 64, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_gateup(int bf16in, const void* xp, const void* Wgate, const void* Wup,
                               const int32_t* offsets, int E, int R_max, int d, int f, void* h,
-                              hipStream_t s) {
+                              void* h_lo, hipStream_t s) {
   if (bf16in) {
-    if (f % 128 == 0) return launch_bf16<256, 128, true>(xp, Wgate, Wup, offsets, E, d, f, h, s);
-    return launch_bf16<256, 64, true>(xp, Wgate, Wup, offsets, E, d, f, h, s);
+    if (h_lo) return gateup_bf16<true>(xp, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+    return gateup_bf16<false>(xp, Wgate, Wup, offsets, E, d, f, h, nullptr, s);
   }
   dim3 grid(f / 64, R_max / 64 + E);
   gemm_f32_kernel<true><<<grid, 256, 0, s>>>(static_cast<const float*>(xp),
@@ -352,12 +464,12 @@ hipError_t launch_gemm_gateup(int bf16in, const void* xp, const void* Wgate, con
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(int bf16in, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int R_max, int f, int d, float* o, hipStream_t s) {
+hipError_t launch_gemm_down(int bf16in, const void* h, const void* h_lo, const void* Wdown,
+                            const int32_t* offsets, int E, int R_max, int f, int d, float* o,
+                            hipStream_t s) {
   if (bf16in) {
-    if (d % 256 == 0) return launch_bf16<256, 256, false>(h, Wdown, nullptr, offsets, E, f, d, o, s);
-    if (d % 128 == 0) return launch_bf16<256, 128, false>(h, Wdown, nullptr, offsets, E, f, d, o, s);
-    return launch_bf16<256, 64, false>(h, Wdown, nullptr, offsets, E, f, d, o, s);
+    if (h_lo) return down_bf16<true>(h, h_lo, Wdown, offsets, E, f, d, o, s);
+    return down_bf16<false>(h, nullptr, Wdown, offsets, E, f, d, o, s);
   }
   dim3 grid(d / 64, R_max / 64 + E);
   gemm_f32_kernel<false><<<grid, 256, 0, s>>>(static_cast<const float*>(h),

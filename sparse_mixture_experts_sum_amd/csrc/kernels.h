@@ -48,12 +48,14 @@ hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
 // Grouped GEMMs over expert-contiguous rows (group e = rows [offsets[e], offsets[e+1])).
 //   gate/up: h[r] = silu(x_perm[r] W_gate[e]) * (x_perm[r] W_up[e])  -> h [R, f]
 //   down:    o[r] = h[r] W_down[e]                                   -> o [R, d] fp32
-// R_max bounds the number of routed rows (sizes the grid).
+// With h_lo non-null (bf16 only) the gate/up epilogue also writes the bf16 rounding
+// residual of h, and the down GEMM consumes h + h_lo. R_max bounds the routed rows.
 hipError_t launch_gemm_gateup(int bf16, const void* xp, const void* Wgate, const void* Wup,
                               const int32_t* offsets, int E, int R_max, int d, int f, void* h,
-                              hipStream_t s);
-hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int R_max, int f, int d, float* o, hipStream_t s);
+                              void* h_lo, hipStream_t s);
+hipError_t launch_gemm_down(int bf16, const void* h, const void* h_lo, const void* Wdown,
+                            const int32_t* offsets, int E, int R_max, int f, int d, float* o,
+                            hipStream_t s);
 
 // y[t] = sum_j w[t,j] * o[pos[t,j]]  (j in slot order)
 hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,

@@ -19,7 +19,7 @@ struct Layout {
   int64_t R = 0, C = 0;
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
-         offsets = 0, counts = 0, logitsT = 0, x_perm = 0, h = 0, o = 0, total = 0;
+         offsets = 0, counts = 0, logitsT = 0, x_perm = 0, h = 0, h_lo = 0, o = 0, total = 0;
 };
 
 int64_t ec_capacity(const moe_shape& s) {
@@ -83,6 +83,8 @@ Layout make_layout(const moe_shape& s) {
   L.src = take(L.R * 4);
   L.x_perm = take((size_t)L.R * d * eb);
   L.h = take((size_t)L.R * f * eb);
+  // expert choice, bf16: the residual of h's rounding (see launch_gemm_gateup)
+  if (s.mode == MOE_EXPERT_CHOICE && s.dtype == MOE_BF16) L.h_lo = take((size_t)L.R * f * eb);
   L.o = take((size_t)L.R * d * 4);
   L.total = cur;
   return L;
@@ -286,6 +288,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   int32_t* idx_b = idx ? idx : at<int32_t>(ws, L.idx);
   float* w_b = w ? w : at<float>(ws, L.w);
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
+  void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
   st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, ws, stream);
   if (st != MOE_OK) return st;
@@ -301,9 +304,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   }
   MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
              launch_gemm_gateup(bf, at<void>(ws, L.x_perm), W_gate, W_up, offsets, E, R, d, ff,
-                                at<void>(ws, L.h), stream));
-  MOE_LAUNCH(MOE_STAGE_GEMM_DOWN, launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, E, R,
-                                                   ff, d, at<float>(ws, L.o), stream));
+                                at<void>(ws, L.h), h_lo, stream));
+  MOE_LAUNCH(MOE_STAGE_GEMM_DOWN, launch_gemm_down(bf, at<void>(ws, L.h), h_lo, W_down, offsets, E,
+                                                   R, ff, d, at<float>(ws, L.o), stream));
   if (s.mode == MOE_TOKEN_CHOICE) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
