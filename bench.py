@@ -44,6 +44,27 @@ def stage_work(w):
     }
 
 
+def gemm_traffic_from_profile():
+    """HBM bytes per gate/up GEMM launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    scaled by the copy-kernel calibration; None when the GEMM source changed since."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "mixtral_layer_hbm_traffic.md")
+    src = os.path.join(ROOT, "sparse_mixture_experts_sum_amd", "csrc", "gemm.hip")
+    try:
+        rec = {}
+        for line in open(prof):
+            if ":" in line and line.startswith("    "):
+                k, v = line.strip().split(":", 1)
+                rec[k.strip()] = v.strip()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("gemm_source_sha256") != sha:
+            return None
+        return int(1024 * (float(rec["gemm_gate_up_fetch_kib"]) * float(rec["fetch_scale"])
+                           + float(rec["gemm_gate_up_write_kib"]) * float(rec["write_scale"])))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, inp, sample_tokens):
     """The fp64 oracle as it stands, on the first `sample_tokens` tokens."""
     from oracle import moe_oracle as O
@@ -75,10 +96,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload id (1-5); default 3")
-    ap.add_argument("--cpu-sample", type=int, default=1024,
+    ap.add_argument("--cpu-sample", type=int, default=16384,
                     help="tokens the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+                    help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -111,9 +132,11 @@ def main():
     counts = out["counts"].cpu().numpy()
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # a plain streaming kernel of known traffic (reads and writes 256 MiB each) so that
+        # HBM counters can be scaled: torch.neg on fp32
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -186,7 +209,7 @@ def main():
         "expert_gemm_frac_of_peak": round(gemm_tf / peak_tf, 4),
         "roofline": {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(gu_tf, 1),
                      "peak": peak_tf, "unit": "TFLOP/s", "frac": round(gu_tf / peak_tf, 4),
-                     "traffic": None},
+                     "traffic": gemm_traffic_from_profile() if args.config == 3 else None},
         "stages": st_out,
         "cpu_baseline": cpu,
     }

@@ -28,6 +28,7 @@
 namespace {
 
 constexpr int kGroupM = 4;  // M-tiles walked together per group of N-tiles
+constexpr int kWaves256 = 8;  // waves per workgroup for 256-column tiles (2 per SIMD)
 
 __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int E, int BM) {
   int mt = 0;
@@ -77,22 +78,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every lane of a 16-lane group 4 consecutive k of one column: source lane i of the
 // group addresses row k0 + i/4, columns n0 + 4*(i%4) .. +3, and result lane j gets
 // element j%4 of source lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12.
-template <int BM, int BNL, bool SWIGLU, bool SPLIT>
+template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 struct Geo {
   static constexpr int BK = 32, STAGES = 4;
-  static constexpr int WM = BM / 2, WNL = BNL / 2;   // per wave (2 x 2 waves)
+  static constexpr int WGN = NW / 2;                 // waves: 2 along M x WGN along N
+  static constexpr int WM = BM / 2, WNL = BNL / WGN; // per wave
   static constexpr int MB = WM / 32, NBW = WNL / 32; // 32x32 blocks per wave
   static constexpr int BN_OUT = SWIGLU ? BNL / 2 : BNL;
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BNL * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int A_PW = A_BYTES / 1024 / 4;    // DMA instructions per wave per stage
-  static constexpr int B_PW = B_BYTES / 1024 / 4;
+  static constexpr int A_PW = A_BYTES / 1024 / NW;   // DMA instructions per wave per stage
+  static constexpr int B_PW = B_BYTES / 1024 / NW;
   static constexpr int LPS = A_PW + B_PW;            // loads per wave per stage
   static constexpr int B_ROW = BNL * 2;              // bytes per B row
   static constexpr int B_SLOTS = BNL / 8;
   static constexpr int B_RPI = 1024 / B_ROW;         // B rows per DMA instruction
   static_assert(MB >= 1 && NBW >= 1 && (!SWIGLU || NBW % 2 == 0), "tile shape");
-  static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for 4-wave DMA");
+  static_assert(A_PW >= 1 && B_PW >= 1, "tile too small for the waves' DMA");
   static constexpr size_t LDS = (size_t)STAGES * STAGE_BYTES;
 };
 
@@ -166,12 +168,12 @@ __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ri
   }
 }
 
-template <int BM, int BNL, bool SWIGLU, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_kernel(
+template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A2, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N,
     void* __restrict__ out, void* __restrict__ out2) {
-  using G = Geo<BM, BNL, SWIGLU, SPLIT>;
+  using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
   // one array per ring stage, so that the compiler can tell a stage's LDS reads from
   // the direct loads still in flight into the other stages
   __shared__ __attribute__((aligned(1024))) char lds0[G::STAGE_BYTES];
@@ -182,14 +184,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the wave index is uniform: keep it scalar so LDS destinations stay plain offsets
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
 
   const int MT = count_mtiles(offsets, E, BM);
   const int NT = N / G::BN_OUT;
   const int total = MT * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  const int lo = (int)(((long long)total * xcd) >> 3);
-  const int hi = (int)(((long long)total * (xcd + 1)) >> 3);
+  // each XCD's share starts on a round boundary (nslot tiles), so that the tiles its
+  // CUs run together are one block of kGroupM M-tiles x (nslot / kGroupM) N-tiles
+  const int rounds = (total + nslot - 1) / nslot;
+  const int lo = min(total, (int)(((long long)rounds * xcd) >> 3) * nslot);
+  const int hi = min(total, (int)(((long long)rounds * (xcd + 1)) >> 3) * nslot);
   const int nk = K / G::BK;
   const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
 
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int m = wm * G::WM + mb * 32 + (lane & 31);
-      const int c = (2 * s + (lane >> 5)) ^ ((m >> 1) & 3);
+      const int c = (2 * s + (lane >> 5)) ^ (((m >> 1) ^ (m >> 3)) & 3);
       a_frag[mb][s] = m * 64 + c * 16;
     }
   int b_frag[G::NBW][2];
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       int nbase;
       if constexpr (SWIGLU) {
         constexpr int H = G::NBW / 2;
-        nbase = nb < H ? wn * (BNL / 4) + nb * 32 : BNL / 2 + wn * (BNL / 4) + (nb - H) * 32;
+        nbase = nb < H ? wn * (G::WNL / 2) + nb * 32 : BNL / 2 + wn * (G::WNL / 2) + (nb - H) * 32;
       } else {
         nbase = wn * G::WNL + nb * 32;
       }
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int k = 16 * s + (g >> 1) * 8 + r;
-        const int phys = (n >> 3) ^ (2 * r);
+        const int phys = (n >> 3) ^ (((0xCA60 >> (4 * r)) & 15) % G::B_SLOTS);
         b_frag[nb][s] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
       }
     }
@@ -247,13 +252,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int j = 0; j < G::A_PW; ++j) {
       const int row = (wave * G::A_PW + j) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      const int c = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
       ld.a_src[j] = min(row, rows - 1) * K + c * 8;
     }
 #pragma unroll
     for (int j = 0; j < G::B_PW; ++j) {
       const int row = (wave * G::B_PW + j) * G::B_RPI + lane / G::B_SLOTS;
-      const int nl = ((lane % G::B_SLOTS) ^ (2 * (row & 3))) * 8;
+      const int nl = ((lane % G::B_SLOTS) ^ (((0xCA60 >> (4 * (row & 3))) & 15) % G::B_SLOTS)) * 8;
       if constexpr (SWIGLU) {
         const bool up = nl >= BNL / 2;
         ld.b_base[j] = up ? W1 : W0;
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int nb = 0; nb < H; ++nb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int ncol = wn * (BNL / 4) + nb * 32 + 8 * q + 4 * (lane >> 5);
+            const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (lane >> 5);
             bf16x4 hv, lv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -418,12 +423,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int BM, int BNL, bool SWIGLU, bool SPLIT>
+template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 hipError_t launch_bf16(const void* A, const void* A2, const void* B0, const void* B1,
                        const int32_t* offsets, int E, int K, int N, void* out, void* out2,
                        hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
-  gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT><<<grid, 256, 0, s>>>(
+  gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW><<<grid, 64 * NW, 0, s>>>(
       static_cast<const bf16*>(A), static_cast<const bf16*>(A2), static_cast<const bf16*>(B0),
       static_cast<const bf16*>(B1), offsets, E, K, N, out, out2);
   return hipGetLastError();
@@ -433,18 +438,18 @@ template <bool SPLIT>
 hipError_t gateup_bf16(const void* xp, const void* Wgate, const void* Wup, const int32_t* offsets,
                        int E, int d, int f, void* h, void* h_lo, hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
-  return launch_bf16<256, 128, true, SPLIT>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+  return launch_bf16<256, 128, true, SPLIT, 4>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
 }
 
 template <bool SPLIT>
 hipError_t down_bf16(const void* h, const void* h_lo, const void* Wdown, const int32_t* offsets,
                      int E, int f, int d, float* o, hipStream_t s) {
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+    return launch_bf16<256, 256, false, SPLIT, kWaves256>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
   if (d % 128 == 0)
-    return launch_bf16<256, 128, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
-  return launch_bf16<256, 64, false, SPLIT>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+    return launch_bf16<256, 128, false, SPLIT, 4>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+  return launch_bf16<256, 64, false, SPLIT, 4>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
 }
 
 }  // namespace
