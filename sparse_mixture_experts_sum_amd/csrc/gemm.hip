@@ -27,8 +27,9 @@
 
 namespace {
 
-constexpr int kGroupM = 4;  // M-tiles walked together per group of N-tiles
 constexpr int kWaves256 = 8;  // waves per workgroup for 256-column tiles (2 per SIMD)
+constexpr int kBK = 32;       // K per LDS stage
+constexpr int kStages = 4;    // LDS ring stages; kStages - 1 are in flight
 
 __device__ __forceinline__ int count_mtiles(const int32_t* offsets, int E, int BM) {
   int mt = 0;
@@ -78,9 +79,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every lane of a 16-lane group 4 consecutive k of one column: source lane i of the
 // group addresses row k0 + i/4, columns n0 + 4*(i%4) .. +3, and result lane j gets
 // element j%4 of source lanes j/4, j/4 + 4, j/4 + 8, j/4 + 12.
+// 16-byte chunk swizzles (see the layout notes above): conflict-free fragment reads for
+// 32- and 64-bank LDS. A rows hold CPR chunks (4 for K stages of 32, 8 for 64).
+template <int CPR>
+__device__ __forceinline__ int a_swz(int row) {
+  if constexpr (CPR == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+  else return (row ^ (row >> 3)) & 7;
+}
+__device__ __forceinline__ int b_swz(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }  // 0,6,10,12
+
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 struct Geo {
-  static constexpr int BK = 32, STAGES = 4;
+  static constexpr int BK = kBK, STAGES = kStages;
+  static constexpr int SUB = BK / 16;                // 16-deep MFMA substeps per stage
+  static constexpr int A_CPR = BK / 8;               // 16-byte chunks per A row
+  static constexpr int A_RPI = 1024 / (BK * 2);      // A rows per DMA instruction
   static constexpr int WGN = NW / 2;                 // waves: 2 along M x WGN along N
   static constexpr int WM = BM / 2, WNL = BNL / WGN; // per wave
   static constexpr int MB = WM / 32, NBW = WNL / 32; // 32x32 blocks per wave
@@ -124,39 +137,43 @@ struct StageLoader {
   }
 };
 
-// One K stage: wait for stage kt's loads, barrier, refill the ring three stages ahead,
-// then 2 x (fragment reads + MB x NBW MFMAs). J = kt % 4 is a template argument so
-// that every LDS access names one of the four stage arrays; FULL steps always refill,
-// so that the compiler sees the same number of loads in flight on every path.
+// s_waitcnt vmcnt(n * PER) for a runtime n in [0, 2]
+template <int PER>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 2) wait_vmcnt<2 * PER>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<0>();
+}
+
+// One K stage: wait for stage kt's loads, barrier, refill the ring STAGES - 1 stages
+// ahead, then SUB x (fragment reads + MB x NBW MFMAs). J = kt % STAGES is a template
+// argument so that every LDS access names one of the stage arrays; FULL steps always
+// refill, so that the compiler sees the same number of loads in flight on every path.
 template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL>
-__device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ring)[4],
+__device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ring)[G::STAGES],
                                           const StageLoader<G, SWIGLU, SPLIT>& ld,
-                                          const int (&a_frag)[G::MB][2],
-                                          const int (&b_frag)[G::NBW][2],
+                                          const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
                                           f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr int AHEAD = G::STAGES - 1;
+  static_assert(AHEAD >= 1 && AHEAD <= 3, "ring depth");
   // this wave's loads for stage kt have landed (later stages may still be in flight)
-  if constexpr (FULL) {
-    wait_vmcnt<2 * G::LPS>();
-  } else {
-    const int after = min(2, nk_total - 1 - kt);
-    if (after == 2) wait_vmcnt<2 * G::LPS>();
-    else if (after == 1) wait_vmcnt<G::LPS>();
-    else wait_vmcnt<0>();
-  }
+  if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
+  else wait_stages<G::LPS>(min(AHEAD - 1, nk_total - 1 - kt));
   // everyone's loads for stage kt have landed, and everyone is done with stage kt-1
   __builtin_amdgcn_s_barrier();
-  if (FULL || kt + 3 < nk_total) ld.issue(kt + 3, ring[(J + 3) & 3]);  // stage kt-1's buffer
+  if (FULL || kt + AHEAD < nk_total) ld.issue(kt + AHEAD, ring[(J + AHEAD) % G::STAGES]);
   const char* st = ring[J];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < G::SUB; ++s) {
     bf16x8 af[G::MB], bfr[G::NBW];
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) af[mb] = *reinterpret_cast<const bf16x8*>(st + a_frag[mb][s]);
+    for (int mb = 0; mb < G::MB; ++mb)
+      af[mb] = *reinterpret_cast<const bf16x8*>(st + (a_frag[mb] ^ (32 * s)));
 #pragma unroll
     for (int nb = 0; nb < G::NBW; ++nb) {
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + b_frag[nb][s]));
-      const s16x4 hi4 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(st + b_frag[nb][s] + 4 * G::B_ROW));
+      const char* bp = st + b_frag[nb] + 16 * s * G::B_ROW;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bp);
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp + 4 * G::B_ROW));
       const s16x8 v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       bfr[nb] = __builtin_bit_cast(bf16x8, v);
     }
@@ -165,6 +182,9 @@ __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ri
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
         acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb], acc[nb][mb], 0, 0, 0);
+    // keep the scheduler from hoisting more than two substeps' fragment reads (register
+    // pressure) when a stage holds more than 32 of K
+    if (s % 2 == 1 && s + 1 < G::SUB) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -178,37 +198,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // the direct loads still in flight into the other stages
   __shared__ __attribute__((aligned(1024))) char lds0[G::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds1[G::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds2[G::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds3[G::STAGE_BYTES];
-  char* const ring[4] = {lds0, lds1, lds2, lds3};
+  __shared__ __attribute__((aligned(1024))) char lds2[G::STAGES > 2 ? G::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char lds3[G::STAGES > 3 ? G::STAGE_BYTES : 16];
+  char* const ring4[4] = {lds0, lds1, lds2, lds3};
+  char* ring[G::STAGES];
+#pragma unroll
+  for (int i = 0; i < G::STAGES; ++i) ring[i] = ring4[i];
   // the wave index is uniform: keep it scalar so LDS destinations stay plain offsets
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
 
-  const int MT = count_mtiles(offsets, E, BM);
   const int NT = N / G::BN_OUT;
-  const int total = MT * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  // each XCD's share starts on a round boundary (nslot tiles), so that the tiles its
-  // CUs run together are one block of kGroupM M-tiles x (nslot / kGroupM) N-tiles
-  const int rounds = (total + nslot - 1) / nslot;
-  const int lo = min(total, (int)(((long long)rounds * xcd) >> 3) * nslot);
-  const int hi = min(total, (int)(((long long)rounds * (xcd + 1)) >> 3) * nslot);
+  // Experts are processed one after another by all XCDs together: XCD x takes the
+  // x-th eighth of each expert's tiles listed N-tile-major, i.e. mostly its own slice
+  // of the expert's weight columns, for all of the expert's rows.
+  int my_total = 0;
+  for (int e = 0; e < E; ++e) {
+    const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
+    my_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
+  }
   const int nk = K / G::BK;
   const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
 
-  // per-lane fragment offsets inside a stage (bytes)
-  int a_frag[G::MB][2];
+  // per-lane fragment offsets inside a stage (bytes) for substep 0. Substep s reads A
+  // chunk 2s + lane / 32 (swizzled), i.e. offset a_frag ^ 32 s (the chunk bits lie below
+  // the row bits), and B rows 16 s further down, i.e. offset b_frag + 16 s B_ROW.
+  int a_frag[G::MB];
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int m = wm * G::WM + mb * 32 + (lane & 31);
-      const int c = (2 * s + (lane >> 5)) ^ (((m >> 1) ^ (m >> 3)) & 3);
-      a_frag[mb][s] = m * 64 + c * 16;
-    }
-  int b_frag[G::NBW][2];
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int m = wm * G::WM + mb * 32 + (lane & 31);
+    a_frag[mb] = m * (G::BK * 2) + ((lane >> 5) ^ a_swz<G::A_CPR>(m)) * 16;
+  }
+  int b_frag[G::NBW];
   {
     const int g = lane >> 4, i = lane & 15, c = i & 3, r = i >> 2;
 #pragma unroll
@@ -221,23 +244,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         nbase = wn * G::WNL + nb * 32;
       }
       const int n = nbase + (g & 1) * 16 + 4 * c;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int k = 16 * s + (g >> 1) * 8 + r;
-        const int phys = (n >> 3) ^ (((0xCA60 >> (4 * r)) & 15) % G::B_SLOTS);
-        b_frag[nb][s] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
-      }
+      const int k = (g >> 1) * 8 + r;
+      const int phys = (n >> 3) ^ (b_swz(k) % G::B_SLOTS);  // the same for k + 4 and k + 16 s
+      b_frag[nb] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
     }
   }
 
-  for (int tile = lo + slot; tile < hi; tile += nslot) {
-    const int grp = tile / (kGroupM * NT);
-    const int m_first = grp * kGroupM;
-    const int gm = min(kGroupM, MT - m_first);
-    const int rem = tile - grp * kGroupM * NT;
-    const int nt = rem / gm, mt = m_first + rem % gm;
-    int e, row0, rows;
-    locate_mtile(offsets, BM, mt, e, row0, rows);
+  for (int i = slot; i < my_total; i += nslot) {
+    int e = 0, acc_i = 0, p = 0, mte = 1;
+    for (;; ++e) {
+      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      const long long pe = (long long)mte * NT;
+      const int plo = (int)((pe * xcd) >> 3), phi = (int)((pe * (xcd + 1)) >> 3);
+      if (i < acc_i + (phi - plo)) {
+        p = plo + (i - acc_i);
+        break;
+      }
+      acc_i += phi - plo;
+    }
+    const int nt = p / mte, mtl = p - nt * mte;
+    const int row0 = offsets[e] + mtl * BM;
+    const int rows = min(BM, offsets[e + 1] - row0);
     const int n0 = nt * G::BN_OUT;
 
     StageLoader<G, SWIGLU, SPLIT> ld;
@@ -251,14 +278,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // per-lane DMA sources (element offsets, without the k step)
 #pragma unroll
     for (int j = 0; j < G::A_PW; ++j) {
-      const int row = (wave * G::A_PW + j) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+      const int row = (wave * G::A_PW + j) * G::A_RPI + lane / G::A_CPR;
+      const int c = (lane % G::A_CPR) ^ a_swz<G::A_CPR>(row);
       ld.a_src[j] = min(row, rows - 1) * K + c * 8;
     }
 #pragma unroll
     for (int j = 0; j < G::B_PW; ++j) {
       const int row = (wave * G::B_PW + j) * G::B_RPI + lane / G::B_SLOTS;
-      const int nl = ((lane % G::B_SLOTS) ^ (((0xCA60 >> (4 * (row & 3))) & 15) % G::B_SLOTS)) * 8;
+      const int nl = ((lane % G::B_SLOTS) ^ (b_swz(row) % G::B_SLOTS)) * 8;
       if constexpr (SWIGLU) {
         const bool up = nl >= BNL / 2;
         ld.b_base[j] = up ? W1 : W0;
@@ -277,29 +304,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 
+#define MOE_STEP(J, FULL, KT) \
+  ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
+    constexpr int S = G::STAGES;
     int kt = 0;
-    if (nk_total >= 7) {
-      ld.issue(0, ring[0]);
-      ld.issue(1, ring[1]);
-      ld.issue(2, ring[2]);
-      for (; kt + 7 <= nk_total; kt += 4) {  // every step refills (kt + 6 < nk_total)
-        ring_step<G, SWIGLU, SPLIT, 0, true>(kt, nk_total, ring, ld, a_frag, b_frag, acc);
-        ring_step<G, SWIGLU, SPLIT, 1, true>(kt + 1, nk_total, ring, ld, a_frag, b_frag, acc);
-        ring_step<G, SWIGLU, SPLIT, 2, true>(kt + 2, nk_total, ring, ld, a_frag, b_frag, acc);
-        ring_step<G, SWIGLU, SPLIT, 3, true>(kt + 3, nk_total, ring, ld, a_frag, b_frag, acc);
+    if (nk_total >= 2 * S - 1) {
+#pragma unroll
+      for (int i = 0; i < S - 1; ++i) ld.issue(i, ring[i]);
+      for (; kt + 2 * S - 1 <= nk_total; kt += S) {  // every step refills
+        MOE_STEP(0, true, kt);
+        MOE_STEP(1, true, kt + 1);
+        if constexpr (S > 2) MOE_STEP(2 % S, true, kt + 2);
+        if constexpr (S > 3) MOE_STEP(3 % S, true, kt + 3);
       }
     } else {
-      ld.issue(0, ring[0]);
-      if (nk_total > 1) ld.issue(1, ring[1]);
-      if (nk_total > 2) ld.issue(2, ring[2]);
+#pragma unroll
+      for (int i = 0; i < S - 1; ++i)
+        if (i < nk_total) ld.issue(i, ring[i]);
     }
-    // at most 6 stages remain
-    if (kt < nk_total) ring_step<G, SWIGLU, SPLIT, 0, false>(kt, nk_total, ring, ld, a_frag, b_frag, acc);
-    if (kt + 1 < nk_total) ring_step<G, SWIGLU, SPLIT, 1, false>(kt + 1, nk_total, ring, ld, a_frag, b_frag, acc);
-    if (kt + 2 < nk_total) ring_step<G, SWIGLU, SPLIT, 2, false>(kt + 2, nk_total, ring, ld, a_frag, b_frag, acc);
-    if (kt + 3 < nk_total) ring_step<G, SWIGLU, SPLIT, 3, false>(kt + 3, nk_total, ring, ld, a_frag, b_frag, acc);
-    if (kt + 4 < nk_total) ring_step<G, SWIGLU, SPLIT, 0, false>(kt + 4, nk_total, ring, ld, a_frag, b_frag, acc);
-    if (kt + 5 < nk_total) ring_step<G, SWIGLU, SPLIT, 1, false>(kt + 5, nk_total, ring, ld, a_frag, b_frag, acc);
+    // at most 2 * S - 2 stages remain
+    if (kt < nk_total) MOE_STEP(0, false, kt);
+    if (kt + 1 < nk_total) MOE_STEP(1 % S, false, kt + 1);
+    if constexpr (S > 2) {
+      if (kt + 2 < nk_total) MOE_STEP(2 % S, false, kt + 2);
+      if (kt + 3 < nk_total) MOE_STEP(3 % S, false, kt + 3);
+    }
+    if constexpr (S > 3) {
+      if (kt + 4 < nk_total) MOE_STEP(4 % S, false, kt + 4);
+      if (kt + 5 < nk_total) MOE_STEP(5 % S, false, kt + 5);
+    }
+#undef MOE_STEP
 
     // epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
     // ncol = 8q + 4 * (lane / 32) inside 32-column block nb
