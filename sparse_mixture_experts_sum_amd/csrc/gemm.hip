@@ -65,6 +65,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+
+// Workgroup barrier that the instruction scheduler does not move code across.
+__device__ __forceinline__ void sync_point() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Tile geometry. BM rows x BNL staged weight columns per tile (SwiGLU: BNL/2 gate
 // columns then BNL/2 up columns, BNL/2 outputs), K staged in steps of 32 through a
 // ring of 4 LDS stages filled by direct global->LDS loads (each wave instruction
@@ -188,6 +198,125 @@ __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ri
   }
 }
 
+// Ping-pong K stage for two waves per SIMD. The two waves of a SIMD run the same stage
+// half a stage apart: while one issues its 16 MFMAs, the other reads its fragments of
+// the stage from LDS and refills the ring, and at the next barrier they swap. Every
+// wave passes two barriers per stage; the "second" wave of each SIMD passes one extra
+// barrier at the start of a tile and the first one extra at the end, which sets the
+// offset. Correctness (for any split of the waves into the two roles):
+//  - before any wave reads stage kt, every wave has waited for its own loads of stage
+//    kt: first waves just before their read barrier, second waves before the barrier
+//    that ends their reads of stage kt-1 (which is the first waves' read barrier of kt);
+//  - a wave refills the buffer of stage kt-1 only after the barrier that follows every
+//    wave's reads of stage kt-1 (reads are complete at lgkmcnt(0) before that barrier);
+//    the MFMA phase reads registers only.
+template <class G, bool SWIGLU, bool SPLIT, bool SECOND, int J, bool FULL>
+__device__ __forceinline__ void pp_step(int kt, int nk_total,
+                                        char* const (&ring)[G::STAGES],
+                                        const StageLoader<G, SWIGLU, SPLIT>& ld,
+                                        const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
+                                        f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr int AHEAD = G::STAGES - 1;
+  static_assert(AHEAD >= 1 && AHEAD <= 3, "ring depth");
+  __builtin_amdgcn_sched_barrier(0);  // the wait stays after the previous MFMA phase
+  if constexpr (!SECOND) {  // own loads of stage kt (kt .. kt + AHEAD - 1 may be in flight)
+    if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
+    else wait_stages<G::LPS>(min(AHEAD - 1, nk_total - 1 - kt));
+  }
+  sync_point();
+  const char* st = ring[J];
+  bf16x8 af[G::SUB][G::MB], bfr[G::SUB][G::NBW];
+#pragma unroll
+  for (int s = 0; s < G::SUB; ++s) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+      af[s][mb] = *reinterpret_cast<const bf16x8*>(st + (a_frag[mb] ^ (32 * s)));
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb) {
+      const char* bp = st + b_frag[nb] + 16 * s * G::B_ROW;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bp);
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp + 4 * G::B_ROW));
+      const s16x8 v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      bfr[s][nb] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // refill after the reads: keeps the compiler from ordering a wait for the new loads
+  // in front of the reads
+  __builtin_amdgcn_sched_barrier(0);
+  if (FULL || kt + AHEAD < nk_total) ld.issue(kt + AHEAD, ring[(J + AHEAD) % G::STAGES]);
+  wait_lgkmcnt0();
+  if constexpr (SECOND) {  // own loads of stage kt + 1 (kt + 1 .. kt + AHEAD may be in flight)
+    if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
+    else wait_stages<G::LPS>(max(0, min(AHEAD - 1, nk_total - 2 - kt)));
+  }
+  sync_point();
+#pragma unroll
+  for (int s = 0; s < G::SUB; ++s)
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][nb], af[s][mb], acc[nb][mb], 0, 0, 0);
+}
+
+// The K loop of one tile. ROLE 0: every wave runs ring_step; ROLE 1 / 2: the first /
+// second wave of a SIMD in the ping-pong schedule (compiled separately, so that each
+// role's waits are fixed at compile time).
+template <class G, bool SWIGLU, bool SPLIT, int ROLE>
+__device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAGES],
+                                       const StageLoader<G, SWIGLU, SPLIT>& ld,
+                                       const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
+                                       f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr int S = G::STAGES;
+  int kt = 0;
+#define MOE_STEP(J, FULL, KT)                                                                 \
+  if constexpr (ROLE == 0)                                                                    \
+    ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc);        \
+  else                                                                                        \
+    pp_step<G, SWIGLU, SPLIT, ROLE == 2, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
+  // Prologue: stages 0 .. S-2 in flight; the second ping-pong waves then wait for their
+  // stage 0 and pass their extra barrier. The main loop (every step refills) sits in the
+  // same branch as an unconditional prologue, so that the compiler sees the same loads
+  // in flight on every path into it. At most 2 * S - 2 stages remain after it.
+  if (nk_total >= 2 * S - 1) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) ld.issue(i, ring[i]);
+    if constexpr (ROLE == 2) {
+      wait_vmcnt<(S - 2) * G::LPS>();
+      sync_point();
+    }
+    for (; kt + 2 * S - 1 <= nk_total; kt += S) {
+      MOE_STEP(0, true, kt);
+      MOE_STEP(1, true, kt + 1);
+      if constexpr (S > 2) { MOE_STEP(2 % S, true, kt + 2); }
+      if constexpr (S > 3) { MOE_STEP(3 % S, true, kt + 3); }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      if (i < nk_total) ld.issue(i, ring[i]);
+    if constexpr (ROLE == 2) {
+      wait_stages<G::LPS>(min(S - 2, nk_total - 1));
+      sync_point();
+    }
+  }
+  if (kt < nk_total) { MOE_STEP(0, false, kt); }
+  if (kt + 1 < nk_total) { MOE_STEP(1 % S, false, kt + 1); }
+  if constexpr (S > 2) {
+    if (kt + 2 < nk_total) { MOE_STEP(2 % S, false, kt + 2); }
+    if (kt + 3 < nk_total) { MOE_STEP(3 % S, false, kt + 3); }
+  }
+  if constexpr (S > 3) {
+    if (kt + 4 < nk_total) { MOE_STEP(4 % S, false, kt + 4); }
+    if (kt + 5 < nk_total) { MOE_STEP(5 % S, false, kt + 5); }
+  }
+#undef MOE_STEP
+  // Every load of the tile has landed by now (each role's last wait was for its last
+  // stage); saying so keeps the compiler's load tracking exact into the next tile.
+  if constexpr (ROLE != 0) wait_vmcnt<0>();
+  if constexpr (ROLE == 1) sync_point();  // the first waves' extra barrier
+}
+
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A2, const bf16* __restrict__ B0,
@@ -208,6 +337,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
+  // ping-pong roles for two waves per SIMD: the second wave (by index) on each SIMD
+  constexpr bool PP = NW == 8;
+  bool second = false;
+  if constexpr (PP) {
+    __shared__ int simd_of[NW];
+    // HW_ID bits 5:4 hold the SIMD the wave runs on
+    if (lane == 0) simd_of[wave] = (int)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+    __syncthreads();
+    int rank = 0;
+    for (int w = 0; w < wave; ++w) rank += simd_of[w] == simd_of[wave];
+    second = __builtin_amdgcn_readfirstlane(rank & 1) != 0;
+  }
 
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
@@ -304,36 +445,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 
-#define MOE_STEP(J, FULL, KT) \
-  ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
-    constexpr int S = G::STAGES;
-    int kt = 0;
-    if (nk_total >= 2 * S - 1) {
-#pragma unroll
-      for (int i = 0; i < S - 1; ++i) ld.issue(i, ring[i]);
-      for (; kt + 2 * S - 1 <= nk_total; kt += S) {  // every step refills
-        MOE_STEP(0, true, kt);
-        MOE_STEP(1, true, kt + 1);
-        if constexpr (S > 2) MOE_STEP(2 % S, true, kt + 2);
-        if constexpr (S > 3) MOE_STEP(3 % S, true, kt + 3);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S - 1; ++i)
-        if (i < nk_total) ld.issue(i, ring[i]);
-    }
-    // at most 2 * S - 2 stages remain
-    if (kt < nk_total) MOE_STEP(0, false, kt);
-    if (kt + 1 < nk_total) MOE_STEP(1 % S, false, kt + 1);
-    if constexpr (S > 2) {
-      if (kt + 2 < nk_total) MOE_STEP(2 % S, false, kt + 2);
-      if (kt + 3 < nk_total) MOE_STEP(3 % S, false, kt + 3);
-    }
-    if constexpr (S > 3) {
-      if (kt + 4 < nk_total) MOE_STEP(4 % S, false, kt + 4);
-      if (kt + 5 < nk_total) MOE_STEP(5 % S, false, kt + 5);
-    }
-#undef MOE_STEP
+    if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
+    else if (second) k_loop<G, SWIGLU, SPLIT, 2>(nk_total, ring, ld, a_frag, b_frag, acc);
+    else k_loop<G, SWIGLU, SPLIT, 1>(nk_total, ring, ld, a_frag, b_frag, acc);
 
     // epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
     // ncol = 8q + 4 * (lane / 32) inside 32-column block nb
@@ -377,10 +491,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           }
       }
     }
-    // stores retired and every wave past its last stage read before the next
-    // tile's loads refill the ring
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!PP) {
+      // stores retired and every wave past its last stage read before the next
+      // tile's loads refill the ring
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    }
+    // (ping-pong: every wave's reads of this tile ended before the first waves' extra
+    // barrier, which precedes both roles' next refills)
   }
 }
 
