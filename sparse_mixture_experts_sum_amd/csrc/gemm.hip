@@ -27,7 +27,7 @@
 
 namespace {
 
-constexpr int kWaves256 = 8;  // waves per workgroup for 256-column tiles (2 per SIMD)
+constexpr int kWaves256 = 4;  // waves per 256 x 256 tile: 4 = pipelined (1 per SIMD), 8 = ping-pong
 constexpr int kBK = 32;       // K per LDS stage
 constexpr int kStages = 4;    // LDS ring stages; kStages - 1 are in flight
 
@@ -63,6 +63,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// silu(z) = z * sigmoid(z) from the hardware base-2 exponential and reciprocal (about
+// 1 ulp each). The bf16 path rounds h to 8 significant bits (or keeps a 16-bit pair),
+// far coarser than these; the IEEE division and range-reduced expf would cost about
+// four times the VALU work in an epilogue that no other wave hides at one wave per SIMD.
+// Limits: z -> +inf gives z; z -> -inf gives exp2 = inf, reciprocal 0, result -0.
+__device__ __forceinline__ float silu_bf16_path(float z) {
+  const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS reads have returned
@@ -131,26 +141,46 @@ struct StageLoader {
   int b_src[G::B_PW];
   int nk, N, wave;
 
-  __device__ __forceinline__ void issue(int kt, char* st) const {
+  // load j (0 .. LPS-1: A loads, then B loads; a constant at every call) of stage kt
+  // into stage buffer st
+  __device__ __forceinline__ void issue_one(int j, int kt, char* st) const {
     const bool second = (SPLIT && !SWIGLU) && kt >= nk;
     const int kk = (second ? kt - nk : kt) * G::BK;
-    const bf16* As = second ? Ab2 : Ab;
-#pragma unroll
-    for (int j = 0; j < G::A_PW; ++j)
+    if (j < G::A_PW) {
+      const bf16* As = second ? Ab2 : Ab;
       __builtin_amdgcn_global_load_lds(As + kk + a_src[j],
                                        (lds_void*)(st + (wave * G::A_PW + j) * 1024), 16, 0, 0);
+    } else {
+      const int jb = j - G::A_PW;
+      __builtin_amdgcn_global_load_lds(b_base[jb] + (size_t)kk * N + b_src[jb],
+                                       (lds_void*)(st + G::A_BYTES + (wave * G::B_PW + jb) * 1024),
+                                       16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* st) const {
 #pragma unroll
-    for (int j = 0; j < G::B_PW; ++j)
+    for (int j = 0; j < G::A_PW; ++j) {
+      const bool second = (SPLIT && !SWIGLU) && kt >= nk;
+      const int kk = (second ? kt - nk : kt) * G::BK;
+      __builtin_amdgcn_global_load_lds((second ? Ab2 : Ab) + kk + a_src[j],
+                                       (lds_void*)(st + (wave * G::A_PW + j) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < G::B_PW; ++j) {
+      const bool second = (SPLIT && !SWIGLU) && kt >= nk;
+      const int kk = (second ? kt - nk : kt) * G::BK;
       __builtin_amdgcn_global_load_lds(b_base[j] + (size_t)kk * N + b_src[j],
                                        (lds_void*)(st + G::A_BYTES + (wave * G::B_PW + j) * 1024),
                                        16, 0, 0);
+    }
   }
 };
 
-// s_waitcnt vmcnt(n * PER) for a runtime n in [0, 2]
+// s_waitcnt vmcnt(n * PER) for a runtime n in [0, 3]
 template <int PER>
 __device__ __forceinline__ void wait_stages(int n) {
-  if (n >= 2) wait_vmcnt<2 * PER>();
+  if (n >= 3) wait_vmcnt<3 * PER>();
+  else if (n == 2) wait_vmcnt<2 * PER>();
   else if (n == 1) wait_vmcnt<PER>();
   else wait_vmcnt<0>();
 }
@@ -199,17 +229,18 @@ __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ri
 }
 
 // Ping-pong K stage for two waves per SIMD. The two waves of a SIMD run the same stage
-// half a stage apart: while one issues its 16 MFMAs, the other reads its fragments of
-// the stage from LDS and refills the ring, and at the next barrier they swap. Every
-// wave passes two barriers per stage; the "second" wave of each SIMD passes one extra
-// barrier at the start of a tile and the first one extra at the end, which sets the
-// offset. Correctness (for any split of the waves into the two roles):
+// half a stage apart: while one issues its MFMAs (with its refill loads of the ring
+// spread between them), the other reads its fragments of the stage from LDS, and at
+// the next barrier they swap. Every wave passes two barriers per stage; the "second"
+// wave of each SIMD passes one extra barrier at the start of a tile and the first one
+// extra at the end, which sets the offset. Correctness (for any split of the waves into
+// the two roles):
 //  - before any wave reads stage kt, every wave has waited for its own loads of stage
 //    kt: first waves just before their read barrier, second waves before the barrier
 //    that ends their reads of stage kt-1 (which is the first waves' read barrier of kt);
-//  - a wave refills the buffer of stage kt-1 only after the barrier that follows every
-//    wave's reads of stage kt-1 (reads are complete at lgkmcnt(0) before that barrier);
-//    the MFMA phase reads registers only.
+//  - a wave refills the buffer of stage kt-1 (with stage kt+3) only in its MFMA phase
+//    of stage kt, which follows the barrier that ends every wave's reads of stage kt-1
+//    (reads are complete at lgkmcnt(0) before that barrier); MFMAs read registers only.
 template <class G, bool SWIGLU, bool SPLIT, bool SECOND, int J, bool FULL>
 __device__ __forceinline__ void pp_step(int kt, int nk_total,
                                         char* const (&ring)[G::STAGES],
@@ -217,7 +248,7 @@ __device__ __forceinline__ void pp_step(int kt, int nk_total,
                                         const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
                                         f32x16 (&acc)[G::NBW][G::MB]) {
   constexpr int AHEAD = G::STAGES - 1;
-  static_assert(AHEAD >= 1 && AHEAD <= 3, "ring depth");
+  static_assert(AHEAD >= 2 && AHEAD <= 3, "ring depth");
   __builtin_amdgcn_sched_barrier(0);  // the wait stays after the previous MFMA phase
   if constexpr (!SECOND) {  // own loads of stage kt (kt .. kt + AHEAD - 1 may be in flight)
     if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
@@ -240,23 +271,165 @@ __device__ __forceinline__ void pp_step(int kt, int nk_total,
       bfr[s][nb] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // refill after the reads: keeps the compiler from ordering a wait for the new loads
-  // in front of the reads
-  __builtin_amdgcn_sched_barrier(0);
-  if (FULL || kt + AHEAD < nk_total) ld.issue(kt + AHEAD, ring[(J + AHEAD) % G::STAGES]);
   wait_lgkmcnt0();
-  if constexpr (SECOND) {  // own loads of stage kt + 1 (kt + 1 .. kt + AHEAD may be in flight)
-    if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
-    else wait_stages<G::LPS>(max(0, min(AHEAD - 1, nk_total - 2 - kt)));
+  if constexpr (SECOND) {  // own loads of stage kt + 1 (kt + 1 .. kt + AHEAD - 1 may be in
+                           // flight; stage kt + AHEAD is issued below)
+    if constexpr (FULL) wait_vmcnt<(AHEAD - 2) * G::LPS>();
+    else wait_stages<G::LPS>(max(0, min(AHEAD - 2, nk_total - 2 - kt)));
   }
   sync_point();
+  // MFMAs with the refill of stage kt + AHEAD spread between them: one load after every
+  // PER MFMAs keeps each wave's loads from queueing behind each other in a burst
+  constexpr int NM = G::SUB * G::NBW * G::MB;
+  constexpr int PER = NM / G::LPS;
+  static_assert(PER >= 1 && PER * G::LPS == NM, "loads per MFMA group");
+  const bool refill = FULL || kt + AHEAD < nk_total;
+  char* const dst = ring[(J + AHEAD) % G::STAGES];
+#define MOE_MFMA(I)                                                                          \
+  {                                                                                          \
+    constexpr int s = (I) / (G::NBW * G::MB), nb = (I) / G::MB % G::NBW, mb = (I) % G::MB;   \
+    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][nb], af[s][mb], acc[nb][mb], \
+                                                          0, 0, 0);                          \
+    if constexpr ((I) % PER == PER - 1) {                                                    \
+      if (refill) ld.issue_one((I) / PER, kt + AHEAD, dst);                                  \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+  }
+  static_assert(NM == 16, "MFMA phase is written out for 16 MFMAs");
+  MOE_MFMA(0) MOE_MFMA(1) MOE_MFMA(2) MOE_MFMA(3) MOE_MFMA(4) MOE_MFMA(5) MOE_MFMA(6)
+  MOE_MFMA(7) MOE_MFMA(8) MOE_MFMA(9) MOE_MFMA(10) MOE_MFMA(11) MOE_MFMA(12) MOE_MFMA(13)
+  MOE_MFMA(14) MOE_MFMA(15)
+#undef MOE_MFMA
+}
+
+// Fragments of one K stage for one wave: A as SUB x MB 8-element rows, B as the two
+// transposed 4-element halves of SUB x NBW fragments.
+template <class G>
+struct Frags {
+  bf16x8 a[G::SUB][G::MB];
+  s16x4 blo[G::SUB][G::NBW], bhi[G::SUB][G::NBW];
+};
+
+// LDS read r of a stage's fragments (r constant at every call): first the SUB x MB A
+// rows, then for each (substep, block) the two halves of the B fragment.
+template <class G>
+__device__ __forceinline__ void read_frag(int r, const char* st, const int (&a_frag)[G::MB],
+                                          const int (&b_frag)[G::NBW], Frags<G>& F) {
+  constexpr int NA = G::SUB * G::MB;
+  if (r < NA) {
+    const int s = r / G::MB, mb = r % G::MB;
+    F.a[s][mb] = *reinterpret_cast<const bf16x8*>(st + (a_frag[mb] ^ (32 * s)));
+  } else {
+    const int i = r - NA, s = i / (2 * G::NBW), nb = (i / 2) % G::NBW, h = i % 2;
+    const char* bp = st + b_frag[nb] + 16 * s * G::B_ROW + h * 4 * G::B_ROW;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bp);
+    if (h) F.bhi[s][nb] = v;
+    else F.blo[s][nb] = v;
+  }
+}
+
+template <class G>
+__device__ __forceinline__ void mfma_frag(int i, const Frags<G>& F, f32x16 (&acc)[G::NBW][G::MB]) {
+  const int s = i / (G::NBW * G::MB), nb = i / G::MB % G::NBW, mb = i % G::MB;
+  const s16x4 lo = F.blo[s][nb], hi = F.bhi[s][nb];
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), F.a[s][mb],
+                                                        acc[nb][mb], 0, 0, 0);
+}
+
+// Software-pipelined K stage for one wave per SIMD (fragments double-buffered in
+// registers). Step kt: wait for the own loads of stage kt+1 and for the own LDS reads of
+// stage kt, barrier; then the MFMAs of stage kt (fragments read in the previous step)
+// with, spread between them, the LDS reads of stage kt+1 and the refill of stage kt's
+// buffer with stage kt+STAGES. Correctness: every wave's loads of stage kt+1 have landed
+// before any wave reads it (each waits before the barrier), and every wave's reads of
+// stage kt are complete (lgkmcnt(0) before the barrier) before any wave refills its
+// buffer after the barrier.
+template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL>
+__device__ __forceinline__ void pipe_step(int kt, int nk_total, char* const (&ring)[G::STAGES],
+                                          const StageLoader<G, SWIGLU, SPLIT>& ld,
+                                          const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
+                                          f32x16 (&acc)[G::NBW][G::MB], const Frags<G>& Fc,
+                                          Frags<G>& Fn) {
+  constexpr int S = G::STAGES;
+  constexpr int NM = G::SUB * G::NBW * G::MB;                // MFMAs per stage
+  constexpr int NR = G::SUB * G::MB + 2 * G::SUB * G::NBW;   // LDS reads per stage
+  constexpr int NG = G::LPS;                                 // groups: one load each
+  static_assert(NM % NG == 0 && NR % NG == 0, "MFMA / read / load groups");
+  constexpr int MPG = NM / NG, RPG = NR / NG;
+  __builtin_amdgcn_sched_barrier(0);
+  // own loads of stage kt + 1 (kt + 1 .. kt + S - 1 may be in flight)
+  if constexpr (FULL) wait_vmcnt<(S - 2) * G::LPS>();
+  else wait_stages<G::LPS>(max(0, min(S - 2, nk_total - 2 - kt)));
+  wait_lgkmcnt0();
+  sync_point();
+  const bool more = FULL || kt + 1 < nk_total;
+  const bool refill = FULL || kt + S < nk_total;
+  const char* src = ring[(J + 1) % S];
+  char* const dst = ring[J];
 #pragma unroll
-  for (int s = 0; s < G::SUB; ++s)
+  for (int g = 0; g < NG; ++g) {
 #pragma unroll
-    for (int nb = 0; nb < G::NBW; ++nb)
+    for (int m = 0; m < MPG; ++m) mfma_frag<G>(g * MPG + m, Fc, acc);
+    if (more) {
 #pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][nb], af[s][mb], acc[nb][mb], 0, 0, 0);
+      for (int r = 0; r < RPG; ++r) read_frag<G>(g * RPG + r, src, a_frag, b_frag, Fn);
+    }
+    if (refill) ld.issue_one(g, kt + S, dst);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The K loop of one tile for one wave per SIMD (pipe_step).
+template <class G, bool SWIGLU, bool SPLIT>
+__device__ __forceinline__ void pipe_loop(int nk_total, char* const (&ring)[G::STAGES],
+                                          const StageLoader<G, SWIGLU, SPLIT>& ld,
+                                          const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
+                                          f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr int S = G::STAGES;
+  int kt = 0;
+  static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
+  Frags<G> F0, F1;
+#define MOE_PSTEP(J, FULL, KT)                                                            \
+  pipe_step<G, SWIGLU, SPLIT, (J) % S, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc, \
+                                             (J) % 2 ? F1 : F0, (J) % 2 ? F0 : F1)
+  // Prologue: the whole ring in flight, then stage 0's fragments. The main loop (every
+  // step refills) sits in the same branch as an unconditional prologue, so that the
+  // compiler sees the same loads in flight on every path into it.
+  if (nk_total >= 2 * S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) ld.issue(i, ring[i]);
+    wait_vmcnt<(S - 1) * G::LPS>();
+    sync_point();
+#pragma unroll
+    for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
+      read_frag<G>(r, ring[0], a_frag, b_frag, F0);
+    for (; kt + 2 * S - 1 < nk_total; kt += S) {
+      MOE_PSTEP(0, true, kt);
+      MOE_PSTEP(1, true, kt + 1);
+      MOE_PSTEP(2, true, kt + 2);
+      MOE_PSTEP(3, true, kt + 3);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (i < nk_total) ld.issue(i, ring[i]);
+    wait_stages<G::LPS>(min(S - 1, nk_total - 1));
+    sync_point();
+#pragma unroll
+    for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
+      read_frag<G>(r, ring[0], a_frag, b_frag, F0);
+  }
+  // at most 2 * S - 1 stages remain
+  if (kt < nk_total) { MOE_PSTEP(0, false, kt); }
+  if (kt + 1 < nk_total) { MOE_PSTEP(1, false, kt + 1); }
+  if (kt + 2 < nk_total) { MOE_PSTEP(2, false, kt + 2); }
+  if (kt + 3 < nk_total) { MOE_PSTEP(3, false, kt + 3); }
+  if (kt + 4 < nk_total) { MOE_PSTEP(4, false, kt + 4); }
+  if (kt + 5 < nk_total) { MOE_PSTEP(5, false, kt + 5); }
+  if (kt + 6 < nk_total) { MOE_PSTEP(6, false, kt + 6); }
+#undef MOE_PSTEP
+  wait_vmcnt<0>();
 }
 
 // The K loop of one tile. ROLE 0: every wave runs ring_step; ROLE 1 / 2: the first /
@@ -339,6 +512,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   // ping-pong roles for two waves per SIMD: the second wave (by index) on each SIMD
   constexpr bool PP = NW == 8;
+  // one wave per SIMD on 256 x 256 tiles: the software-pipelined loop
+  constexpr bool PIPE = NW == 4 && BM == 256 && BNL == 256;
   bool second = false;
   if constexpr (PP) {
     __shared__ int simd_of[NW];
@@ -363,35 +538,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int nk = K / G::BK;
   const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
 
-  // per-lane fragment offsets inside a stage (bytes) for substep 0. Substep s reads A
-  // chunk 2s + lane / 32 (swizzled), i.e. offset a_frag ^ 32 s (the chunk bits lie below
-  // the row bits), and B rows 16 s further down, i.e. offset b_frag + 16 s B_ROW.
-  int a_frag[G::MB];
-#pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    const int m = wm * G::WM + mb * 32 + (lane & 31);
-    a_frag[mb] = m * (G::BK * 2) + ((lane >> 5) ^ a_swz<G::A_CPR>(m)) * 16;
-  }
-  int b_frag[G::NBW];
-  {
-    const int g = lane >> 4, i = lane & 15, c = i & 3, r = i >> 2;
-#pragma unroll
-    for (int nb = 0; nb < G::NBW; ++nb) {
-      int nbase;
-      if constexpr (SWIGLU) {
-        constexpr int H = G::NBW / 2;
-        nbase = nb < H ? wn * (G::WNL / 2) + nb * 32 : BNL / 2 + wn * (G::WNL / 2) + (nb - H) * 32;
-      } else {
-        nbase = wn * G::WNL + nb * 32;
-      }
-      const int n = nbase + (g & 1) * 16 + 4 * c;
-      const int k = (g >> 1) * 8 + r;
-      const int phys = (n >> 3) ^ (b_swz(k) % G::B_SLOTS);  // the same for k + 4 and k + 16 s
-      b_frag[nb] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
-    }
-  }
-
   for (int i = slot; i < my_total; i += nslot) {
+    // Per-tile copies of per-lane constants, from the lane id that mbcnt rebuilds without
+    // any register: recomputing them (a few VALU ops per tile) is cheaper than keeping
+    // them live through the K loop, where registers are short, and reloading spills.
+    int ln;  // volatile: rebuilt in every tile, never hoisted out of the tile loop
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    // per-lane fragment offsets inside a stage (bytes) for substep 0. Substep s reads A
+    // chunk 2s + lane / 32 (swizzled), i.e. offset a_frag ^ 32 s (the chunk bits lie below
+    // the row bits), and B rows 16 s further down, i.e. offset b_frag + 16 s B_ROW.
+    int a_frag[G::MB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int m = wm * G::WM + mb * 32 + (ln & 31);
+      a_frag[mb] = m * (G::BK * 2) + ((ln >> 5) ^ a_swz<G::A_CPR>(m)) * 16;
+    }
+    int b_frag[G::NBW];
+    {
+      const int g = ln >> 4, i = ln & 15, c = i & 3, r = i >> 2;
+#pragma unroll
+      for (int nb = 0; nb < G::NBW; ++nb) {
+        int nbase;
+        if constexpr (SWIGLU) {
+          constexpr int H = G::NBW / 2;
+          nbase = nb < H ? wn * (G::WNL / 2) + nb * 32 : BNL / 2 + wn * (G::WNL / 2) + (nb - H) * 32;
+        } else {
+          nbase = wn * G::WNL + nb * 32;
+        }
+        const int n = nbase + (g & 1) * 16 + 4 * c;
+        const int k = (g >> 1) * 8 + r;
+        const int phys = (n >> 3) ^ (b_swz(k) % G::B_SLOTS);  // the same for k + 4 and k + 16 s
+        b_frag[nb] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
+      }
+    }
+
     int e = 0, acc_i = 0, p = 0, mte = 1;
     for (;; ++e) {
       mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
@@ -419,14 +599,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // per-lane DMA sources (element offsets, without the k step)
 #pragma unroll
     for (int j = 0; j < G::A_PW; ++j) {
-      const int row = (wave * G::A_PW + j) * G::A_RPI + lane / G::A_CPR;
-      const int c = (lane % G::A_CPR) ^ a_swz<G::A_CPR>(row);
+      const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
+      const int c = (ln % G::A_CPR) ^ a_swz<G::A_CPR>(row);
       ld.a_src[j] = min(row, rows - 1) * K + c * 8;
     }
 #pragma unroll
     for (int j = 0; j < G::B_PW; ++j) {
-      const int row = (wave * G::B_PW + j) * G::B_RPI + lane / G::B_SLOTS;
-      const int nl = ((lane % G::B_SLOTS) ^ (b_swz(row) % G::B_SLOTS)) * 8;
+      const int row = (wave * G::B_PW + j) * G::B_RPI + ln / G::B_SLOTS;
+      const int nl = ((ln % G::B_SLOTS) ^ (b_swz(row) % G::B_SLOTS)) * 8;
       if constexpr (SWIGLU) {
         const bool up = nl >= BNL / 2;
         ld.b_base[j] = up ? W1 : W0;
@@ -445,7 +625,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 
-    if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
+    if constexpr (PIPE) pipe_loop<G, SWIGLU, SPLIT>(nk_total, ring, ld, a_frag, b_frag, acc);
+    else if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
     else if (second) k_loop<G, SWIGLU, SPLIT, 2>(nk_total, ring, ld, a_frag, b_frag, acc);
     else k_loop<G, SWIGLU, SPLIT, 1>(nk_total, ring, ld, a_frag, b_frag, acc);
 
@@ -453,7 +634,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // ncol = 8q + 4 * (lane / 32) inside 32-column block nb
 #pragma unroll
     for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = wm * G::WM + mb * 32 + (lane & 31);
+      const int m = wm * G::WM + mb * 32 + (ln & 31);
       if (m >= rows) continue;
       const size_t rowoff = (size_t)(row0 + m) * N + n0;
       if constexpr (SWIGLU) {
@@ -462,11 +643,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         for (int nb = 0; nb < H; ++nb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (lane >> 5);
+            const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (ln >> 5);
             bf16x4 hv, lv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float hf = silu(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
+              const float hf = silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
               hv[i] = (bf16)hf;
               if constexpr (SPLIT) lv[i] = (bf16)(hf - (float)hv[i]);
             }
@@ -484,14 +665,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
         for (int nb = 0; nb < G::NBW; ++nb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (lane >> 5);
+            const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (ln >> 5);
             const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
                              acc[nb][mb][4 * q + 3]};
             *reinterpret_cast<f32x4*>(static_cast<float*>(out) + rowoff + ncol) = v;
           }
       }
     }
-    if constexpr (!PP) {
+    if constexpr (!PP && !PIPE) {
       // stores retired and every wave past its last stage read before the next
       // tile's loads refill the ring
       wait_vmcnt<0>();
