@@ -176,6 +176,9 @@ struct StageLoader {
   }
 };
 
+// min(max(n, 0), 2): stages that may stay in flight after the one waited for
+__device__ __forceinline__ int clamp_stages(int n) { return n < 0 ? 0 : (n > 2 ? 2 : n); }
+
 // s_waitcnt vmcnt(n * PER) for a runtime n in [0, 3]
 template <int PER>
 __device__ __forceinline__ void wait_stages(int n) {
@@ -345,9 +348,16 @@ __device__ __forceinline__ void mfma_frag(int i, const Frags<G>& F, f32x16 (&acc
 // before any wave reads it (each waits before the barrier), and every wave's reads of
 // stage kt are complete (lgkmcnt(0) before the barrier) before any wave refills its
 // buffer after the barrier.
+// FULL steps read the next stage and refill; otherwise `more` and `refill` say which
+// happens and n_after is the number of stages in flight after the next one. The refill
+// loads stage `rstage` of loader `rl` (the next tile's loader near the end of a tile).
+// (A class template: hipcc's host pass rejects later calls of this step as a function
+// template once it has been instantiated from two callers.)
 template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL>
-__device__ __forceinline__ void pipe_step(int kt, int nk_total, char* const (&ring)[G::STAGES],
-                                          const StageLoader<G, SWIGLU, SPLIT>& ld,
+struct PipeStep {
+static __device__ __forceinline__ void run(int n_after, bool more_, bool refill_,
+                                          const StageLoader<G, SWIGLU, SPLIT>& rl, int rstage,
+                                          char* const (&ring)[G::STAGES],
                                           const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
                                           f32x16 (&acc)[G::NBW][G::MB], const Frags<G>& Fc,
                                           Frags<G>& Fn) {
@@ -360,11 +370,11 @@ __device__ __forceinline__ void pipe_step(int kt, int nk_total, char* const (&ri
   __builtin_amdgcn_sched_barrier(0);
   // own loads of stage kt + 1 (kt + 1 .. kt + S - 1 may be in flight)
   if constexpr (FULL) wait_vmcnt<(S - 2) * G::LPS>();
-  else wait_stages<G::LPS>(max(0, min(S - 2, nk_total - 2 - kt)));
+  else wait_stages<G::LPS>(n_after);
   wait_lgkmcnt0();
   sync_point();
-  const bool more = FULL || kt + 1 < nk_total;
-  const bool refill = FULL || kt + S < nk_total;
+  const bool more = FULL || more_;
+  const bool refill = FULL || refill_;
   const char* src = ring[(J + 1) % S];
   char* const dst = ring[J];
 #pragma unroll
@@ -375,62 +385,11 @@ __device__ __forceinline__ void pipe_step(int kt, int nk_total, char* const (&ri
 #pragma unroll
       for (int r = 0; r < RPG; ++r) read_frag<G>(g * RPG + r, src, a_frag, b_frag, Fn);
     }
-    if (refill) ld.issue_one(g, kt + S, dst);
+    if (refill) rl.issue_one(g, rstage, dst);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-
-// The K loop of one tile for one wave per SIMD (pipe_step).
-template <class G, bool SWIGLU, bool SPLIT>
-__device__ __forceinline__ void pipe_loop(int nk_total, char* const (&ring)[G::STAGES],
-                                          const StageLoader<G, SWIGLU, SPLIT>& ld,
-                                          const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
-                                          f32x16 (&acc)[G::NBW][G::MB]) {
-  constexpr int S = G::STAGES;
-  int kt = 0;
-  static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
-  Frags<G> F0, F1;
-#define MOE_PSTEP(J, FULL, KT)                                                            \
-  pipe_step<G, SWIGLU, SPLIT, (J) % S, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc, \
-                                             (J) % 2 ? F1 : F0, (J) % 2 ? F0 : F1)
-  // Prologue: the whole ring in flight, then stage 0's fragments. The main loop (every
-  // step refills) sits in the same branch as an unconditional prologue, so that the
-  // compiler sees the same loads in flight on every path into it.
-  if (nk_total >= 2 * S) {
-#pragma unroll
-    for (int i = 0; i < S; ++i) ld.issue(i, ring[i]);
-    wait_vmcnt<(S - 1) * G::LPS>();
-    sync_point();
-#pragma unroll
-    for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
-      read_frag<G>(r, ring[0], a_frag, b_frag, F0);
-    for (; kt + 2 * S - 1 < nk_total; kt += S) {
-      MOE_PSTEP(0, true, kt);
-      MOE_PSTEP(1, true, kt + 1);
-      MOE_PSTEP(2, true, kt + 2);
-      MOE_PSTEP(3, true, kt + 3);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (i < nk_total) ld.issue(i, ring[i]);
-    wait_stages<G::LPS>(min(S - 1, nk_total - 1));
-    sync_point();
-#pragma unroll
-    for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
-      read_frag<G>(r, ring[0], a_frag, b_frag, F0);
-  }
-  // at most 2 * S - 1 stages remain
-  if (kt < nk_total) { MOE_PSTEP(0, false, kt); }
-  if (kt + 1 < nk_total) { MOE_PSTEP(1, false, kt + 1); }
-  if (kt + 2 < nk_total) { MOE_PSTEP(2, false, kt + 2); }
-  if (kt + 3 < nk_total) { MOE_PSTEP(3, false, kt + 3); }
-  if (kt + 4 < nk_total) { MOE_PSTEP(4, false, kt + 4); }
-  if (kt + 5 < nk_total) { MOE_PSTEP(5, false, kt + 5); }
-  if (kt + 6 < nk_total) { MOE_PSTEP(6, false, kt + 6); }
-#undef MOE_PSTEP
-  wait_vmcnt<0>();
-}
+};
 
 // The K loop of one tile. ROLE 0: every wave runs ring_step; ROLE 1 / 2: the first /
 // second wave of a SIMD in the ping-pong schedule (compiled separately, so that each
@@ -490,6 +449,250 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
   if constexpr (ROLE == 1) sync_point();  // the first waves' extra barrier
 }
 
+// Kernel arguments shared by the tile helpers.
+struct GemmArgs {
+  const bf16* A;         // rows (x_perm or h), [R, K]
+  const bf16* A2;        // second row set of the split down projection (h_lo)
+  const bf16* B0;        // W_gate or W_down, [E, K, N]
+  const bf16* B1;        // W_up (SwiGLU)
+  const int32_t* offsets;
+  int E, K, N;
+  void* out;             // h (bf16) or o (fp32)
+  void* out2;            // h_lo (bf16, split)
+};
+
+// One output tile: expert e, rows [row0, row0 + rows), output columns from n0.
+struct TileCoord {
+  int e, row0, rows, n0;
+};
+
+// Tile i of XCD xcd's share. Experts are processed one after another by all XCDs
+// together: XCD x takes the x-th eighth of each expert's tiles listed N-tile-major, i.e.
+// mostly its own slice of the expert's weight columns, for all of the expert's rows.
+template <int BM>
+__device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, int NT,
+                                                 int bn_out, int xcd) {
+  int e = 0, acc_i = 0, p = 0, mte = 1;
+  for (;; ++e) {
+    mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+    const long long pe = (long long)mte * NT;
+    const int plo = (int)((pe * xcd) >> 3), phi = (int)((pe * (xcd + 1)) >> 3);
+    if (i < acc_i + (phi - plo)) {
+      p = plo + (i - acc_i);
+      break;
+    }
+    acc_i += phi - plo;
+  }
+  const int nt = p / mte, mtl = p - nt * mte;
+  TileCoord t;
+  t.e = e;
+  t.row0 = offsets[e] + mtl * BM;
+  t.rows = min(BM, offsets[e + 1] - t.row0);
+  t.n0 = nt * bn_out;
+  return t;
+}
+
+// Lane id rebuilt by mbcnt inside volatile asm: per-tile copies of per-lane constants are
+// recomputed from it (a few VALU ops per tile) instead of being kept live through the K
+// loop, where registers are short, and reloaded from spills.
+__device__ __forceinline__ int fresh_lane() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  return ln;
+}
+
+// Per-lane fragment offsets inside a stage (bytes) for substep 0. Substep s reads A
+// chunk 2s + lane / 32 (swizzled), i.e. offset a_frag ^ 32 s (the chunk bits lie below
+// the row bits), and B rows 16 s further down, i.e. offset b_frag + 16 s B_ROW.
+template <class G, bool SWIGLU, int BNL>
+__device__ __forceinline__ void frag_offsets(int ln, int wm, int wn, int (&a_frag)[G::MB],
+                                             int (&b_frag)[G::NBW]) {
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int m = wm * G::WM + mb * 32 + (ln & 31);
+    a_frag[mb] = m * (G::BK * 2) + ((ln >> 5) ^ a_swz<G::A_CPR>(m)) * 16;
+  }
+  const int g = ln >> 4, i = ln & 15, c = i & 3, r = i >> 2;
+#pragma unroll
+  for (int nb = 0; nb < G::NBW; ++nb) {
+    int nbase;
+    if constexpr (SWIGLU) {
+      constexpr int H = G::NBW / 2;
+      nbase = nb < H ? wn * (G::WNL / 2) + nb * 32 : BNL / 2 + wn * (G::WNL / 2) + (nb - H) * 32;
+    } else {
+      nbase = wn * G::WNL + nb * 32;
+    }
+    const int n = nbase + (g & 1) * 16 + 4 * c;
+    const int k = (g >> 1) * 8 + r;
+    const int phys = (n >> 3) ^ (b_swz(k) % G::B_SLOTS);  // the same for k + 4 and k + 16 s
+    b_frag[nb] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
+  }
+}
+
+// Direct-load sources of tile t for this lane (element offsets, without the K step).
+template <class G, bool SWIGLU, bool SPLIT, int BNL>
+__device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmArgs& a,
+                                                                    const TileCoord& t, int ln,
+                                                                    int wave, int nk) {
+  StageLoader<G, SWIGLU, SPLIT> ld;
+  ld.Ab = a.A + (size_t)t.row0 * a.K;
+  ld.Ab2 = (SPLIT && !SWIGLU) ? a.A2 + (size_t)t.row0 * a.K : ld.Ab;
+  ld.nk = nk;
+  ld.N = a.N;
+  ld.wave = wave;
+  const bf16* W0 = a.B0 + (size_t)t.e * a.K * a.N;
+  const bf16* W1 = SWIGLU ? a.B1 + (size_t)t.e * a.K * a.N : W0;
+#pragma unroll
+  for (int j = 0; j < G::A_PW; ++j) {
+    const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
+    const int c = (ln % G::A_CPR) ^ a_swz<G::A_CPR>(row);
+    ld.a_src[j] = min(row, t.rows - 1) * a.K + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < G::B_PW; ++j) {
+    const int row = (wave * G::B_PW + j) * G::B_RPI + ln / G::B_SLOTS;
+    const int nl = ((ln % G::B_SLOTS) ^ (b_swz(row) % G::B_SLOTS)) * 8;
+    if constexpr (SWIGLU) {
+      const bool up = nl >= BNL / 2;
+      ld.b_base[j] = up ? W1 : W0;
+      ld.b_src[j] = row * a.N + t.n0 + (up ? nl - BNL / 2 : nl);
+    } else {
+      ld.b_base[j] = W0;
+      ld.b_src[j] = row * a.N + t.n0 + nl;
+    }
+  }
+  return ld;
+}
+
+template <class G>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[G::NBW][G::MB]) {
+#pragma unroll
+  for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+}
+
+// Epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
+// ncol = 8q + 4 * (lane / 32) inside 32-column block nb. SwiGLU: h = silu(gate) * up in
+// bf16 (and the bf16 residual of h when split); down projection: o in fp32.
+template <class G, bool SWIGLU, bool SPLIT>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t, int ln, int wm,
+                                           int wn, const f32x16 (&acc)[G::NBW][G::MB]) {
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int m = wm * G::WM + mb * 32 + (ln & 31);
+    if (m >= t.rows) continue;
+    const size_t rowoff = (size_t)(t.row0 + m) * a.N + t.n0;
+    if constexpr (SWIGLU) {
+      constexpr int H = G::NBW / 2;
+#pragma unroll
+      for (int nb = 0; nb < H; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (ln >> 5);
+          bf16x4 hv, lv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float hf = silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
+            hv[i] = (bf16)hf;
+            if constexpr (SPLIT) lv[i] = (bf16)(hf - (float)hv[i]);
+          }
+          *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.out) + rowoff + ncol) =
+              __builtin_bit_cast(u32x2, hv);
+          if constexpr (SPLIT)
+            *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.out2) + rowoff + ncol) =
+                __builtin_bit_cast(u32x2, lv);
+          // one group of 4 outputs at a time: keeps the accumulator copies out of
+          // AGPRs from piling up in VGPRs
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (ln >> 5);
+          const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
+                           acc[nb][mb][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + rowoff + ncol) = v;
+        }
+    }
+  }
+}
+
+// This workgroup's tiles first, first + nslot, ... < my_total as one stream of K stages
+// through the ring (PipeStep): the last S steps of a tile refill the ring with the next
+// tile's first S stages, so those loads are in flight while this tile's epilogue runs
+// and the next tile only waits for its stage 0 to be read. Needs nk_total % S == 0, so
+// that stage s of every tile sits in ring buffer s % S. (The next tile's fragments are
+// read after the epilogue: holding them through it would leave too few registers.)
+template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL>
+__device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my_total, int nslot,
+                                            int NT, int xcd, int wave, int wm, int wn,
+                                            int nk, int nk_total, char* const (&ring)[G::STAGES]) {
+  constexpr int S = G::STAGES;
+  static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
+  int ln = fresh_lane();
+  int a_frag[G::MB], b_frag[G::NBW];
+  frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
+  TileCoord t = locate_tile<BM>(first, a.offsets, NT, G::BN_OUT, xcd);
+  StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk);
+#define MOE_SSTEP(J, RL, RSTAGE)                                                             \
+  PipeStep<G, SWIGLU, SPLIT, J, true>::run(0, true, true, RL, RSTAGE, ring, a_frag, b_frag, acc, \
+                                       (J) % 2 ? F1 : F0, (J) % 2 ? F0 : F1)
+  // prologue of the first tile: the whole ring in flight
+#pragma unroll
+  for (int i = 0; i < S; ++i) ld.issue(i, ring[i]);
+  for (int i = first;;) {
+    // accumulators and fragments are per tile (none is carried around this loop)
+    f32x16 acc[G::NBW][G::MB];
+    zero_acc<G>(acc);
+    Frags<G> F0, F1;
+    // stage 0's fragments (the ring holds stages 0 .. S-1 of this tile, stage 0 is the
+    // oldest load in flight; epilogue stores of the previous tile may be newer)
+    wait_vmcnt<(S - 1) * G::LPS>();
+    sync_point();
+#pragma unroll
+    for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
+      read_frag<G>(r, ring[0], a_frag, b_frag, F0);
+    int kt = 0;
+    for (; kt + 2 * S <= nk_total; kt += S) {  // refills from this tile
+      MOE_SSTEP(0, ld, kt + S);
+      MOE_SSTEP(1, ld, kt + S + 1);
+      MOE_SSTEP(2, ld, kt + S + 2);
+      MOE_SSTEP(3, ld, kt + S + 3);
+    }
+    // kt == nk_total - S: the last S steps refill the ring with the next tile's first S
+    // stages; after the last tile they load this tile's first stages again, unused but
+    // in bounds, so that every path into the loop above has the same loads in flight
+    // (the compiler then needs no extra wait there). The last step reads nothing.
+    const int inext = i + nslot;
+    const bool has_next = inext < my_total;
+    TileCoord tn = t;
+    StageLoader<G, SWIGLU, SPLIT> ldn = ld;
+    if (has_next) {
+      ln = fresh_lane();
+      tn = locate_tile<BM>(inext, a.offsets, NT, G::BN_OUT, xcd);
+      ldn = make_loader<G, SWIGLU, SPLIT, BNL>(a, tn, ln, wave, nk);
+    }
+    MOE_SSTEP(0, ldn, 0);
+    MOE_SSTEP(1, ldn, 1);
+    MOE_SSTEP(2, ldn, 2);
+    PipeStep<G, SWIGLU, SPLIT, 3, false>::run(S - 2, false, true, ldn, 3, ring, a_frag, b_frag,
+                                              acc, F1, F0);
+    ln = fresh_lane();
+    store_tile<G, SWIGLU, SPLIT>(a, t, ln, wm, wn, acc);
+    if (!has_next) break;
+    t = tn;
+    ld = ldn;
+    i = inext;
+  }
+#undef MOE_SSTEP
+  wait_vmcnt<0>();
+}
+
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ A2, const bf16* __restrict__ B0,
@@ -527,9 +730,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  // Experts are processed one after another by all XCDs together: XCD x takes the
-  // x-th eighth of each expert's tiles listed N-tile-major, i.e. mostly its own slice
-  // of the expert's weight columns, for all of the expert's rows.
+  // this XCD's number of tiles (the order is described at locate_tile)
   int my_total = 0;
   for (int e = 0; e < E; ++e) {
     const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
@@ -538,141 +739,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int nk = K / G::BK;
   const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
 
+  const GemmArgs args{A, A2, B0, B1, offsets, E, K, N, out, out2};
+  if constexpr (PIPE) {
+    if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
+      if (slot < my_total)
+        pipe_stream<G, SWIGLU, SPLIT, BM, BNL>(args, slot, my_total, nslot, NT, xcd, wave, wm, wn,
+                                               nk, nk_total, ring);
+      return;
+    }
+  }
   for (int i = slot; i < my_total; i += nslot) {
-    // Per-tile copies of per-lane constants, from the lane id that mbcnt rebuilds without
-    // any register: recomputing them (a few VALU ops per tile) is cheaper than keeping
-    // them live through the K loop, where registers are short, and reloading spills.
-    int ln;  // volatile: rebuilt in every tile, never hoisted out of the tile loop
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    // per-lane fragment offsets inside a stage (bytes) for substep 0. Substep s reads A
-    // chunk 2s + lane / 32 (swizzled), i.e. offset a_frag ^ 32 s (the chunk bits lie below
-    // the row bits), and B rows 16 s further down, i.e. offset b_frag + 16 s B_ROW.
-    int a_frag[G::MB];
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = wm * G::WM + mb * 32 + (ln & 31);
-      a_frag[mb] = m * (G::BK * 2) + ((ln >> 5) ^ a_swz<G::A_CPR>(m)) * 16;
-    }
-    int b_frag[G::NBW];
-    {
-      const int g = ln >> 4, i = ln & 15, c = i & 3, r = i >> 2;
-#pragma unroll
-      for (int nb = 0; nb < G::NBW; ++nb) {
-        int nbase;
-        if constexpr (SWIGLU) {
-          constexpr int H = G::NBW / 2;
-          nbase = nb < H ? wn * (G::WNL / 2) + nb * 32 : BNL / 2 + wn * (G::WNL / 2) + (nb - H) * 32;
-        } else {
-          nbase = wn * G::WNL + nb * 32;
-        }
-        const int n = nbase + (g & 1) * 16 + 4 * c;
-        const int k = (g >> 1) * 8 + r;
-        const int phys = (n >> 3) ^ (b_swz(k) % G::B_SLOTS);  // the same for k + 4 and k + 16 s
-        b_frag[nb] = G::A_BYTES + k * G::B_ROW + phys * 16 + ((n >> 2) & 1) * 8;
-      }
-    }
-
-    int e = 0, acc_i = 0, p = 0, mte = 1;
-    for (;; ++e) {
-      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      const long long pe = (long long)mte * NT;
-      const int plo = (int)((pe * xcd) >> 3), phi = (int)((pe * (xcd + 1)) >> 3);
-      if (i < acc_i + (phi - plo)) {
-        p = plo + (i - acc_i);
-        break;
-      }
-      acc_i += phi - plo;
-    }
-    const int nt = p / mte, mtl = p - nt * mte;
-    const int row0 = offsets[e] + mtl * BM;
-    const int rows = min(BM, offsets[e + 1] - row0);
-    const int n0 = nt * G::BN_OUT;
-
-    StageLoader<G, SWIGLU, SPLIT> ld;
-    ld.Ab = A + (size_t)row0 * K;
-    ld.Ab2 = (SPLIT && !SWIGLU) ? A2 + (size_t)row0 * K : ld.Ab;
-    ld.nk = nk;
-    ld.N = N;
-    ld.wave = wave;
-    const bf16* W0 = B0 + (size_t)e * K * N;
-    const bf16* W1 = SWIGLU ? B1 + (size_t)e * K * N : W0;
-    // per-lane DMA sources (element offsets, without the k step)
-#pragma unroll
-    for (int j = 0; j < G::A_PW; ++j) {
-      const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
-      const int c = (ln % G::A_CPR) ^ a_swz<G::A_CPR>(row);
-      ld.a_src[j] = min(row, rows - 1) * K + c * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < G::B_PW; ++j) {
-      const int row = (wave * G::B_PW + j) * G::B_RPI + ln / G::B_SLOTS;
-      const int nl = ((ln % G::B_SLOTS) ^ (b_swz(row) % G::B_SLOTS)) * 8;
-      if constexpr (SWIGLU) {
-        const bool up = nl >= BNL / 2;
-        ld.b_base[j] = up ? W1 : W0;
-        ld.b_src[j] = row * N + n0 + (up ? nl - BNL / 2 : nl);
-      } else {
-        ld.b_base[j] = W0;
-        ld.b_src[j] = row * N + n0 + nl;
-      }
-    }
-
+    const int ln = fresh_lane();
+    int a_frag[G::MB], b_frag[G::NBW];
+    frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
+    const TileCoord t = locate_tile<BM>(i, offsets, NT, G::BN_OUT, xcd);
+    const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk);
     f32x16 acc[G::NBW][G::MB];
-#pragma unroll
-    for (int nb = 0; nb < G::NBW; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
+    zero_acc<G>(acc);
 
-    if constexpr (PIPE) pipe_loop<G, SWIGLU, SPLIT>(nk_total, ring, ld, a_frag, b_frag, acc);
-    else if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
+    // (the pipelined layout falls back to the plain ring when its stream does not apply)
+    if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
     else if (second) k_loop<G, SWIGLU, SPLIT, 2>(nk_total, ring, ld, a_frag, b_frag, acc);
     else k_loop<G, SWIGLU, SPLIT, 1>(nk_total, ring, ld, a_frag, b_frag, acc);
 
-    // epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
-    // ncol = 8q + 4 * (lane / 32) inside 32-column block nb
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-      const int m = wm * G::WM + mb * 32 + (ln & 31);
-      if (m >= rows) continue;
-      const size_t rowoff = (size_t)(row0 + m) * N + n0;
-      if constexpr (SWIGLU) {
-        constexpr int H = G::NBW / 2;
-#pragma unroll
-        for (int nb = 0; nb < H; ++nb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (ln >> 5);
-            bf16x4 hv, lv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float hf = silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
-              hv[i] = (bf16)hf;
-              if constexpr (SPLIT) lv[i] = (bf16)(hf - (float)hv[i]);
-            }
-            *reinterpret_cast<u32x2*>(static_cast<bf16*>(out) + rowoff + ncol) =
-                __builtin_bit_cast(u32x2, hv);
-            if constexpr (SPLIT)
-              *reinterpret_cast<u32x2*>(static_cast<bf16*>(out2) + rowoff + ncol) =
-                  __builtin_bit_cast(u32x2, lv);
-            // one group of 4 outputs at a time: keeps the accumulator copies out of
-            // AGPRs from piling up in VGPRs
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < G::NBW; ++nb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (ln >> 5);
-            const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
-                             acc[nb][mb][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out) + rowoff + ncol) = v;
-          }
-      }
-    }
-    if constexpr (!PP && !PIPE) {
+    store_tile<G, SWIGLU, SPLIT>(args, t, ln, wm, wn, acc);
+    if constexpr (!PP) {
       // stores retired and every wave past its last stage read before the next
       // tile's loads refill the ring
       wait_vmcnt<0>();
