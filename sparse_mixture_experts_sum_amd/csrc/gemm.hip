@@ -6,20 +6,27 @@
 // rows form one dense GEMM against that expert's weights.
 //
 // bf16 path (the hot path):
-//   * persistent workgroups (one per CU) walk the tile list; each XCD takes a
-//     contiguous share of the tiles, in an order that keeps 4 M-tiles x 8 N-tiles of
-//     the same weights and rows in flight together, so that XCD's L2 serves the
-//     re-reads;
-//   * 256 threads, 2x2 waves, v_mfma_f32_32x32x16_bf16 with the weight fragment as
-//     the first operand, so that each lane's 16 accumulators are 4 runs of 4
-//     consecutive output columns of one row (8- and 16-byte stores);
-//   * K steps of 64, double-buffered LDS; the next step's global loads are in flight
-//     while the current step's MFMAs run;
-//   * weights are stored [K, N] (the x @ W layout of the pages), N contiguous; each
-//     thread loads an 8x8 block (8 rows of 16 bytes) and transposes it in registers
-//     so that LDS holds K-contiguous rows, which the MFMA operand needs;
+//   * persistent workgroups (one per CU); all XCDs walk the experts in the same order,
+//     XCD x taking the x-th eighth of each expert's tiles listed N-tile-major, so that
+//     an XCD's CUs share weight columns in its L2 and the XCDs share the expert's rows
+//     in the memory-side cache (locate_tile);
+//   * v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand, so that
+//     each lane's 16 accumulators are 4 runs of 4 consecutive output columns of one row
+//     (8- and 16-byte stores);
+//   * K stages of 32 through a ring of 4 LDS buffers filled by direct global->LDS loads
+//     (no registers in between); weights stay [K, N] as the pages store them and the B
+//     fragments come out of LDS with ds_read_b64_tr_b16 (transposing reads), the A
+//     fragments with 16-byte reads; both layouts are swizzled so that the fragment reads
+//     are free of bank conflicts;
+//   * 256 x 256 tiles: four waves (one per SIMD), each a 128 x 128 block with its 256
+//     accumulators in AGPRs, software-pipelined (PipeStep): the MFMAs of one stage run
+//     while the fragments of the next are read and the ring is refilled, one barrier
+//     per stage, and the stages stream across tiles (pipe_stream). Alternatives kept
+//     behind kWaves256 = 8: two waves per SIMD in a ping-pong schedule (pp_step).
+//     Smaller tiles (256 x 128, 256 x 64) use the plain ring (ring_step);
 //   * gate and up tiles share the A tile; the SwiGLU epilogue silu(g) * u runs in
-//     registers and writes h in bf16. The down projection writes o in fp32.
+//     registers and writes h in bf16 (plus its bf16 residual when asked). The down
+//     projection writes o in fp32.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 outputs per thread).
 #include "common.h"
