@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
                                                            int E, int k, int32_t* blk_counts,
                                                            float* blk_psum) {
   __shared__ int cnt[64];
+  __shared__ float red[256];
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * kRouterTokens;
   const int ntok = min(kRouterTokens, T - t0);
@@ -109,11 +110,15 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
     const int e = idx[(size_t)t0 * k + q];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
-  if (tid < E) {
-    float s = 0.f;
-    for (int q = 0; q < ntok; ++q) s += probs[(size_t)(t0 + q) * E + tid];
-    blk_psum[(size_t)blockIdx.x * E + tid] = s;
+  // the router's block sums, in the router's order (block_expert_sums)
+  const int tok = tid >> 2, part = tid & 3;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = part + 4 * i;
+    v[i] = (tok < ntok && e < E) ? probs[(size_t)(t0 + tok) * E + e] : 0.f;
   }
+  block_expert_sums<16>(v, (E + 3) / 4, E, red, blk_psum + (size_t)blockIdx.x * E);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
 }

@@ -65,3 +65,26 @@ __device__ inline int block_exclusive_scan(int v, int* sh, int* total) {
   __syncthreads();  // sh may be reused by the caller right after
   return base + incl - v;
 }
+
+// Per-expert sums over the 64 tokens of a router block (kRouterTokens), in one fixed
+// order shared by the router and the standalone statistics kernel, so that both give
+// bitwise the same partials. 256 threads; thread tid holds v[i] for token tid / 4 of the
+// block and expert (tid % 4) + 4 i, i < nper (zero for tokens past T). Order: an xor
+// butterfly over the 16 tokens of each wave (the same tree in every lane), then the four
+// wave sums in wave order. red: 4 x 64 floats of LDS. out[e] for e < E (E <= 64).
+template <int NMAX>
+__device__ __forceinline__ void block_expert_sums(float (&v)[NMAX], int nper, int E, float* red,
+                                                  float* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, part = tid & 3;
+#pragma unroll
+  for (int i = 0; i < NMAX; ++i) {
+    if (i < nper) {
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) v[i] += __shfl_xor(v[i], off);
+      if ((lane >> 2) == 0 && part + 4 * i < E) red[wave * 64 + part + 4 * i] = v[i];
+    }
+  }
+  __syncthreads();
+  if (tid < E) out[tid] = ((red[tid] + red[64 + tid]) + red[128 + tid]) + red[192 + tid];
+}
+

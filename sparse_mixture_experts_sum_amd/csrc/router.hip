@@ -46,18 +46,89 @@ struct RouterMma<float> {
 
 constexpr int kRT = kRouterTokens;  // tokens per workgroup (4 waves x 16)
 
+// Workgroup barrier after this wave's LDS accesses have completed; unlike __syncthreads
+// it does not wait for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+constexpr int kRouterWgBytes = 131072;  // LDS for the transposed W_g slice
+constexpr int kRouterPF = 4;            // iterations of x loads in flight per wave
+
+// x chunks of iteration `it` of a stage: lane group g takes chunks 4u + g, u = 0..3 (the
+// k ranges of the four 32-deep MFMA steps). Loads stay in bounds (clamped to the last
+// chunk of the stage) and are always issued, so that the compiler sees the same number
+// of loads in flight on every path; chunks past the stage's end read as zero, and so
+// does everything of an iteration past the last (the loop then runs whole groups of PF
+// iterations with no branch).
+template <int VEC, typename TI>
+__device__ __forceinline__ void router_load_x(const TI* xs, int it, int kn, int g,
+                                              u32x4 (&av)[4]) {
+  constexpr int ITK = 16 * VEC;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kx = it * ITK + (4 * u + g) * VEC;
+    const u32x4 v = ld16(xs + min(kx, kn - VEC));
+    av[u] = kx < kn ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Stage W_g[kc : kc + kn, 0 : E) transposed into LDS (row n = expert, LDW elements per
+// row). bf16 with E a multiple of 8: each thread reads 8 k-rows x 8 experts (8 x 16
+// bytes), transposes the block in registers (v_perm_b32 picks the low or high halves of
+// two dwords) and writes 8 rows of 16 bytes; otherwise element by element.
+template <typename TI>
+__device__ __forceinline__ void stage_wg_transposed(const TI* __restrict__ src, int kn, int E,
+                                                    int LDW, TI* Wl, int tid) {
+  if constexpr (sizeof(TI) == 2) {
+    if (E % 8 == 0 && kn % 8 == 0) {
+      const int eb8 = E / 8, nblk = (kn / 8) * eb8;
+      for (int bi = tid; bi < nblk; bi += 256) {
+        const int k0 = (bi / eb8) * 8, e0 = (bi % eb8) * 8;
+        u32x4 c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = ld16(src + (size_t)(k0 + i) * E + e0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = __builtin_amdgcn_perm(c[2 * j + 1][e >> 1], c[2 * j][e >> 1], sel);
+          st16(Wl + (size_t)(e0 + e) * LDW + k0, o);
+        }
+      }
+      return;
+    }
+  }
+  constexpr int VEC = 16 / (int)sizeof(TI);
+  const int nchunk = kn * E / VEC;
+  for (int c = tid; c < nchunk; c += 256) {
+    u32x4 v = ld16(src + (size_t)c * VEC);
+    const TI* ve = reinterpret_cast<const TI*>(&v);
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      const int flat = c * VEC + q;
+      const int kk = flat / E, n = flat - kk * E;
+      Wl[n * LDW + kk] = ve[q];
+    }
+  }
+}
+
 template <typename TI, int EP>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   using M = RouterMma<TI>;
   constexpr int VEC = M::VEC;
-  constexpr int ITK = 16 * VEC;                          // k per iteration (4 groups x 4 chunks)
-  constexpr int KC = 32768 / (EP * (int)sizeof(TI));     // k per LDS stage of W_g
-  constexpr int LDW = KC + 16 / (int)sizeof(TI);         // padded row (16 bytes)
+  constexpr int ITK = 16 * VEC;                                  // k per iteration
+  constexpr int KC = kRouterWgBytes / (EP * (int)sizeof(TI));    // k per LDS stage of W_g
+  constexpr int LDW = KC + 16 / (int)sizeof(TI);                 // padded row (16 bytes)
   constexpr int LSP = EP + 1;
+  constexpr int PF = kRouterPF;
   static_assert(KC % ITK == 0, "stage must hold whole iterations");
 
   __shared__ __attribute__((aligned(16))) TI Wl[EP * LDW];
   __shared__ float Ls[kRT * LSP];
+  __shared__ float red[256];
+  __shared__ float bias_s[64];
   __shared__ int sel[kRT * 8];
   __shared__ int running[64];
 
@@ -72,54 +143,54 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   f32x4 acc[EP / 16];
 #pragma unroll
   for (int nb = 0; nb < EP / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the bias is loaded now and stored to LDS after the logits pass, so that its load
+  // latency hides behind that pass
+  const float bias_r = (a.bias && tid < E) ? a.bias[tid] : 0.f;
 
+  // W_g is staged transposed in LDS (one slice of up to KC rows of k at a time; at most
+  // a few slices: d / KC); x is streamed from HBM into registers, PF iterations ahead.
+  // Nothing is zeroed: B fragments of padding experts (>= E) read expert E-1's row (their
+  // logits are never used), and reads past the slice's last k are clamped into it (the
+  // matching x chunks are zero).
   for (int kc = 0; kc < d; kc += KC) {
     const int kn = min(KC, d - kc);
-    __syncthreads();
-    // zero the stage (rows >= E and columns >= kn stay zero)
-    for (int i = tid; i < EP * LDW * (int)sizeof(TI) / 16; i += 256)
-      st16(reinterpret_cast<char*>(Wl) + 16 * i, u32x4{0u, 0u, 0u, 0u});
-    __syncthreads();
-    // W_g[kc : kc+kn, :] is contiguous: read it in 16-byte chunks, scatter transposed
-    const TI* src = Wg + (size_t)kc * E;
-    const int nchunk = kn * E / VEC;
-    for (int c = tid; c < nchunk; c += 256) {
-      u32x4 v = ld16(src + (size_t)c * VEC);
-      const TI* ve = reinterpret_cast<const TI*>(&v);
+    // the first x loads of the slice go out before W_g is staged, so that the two
+    // latencies overlap (the barriers below wait for LDS work only, not for loads)
+    const TI* xs = xrow + kc;
+    const int nit = (kn + ITK - 1) / ITK;
+    u32x4 av[PF][4];
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) {
-        const int flat = c * VEC + q;
-        const int kk = flat / E, n = flat - kk * E;
-        Wl[n * LDW + kk] = ve[q];
-      }
-    }
-    __syncthreads();
-    for (int kk = 0; kk < kn; kk += ITK) {
-      u32x4 av[4];
+    for (int p = 0; p < PF - 1; ++p) router_load_x<VEC>(xs, p, kn, g, av[p]);
+    lds_barrier();  // the previous slice's fragment reads are done
+    stage_wg_transposed<TI>(Wg + (size_t)kc * E, kn, E, LDW, Wl, tid);
+    lds_barrier();  // the slice is in LDS
+    for (int it0 = 0; it0 < nit; it0 += PF) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kx = kk + (4 * u + g) * VEC;
-        av[u] = kx < kn ? ld16(xrow + kc + kx) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < PF; ++j) {
+        const int it = it0 + j;
+        router_load_x<VEC>(xs, it + PF - 1, kn, g, av[(j + PF - 1) % PF]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kx = kk + (4 * u + g) * VEC;
+        for (int u = 0; u < 4; ++u) {
+          const int kx = it * ITK + (4 * u + g) * VEC;
 #pragma unroll
-        for (int nb = 0; nb < EP / 16; ++nb) {
-          u32x4 bv = ld16(&Wl[(nb * 16 + (lane & 15)) * LDW + kx]);
-          M::step(acc[nb], av[u], bv);
+          for (int nb = 0; nb < EP / 16; ++nb) {
+            const u32x4 bv = ld16(&Wl[min(nb * 16 + (lane & 15), E - 1) * LDW + min(kx, kn - VEC)]);
+            M::step(acc[nb], av[j][u], bv);
+          }
         }
       }
     }
   }
 
+  if (tid < 64) bias_s[tid] = bias_r;
+  __syncthreads();
   // acc[nb][r] = logit of token (wave*16 + 4g + r), expert (nb*16 + lane%16)
   if (ec) {
 #pragma unroll
     for (int nb = 0; nb < EP / 16; ++nb) {
       const int e = nb * 16 + (lane & 15);
       if (e >= E) continue;
-      const float bz = a.bias ? a.bias[e] : 0.f;
+      const float bz = bias_s[e];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + wave * 16 + 4 * g + r;
@@ -149,7 +220,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     const int e = part + 4 * i;
     lv[i] = -FLT_MAX;
     if (e < E) {
-      lv[i] = Ls[tok * LSP + e] + (a.bias ? a.bias[e] : 0.f);
+      lv[i] = Ls[tok * LSP + e] + bias_s[e];
       lmax = fmaxf(lmax, lv[i]);
     }
   }
@@ -205,25 +276,21 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     if (part == 0)
       for (int j = 0; j < k; ++j) sel[tok * k + j] = sele[j];
   }
-  // probabilities: to HBM (optional) and into the tile for the block sums
+  // probabilities: to HBM (optional) and into the block's per-expert sums
+  float pv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = part + 4 * i;
+    pv[i] = 0.f;
     if (e < E) {
       const float pe = ex[i] / lsum;
       if (valid && a.probs) a.probs[(size_t)t * E + e] = pe;
-      Ls[tok * LSP + e] = valid ? pe : 0.f;
+      pv[i] = valid ? pe : 0.f;
     }
   }
-  __syncthreads();
+  block_expert_sums<PER>(pv, PER, E, red, a.blk_psum + (size_t)blockIdx.x * E);
 
   const int nvalid = min(kRT, T - t0);
-  // per-block probability sums, fixed token order
-  if (tid < E) {
-    float s = 0.f;
-    for (int q = 0; q < kRT; ++q) s += Ls[q * LSP + tid];
-    a.blk_psum[(size_t)blockIdx.x * E + tid] = s;
-  }
   // slot ranks within the block: wave 0 walks the slots in flattened order, 64 at a time
   if (wave == 0) {
     const int nent = nvalid * k;
