@@ -123,3 +123,48 @@ def forward_ec(x, Wg, b, Wgate, Wup, Wdown, cf):
             for c in range(len(out)):
                 ys[t][c] += col[t] * out[c]
     return {"y": ys, "idx": idx, "w": score}
+
+
+def forward_tc_capacity(x, Wg, b, Wgate, Wup, Wdown, k, cf, renormalize=True):
+    """Capacity-limited token choice by literal loops (P5
+    ``expert_capacity_routing``): a running count per expert, tokens in order,
+    an assignment kept while its expert's count is below int((T / E) * cf * k).
+    Returns dict(y, idx, w, kept, load)."""
+    T, E = len(x), len(Wg[0])
+    cap = int((T / E) * cf * k)
+    load = [0] * E
+    ys, idxs, ws, kepts = [], [], [], []
+    for t in range(T):
+        s = _vecmat(x[t], Wg)
+        if b is not None:
+            s = [s[e] + float(b[e]) for e in range(E)]
+        p = _softmax(s)
+        chosen = _best_subset(p, k)
+        chosen.sort(key=lambda e: (-p[e], e))
+        keep = []
+        for e in chosen:
+            if load[e] < cap:
+                load[e] += 1
+                keep.append(True)
+            else:
+                keep.append(False)
+        wsel = [p[e] if kp else 0.0 for e, kp in zip(chosen, keep)]
+        if renormalize:
+            tot = 0.0
+            for v in wsel:
+                tot += v
+            if tot > 0.0:
+                wsel = [v / tot for v in wsel]
+        y = [0.0] * len(Wdown[0][0])
+        for j, e in enumerate(chosen):
+            if not keep[j]:
+                continue
+            out = expert(x[t], Wgate[e], Wup[e], Wdown[e])
+            for c in range(len(y)):
+                y[c] += wsel[j] * out[c]
+        ys.append(y)
+        idxs.append(chosen)
+        ws.append(wsel)
+        kepts.append(keep)
+    return {"y": ys, "idx": idxs, "w": ws, "kept": kepts, "load": load}
+

@@ -21,7 +21,8 @@ Pages cited (by title):
      ``TopKGating``, ``ExpertChoiceGating``, ``compute_load_balancing_loss``,
      ``MoELayerWithAuxLoss``)
   P5 "机器学习基础系列——混合专家模型" (``GatingNetwork`` with bias,
-     ``MixtureOfExperts`` dense mixture, ``SparseMoE``)
+     ``MixtureOfExperts`` dense mixture, ``SparseMoE``,
+     ``expert_capacity_routing``)
 
 Readings where the pages leave a step open or disagree:
   * renormalisation: P1/P3 code renormalise the selected weights, P2's
@@ -35,6 +36,13 @@ Readings where the pages leave a step open or disagree:
   * expert choice: softmax over tokens of each expert's logit column, top-C
     tokens per expert with C = floor(T*cf/E), outputs combined with the
     selected scores and no renormalisation; a token no expert picks gets 0.
+  * token choice with an expert capacity (P5 ``expert_capacity_routing``):
+    capacity = int((T / E) * cf * k); assignments are taken token by token and
+    kept while the expert is below capacity. The page walks a token's slots
+    from its smallest selected gate up; a token's slots go to distinct
+    experts, so that order decides nothing. Kept gates are renormalised over
+    the token's kept slots (zeros stay zeros); with renormalize=False (not on
+    the page, which always renormalises) the kept slots keep the raw gates.
 """
 from __future__ import annotations
 
@@ -241,6 +249,54 @@ def forward_ec(x, Wg, b, Wgate, Wup, Wdown, cf):
     idx, score, S, s = route_ec(x, Wg, b, cf)
     y = mix_ec(x, idx, score, Wgate, Wup, Wdown)
     return {"y": y, "idx": idx, "w": score, "probs": S, "logits": s}
+
+
+# --------------------------------------------------------------------------
+# Token choice with an expert capacity
+# --------------------------------------------------------------------------
+
+def tc_capacity(T, E, k, cf):
+    """capacity = int((T / E) * cf * k) (P5 ``expert_capacity_routing``), the
+    product taken in that order in float64 as on the page."""
+    return int((T / E) * cf * k)
+
+
+def route_tc_capacity(x, Wg, b, k, cf, renormalize=True):
+    """Token choice with an expert capacity (P5 ``expert_capacity_routing``).
+    Each token's top-k experts (as in ``route_tc``) are visited token by token;
+    an assignment is kept while its expert has taken fewer than `capacity`
+    assignments, and dropped otherwise. The kept gates, divided by their sum
+    over the token's kept slots (a sum of 0 is divided by 1), are the weights;
+    dropped slots weigh 0. Returns (idx [T,k], w [T,k], kept [T,k], probs,
+    logits, load [E]) with load the kept assignments per expert."""
+    s = router_logits(x, Wg, b)
+    p = softmax_rows(s)
+    idx = topk_experts(p, k)
+    T, E = p.shape
+    cap = tc_capacity(T, E, k, cf)
+    load = np.zeros(E, dtype=np.int64)
+    kept = np.zeros(idx.shape, dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if load[e] < cap:
+                kept[t, j] = True
+                load[e] += 1
+    g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)
+    if renormalize:
+        rows = g.sum(axis=1, keepdims=True)
+        rows[rows == 0] = 1.0
+        g = g / rows
+    return idx, g, kept, p, s, load
+
+
+def forward_tc_capacity(x, Wg, b, Wgate, Wup, Wdown, k, cf, renormalize=True):
+    """Capacity-limited token-choice layer forward: y_t = sum over the token's
+    kept slots of w * E_e(x_t) (dropped slots weigh 0). Returns dict with y,
+    idx, w, kept, probs, logits, load."""
+    idx, w, kept, p, s, load = route_tc_capacity(x, Wg, b, k, cf, renormalize)
+    y = mix(x, idx, w, Wgate, Wup, Wdown)
+    return {"y": y, "idx": idx, "w": w, "kept": kept, "probs": p, "logits": s, "load": load}
 
 
 # --------------------------------------------------------------------------

@@ -364,4 +364,97 @@ def pin_margins(O):
     assert np.all(np.isinf(O.ec_margin(s, 3)))
 
 
+
+# ----------------------------------------------------------------------------
+# token choice with an expert capacity
+# ----------------------------------------------------------------------------
+
+def pin_capacity_golden(O):
+    """The capacity of the page's own call (tests/golden/page_values.json), and the
+    truncation of the product at a few exact points."""
+    with open(os.path.join(GOLDEN, "page_values.json")) as fh:
+        d = json.load(fh)["p5_capacity_of_page_call"]
+    assert O.tc_capacity(d["T"], d["E"], d["k"], d["capacity_factor"]) == d["value"]
+    for T, E, k, cf, C in [(64, 8, 1, 1.0, 8), (10, 4, 2, 1.0, 5), (7, 8, 1, 1.0, 0),
+                           (1000, 8, 2, 1.25, 312), (12, 8, 2, 1.0, 3)]:
+        assert O.tc_capacity(T, E, k, cf) == C, (T, E, k, cf)
+
+
+def pin_capacity_unlimited_is_plain_tc(O):
+    """A capacity of at least T*k drops nothing: routing equals plain token choice."""
+    c = _case(31, T=9, E=5, bias=True)
+    for renorm in (True, False):
+        idx, w, kept, p, s, load = O.route_tc_capacity(c["x"], c["Wg"], c["b"], 2, 1e6, renorm)
+        idx0, w0, p0, s0 = O.route_tc(c["x"], c["Wg"], c["b"], 2, renorm)
+        assert kept.all()
+        assert np.array_equal(idx, idx0)
+        assert np.allclose(w, w0, rtol=1e-15, atol=0)
+        assert load.tolist() == np.bincount(idx0.ravel(), minlength=5).tolist()
+
+
+def pin_capacity_brute(O):
+    """Output, weights, kept slots and loads equal the literal-loop brute force
+    (subset enumeration for top-k, a running count per expert) under tight
+    capacities, with and without renormalisation."""
+    for seed, cf, T, E, k in [(32, 0.5, 7, 4, 2), (33, 0.75, 8, 3, 2), (34, 0.4, 6, 4, 1),
+                              (35, 1.0, 8, 4, 3)]:
+        c = _case(seed, T=T, E=E, bias=True, wg_std=1.5)
+        for renorm in (True, False):
+            ref = B.forward_tc_capacity(_lists(c["x"]), _lists(c["Wg"]), _lists(c["b"]),
+                                        _lists(c["Wgate"]), _lists(c["Wup"]), _lists(c["Wdown"]),
+                                        k, cf, renorm)
+            got = O.forward_tc_capacity(c["x"], c["Wg"], c["b"], c["Wgate"], c["Wup"],
+                                        c["Wdown"], k, cf, renorm)
+            assert got["idx"].tolist() == ref["idx"]
+            assert got["kept"].tolist() == ref["kept"]
+            assert got["load"].tolist() == ref["load"]
+            assert np.allclose(got["w"], np.array(ref["w"]), rtol=1e-12, atol=1e-15)
+            assert np.allclose(got["y"], np.array(ref["y"]), rtol=1e-10, atol=1e-12)
+
+
+def pin_capacity_one_expert_closed_form(O):
+    """Every token routed to one expert with k = 1: the first C tokens keep weight 1
+    and that expert's output; the others get weight 0 and y = 0."""
+    T, E, cf = 10, 4, 1.2   # C = int(10 / 4 * 1.2 * 1) = 3
+    c = _case(36, T=T, E=E)
+    b = np.zeros(E)
+    b[2] = 60.0
+    got = O.forward_tc_capacity(c["x"], c["Wg"], b, c["Wgate"], c["Wup"], c["Wdown"], 1, cf)
+    assert got["idx"][:, 0].tolist() == [2] * T
+    assert got["kept"][:, 0].tolist() == [True] * 3 + [False] * (T - 3)
+    assert got["w"][:, 0].tolist() == [1.0] * 3 + [0.0] * (T - 3)
+    for t in range(T):
+        want = B.expert(_lists(c["x"][t]), _lists(c["Wgate"][2]), _lists(c["Wup"][2]),
+                        _lists(c["Wdown"][2])) if t < 3 else [0.0] * c["x"].shape[1]
+        assert np.allclose(got["y"][t], want, rtol=1e-10, atol=1e-12), t
+
+
+def pin_capacity_zero_drops_everything(O):
+    """Capacity 0 (int() of a product below 1): every slot dropped, all weights and
+    outputs exactly 0, no NaN from an empty renormalisation."""
+    c = _case(37, T=5, E=8)
+    got = O.forward_tc_capacity(c["x"], c["Wg"], None, c["Wgate"], c["Wup"], c["Wdown"], 1, 1.0)
+    assert not got["kept"].any()
+    assert np.all(got["w"] == 0.0) and np.all(got["y"] == 0.0)
+    assert got["load"].tolist() == [0] * 8
+
+
+def pin_capacity_keeps_earliest_tokens(O):
+    """Invariants: each expert keeps min(count, C) assignments, and they are its
+    earliest tokens; each token's kept weights sum to 1 (or it has none)."""
+    c = _case(38, T=40, d=6, E=5, bias=True, wg_std=1.0)
+    idx, w, kept, p, s, load = O.route_tc_capacity(c["x"], c["Wg"], c["b"], 2, 0.6)
+    C = O.tc_capacity(40, 5, 2, 0.6)
+    for e in range(5):
+        tt, jj = np.nonzero(idx == e)
+        order = np.argsort(tt, kind="stable")
+        flags = kept[tt[order], jj[order]]
+        n = min(len(tt), C)
+        assert flags.tolist() == [True] * n + [False] * (len(tt) - n), e
+        assert load[e] == n
+    sums = w.sum(axis=1)
+    assert np.allclose(sums[kept.any(axis=1)], 1.0, rtol=1e-14)
+    assert np.all(sums[~kept.any(axis=1)] == 0.0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

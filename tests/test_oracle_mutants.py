@@ -41,6 +41,13 @@ MUTANTS = {
     "ec_unsorted_tokens": ("chosen = np.sort(chosen)\n", "\n"),
     "ec_score_unweighted": ("y[tt] += _f64(score[e])[:, None] * out", "y[tt] += out"),
     "margin_off_by_one": ("return ps[:, k - 1] - ps[:, k]", "return ps[:, k] - ps[:, k + 1 if k + 1 < E else k]"),
+    "tc_capacity_keeps_one_more": ("if load[e] < cap:", "if load[e] <= cap:"),
+    "tc_capacity_no_zero_guard": ("rows[rows == 0] = 1.0", "rows = rows"),
+    "tc_capacity_dropped_keep_gate": ("g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)",
+                                      "g = np.take_along_axis(p, idx, axis=1)"),
+    "tc_capacity_truncates_factors": ("return int((T / E) * cf * k)", "return int(T / E) * int(cf * k)"),
+    "tc_capacity_renorm_over_all_slots": ("rows = g.sum(axis=1, keepdims=True)",
+                                          "rows = np.take_along_axis(p, idx, axis=1).sum(axis=1, keepdims=True)"),
 }
 
 
