@@ -16,7 +16,11 @@
  *     compute_load_balancing_loss);
  *   - expert-choice routing with capacity C = floor(T * cf / E): each expert takes the
  *     C tokens of largest softmax-over-tokens score (the Korean page's
- *     ExpertChoiceGating).
+ *     ExpertChoiceGating);
+ *   - token choice with an expert capacity C = int((T / E) * cf * k): top-k routing as
+ *     above, after which each expert keeps its first C assignments in token order and
+ *     drops the rest; a token that lost a slot has its kept weights divided by their
+ *     sum ("机器学习基础系列——混合专家模型", expert_capacity_routing).
  *
  * Conventions for every entry point:
  *   - All tensors are row-major and live in device memory (HBM) unless stated; the
@@ -64,7 +68,13 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-typedef enum moe_mode { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 } moe_mode;
+/* MOE_TOKEN_CHOICE_CAPACITY is token choice (every "token choice" rule below applies)
+ * with an expert capacity: see moe_capacity and moe_route. */
+typedef enum moe_mode {
+  MOE_TOKEN_CHOICE = 0,
+  MOE_EXPERT_CHOICE = 1,
+  MOE_TOKEN_CHOICE_CAPACITY = 2
+} moe_mode;
 
 /* Shape of one layer call. */
 typedef struct moe_shape {
@@ -78,15 +88,19 @@ typedef struct moe_shape {
   int32_t renormalize;   /* token choice: 1 = selected weights divided by their sum
                             (Mixture of Experts（MoE）の理論と実装, MoELayer.route);
                             0 = raw probabilities (the qiita router equations) */
-  float capacity_factor; /* expert choice: C = floor(T * capacity_factor / E) */
+  float capacity_factor; /* expert choice: C = floor(T * capacity_factor / E);
+                            token choice with capacity: C = int((T / E) * capacity_factor
+                            * k), > 0 and finite; ignored in plain token choice */
 } moe_shape;
 
 /* Human-readable name of a status code. Never NULL; the string is static. */
 const char* moe_status_string(int32_t status);
 
-/* Expert-choice capacity C = floor(T * cf / E) (the Korean page's ExpertChoiceGating,
- * expert_capacity). Host only. Returns MOE_ERR_BAD_SHAPE when mode is not expert
- * choice or C falls outside [1, T]. */
+/* Capacity C. Expert choice: floor(T * cf / E) (the Korean page's ExpertChoiceGating,
+ * expert_capacity); MOE_ERR_BAD_SHAPE unless 1 <= C <= T. Token choice with capacity:
+ * floor((T / E) * cf * k) evaluated in double in that order ("机器学习基础系列——混合专家
+ * 模型", expert_capacity_routing); C = 0 is valid and drops every assignment. Host
+ * only. Plain token choice returns MOE_ERR_BAD_SHAPE. */
 moe_status moe_capacity(const moe_shape* shape, int64_t* capacity);
 
 /* Bytes of device workspace moe_route / moe_forward / moe_aux_loss need for `shape`.
@@ -97,13 +111,15 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
  * tests and debugging. After a moe_forward call has completed on the stream the
  * buffer holds that call's values until the workspace is used again. Host only.
  *   MOE_WS_OFFSETS [E+1] int32   first row of each expert's group; [E] = R
- *   MOE_WS_POS     [T, k] int32  token choice: row of each (token, slot)
+ *   MOE_WS_POS     [T, k] int32  token choice: row of each (token, slot), -1 when the
+ *                                expert capacity dropped the slot
  *   MOE_WS_SRC     [R] int32     token of each row
  *   MOE_WS_XPERM   [R, d_model]  dtype, x rows in expert-contiguous order
  *   MOE_WS_H       [R, d_ff]     dtype, silu(x W_gate) * (x W_up) per row
  *   MOE_WS_O       [R, d_model]  fp32, expert output per row (before weighting)
- * R = T*k (token choice) or E*C (expert choice). MOE_WS_POS is MOE_ERR_UNSUPPORTED in
- * expert choice. */
+ * R = T*k (token choice) or E*C (expert choice). With an expert capacity only rows
+ * [0, offsets[E]) hold kept slots, offsets[E] = sum_e min(counts_e, C). MOE_WS_POS is
+ * MOE_ERR_UNSUPPORTED in expert choice. */
 enum {
   MOE_WS_OFFSETS = 0,
   MOE_WS_POS = 1,
@@ -128,6 +144,12 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
  * Optional outputs (NULL to skip):
  *   probs  [T, E] fp32    softmax probabilities (expert choice: over tokens, per column)
  *   counts [E] int32      assignments per expert (expert choice: C each)
+ * Token choice with capacity: idx and counts are those of plain token choice (counts
+ * before any drop); w holds the weights after the capacity: 0 for a dropped slot, and
+ * for a token that lost a slot its kept weights divided by their sum when renormalize
+ * = 1 (a token that lost every slot gets zeros), unchanged when renormalize = 0. An
+ * expert keeps the assignments of lowest token index; a token's slots go to distinct
+ * experts, so the order of slots within a token decides nothing.
  * idx and w are required. */
 moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
                      int32_t* idx, float* w, float* probs, int32_t* counts, void* ws,
@@ -142,7 +164,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
  *   y             [T, d_model] fp32   y_t = sum over the token's experts of
  *                 weight * E_e(x_t); in expert choice a token no expert takes gets 0
  * Optional outputs (NULL to skip): idx, w, probs, counts as in moe_route, and, token
- * choice only:
+ * choice only (with capacity: computed from the assignments before any drop):
  *   f     [E] fp32   counts / T (sums to k)
  *   p     [E] fp32   mean over tokens of probs
  *   loss  [1] fp32   E * sum_e (f_e / k) * p_e (1 under uniform routing)

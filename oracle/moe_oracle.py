@@ -261,6 +261,36 @@ def tc_capacity(T, E, k, cf):
     return int((T / E) * cf * k)
 
 
+def capacity_keep(idx, E, cap):
+    """Which assignments survive an expert capacity (P5 ``expert_capacity_routing``):
+    tokens are visited in order and each of a token's assignments is kept while its
+    expert has taken fewer than `cap`. Returns (kept [T,k] bool, load [E])."""
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    load = np.zeros(E, dtype=np.int64)
+    kept = np.zeros(idx.shape, dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if load[e] < cap:
+                kept[t, j] = True
+                load[e] += 1
+    return kept, load
+
+
+def capacity_weights(p, idx, kept, renormalize=True):
+    """Gate weights after the capacity: the kept slots' probabilities, divided by
+    their sum over the token's kept slots (a sum of 0 is divided by 1) when
+    renormalising; dropped slots weigh 0."""
+    idx = np.asarray(idx, dtype=np.int64)
+    g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)
+    if renormalize:
+        rows = g.sum(axis=1, keepdims=True)
+        rows[rows == 0] = 1.0
+        g = g / rows
+    return g
+
+
 def route_tc_capacity(x, Wg, b, k, cf, renormalize=True):
     """Token choice with an expert capacity (P5 ``expert_capacity_routing``).
     Each token's top-k experts (as in ``route_tc``) are visited token by token;
@@ -274,19 +304,8 @@ def route_tc_capacity(x, Wg, b, k, cf, renormalize=True):
     idx = topk_experts(p, k)
     T, E = p.shape
     cap = tc_capacity(T, E, k, cf)
-    load = np.zeros(E, dtype=np.int64)
-    kept = np.zeros(idx.shape, dtype=bool)
-    for t in range(T):
-        for j in range(k):
-            e = idx[t, j]
-            if load[e] < cap:
-                kept[t, j] = True
-                load[e] += 1
-    g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)
-    if renormalize:
-        rows = g.sum(axis=1, keepdims=True)
-        rows[rows == 0] = 1.0
-        g = g / rows
+    kept, load = capacity_keep(idx, E, cap)
+    g = capacity_weights(p, idx, kept, renormalize)
     return idx, g, kept, p, s, load
 
 

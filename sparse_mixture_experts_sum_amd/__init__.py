@@ -24,7 +24,9 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_hip.so")
 
 MOE_FP32, MOE_BF16 = 0, 1
-MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE, MOE_TOKEN_CHOICE_CAPACITY = 0, 1, 2
+# mode names: token choice, expert choice, token choice with an expert capacity
+MODES = {"tc": MOE_TOKEN_CHOICE, "ec": MOE_EXPERT_CHOICE, "tc_capacity": MOE_TOKEN_CHOICE_CAPACITY}
 NUM_STAGES = 8
 WS_OFFSETS, WS_POS, WS_SRC, WS_XPERM, WS_H, WS_O = range(6)
 
@@ -96,8 +98,10 @@ def _check(fn: str, st: int):
 
 def make_shape(T, d_model, d_ff, E, k=2, mode="tc", dtype="bf16", renormalize=True,
                capacity_factor=1.0) -> MoeShape:
+    if mode not in MODES:
+        raise ValueError(f"mode must be one of {sorted(MODES)}, got {mode!r}")
     return MoeShape(T=int(T), d_model=int(d_model), d_ff=int(d_ff), E=int(E), k=int(k),
-                    mode=MOE_TOKEN_CHOICE if mode == "tc" else MOE_EXPERT_CHOICE,
+                    mode=MODES[mode],
                     dtype=MOE_BF16 if dtype in ("bf16", torch.bfloat16) else MOE_FP32,
                     renormalize=1 if renormalize else 0,
                     capacity_factor=float(capacity_factor))
@@ -160,7 +164,8 @@ def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch
 
 def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormalize=True,
               want_probs=True, want_counts=True, workspace=None) -> dict:
-    """Router only. Token choice returns idx/w [T,k]; expert choice idx/w [E,C]."""
+    """Router only. Token choice (with or without capacity) returns idx/w [T,k];
+    expert choice idx/w [E,C]."""
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
@@ -170,7 +175,7 @@ def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormal
     E = W_g.shape[1]
     shape = make_shape(T, d, 64, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
     ws = _workspace(shape, dev, workspace)
-    if mode == "tc":
+    if mode != "ec":
         idx = torch.empty(T, k, dtype=torch.int32, device=dev)
         w = torch.empty(T, k, dtype=torch.float32, device=dev)
     else:
@@ -208,7 +213,7 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
         _need(y, "y", torch.float32, dev)
     idx = w = probs = counts = fo = po = lo = None
     if want_routing:
-        if mode == "tc":
+        if mode != "ec":
             idx = torch.empty(T, k, dtype=torch.int32, device=dev)
             w = torch.empty(T, k, dtype=torch.float32, device=dev)
         else:
@@ -218,7 +223,7 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
         counts = torch.empty(E, dtype=torch.int32, device=dev)
     if want_probs:
         probs = torch.empty(T, E, dtype=torch.float32, device=dev)
-    if want_stats and mode == "tc":
+    if want_stats and mode != "ec":
         fo = torch.empty(E, dtype=torch.float32, device=dev)
         po = torch.empty(E, dtype=torch.float32, device=dev)
         lo = torch.empty(1, dtype=torch.float32, device=dev)

@@ -6,6 +6,8 @@
 // rows by expert before sending them; here the same grouping feeds the grouped GEMMs
 // of one GPU. Row order inside an expert's group is the flattened (token, slot)
 // order, so the permutation is stable and deterministic without atomics.
+#include <limits.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -14,13 +16,19 @@ namespace {
 constexpr int kScanThreads = 1024;
 
 // One workgroup. Entry (e, b) of the expert-major sequence q = e*nblk + b holds
-// blk_counts[b, e]; its exclusive prefix is the first row of block b's slots for
-// expert e, and the prefix at (e, 0) is the start of expert e's group.
+// blk_counts[b, e]; its exclusive prefix is the first slot of block b's slots for
+// expert e in the expert's flattened (token, slot) order, and the prefix at (e, 0) is
+// the start of expert e's group. With an expert capacity `cap`, expert e keeps only
+// the first cap of its slots: its group shrinks to min(count, cap) rows, the groups
+// are laid out from those sizes, and base[b, e] is the clamped group start plus the
+// block's unclamped prefix (rows at or past start + cap are dropped by the permute).
+// counts stay the unclamped assignments. cap = INT_MAX: no capacity.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    const int32_t* __restrict__ blk_counts, int nblk, int E, int32_t* counts, int32_t* offsets,
-    int32_t* base, int32_t* user_counts) {
+    const int32_t* __restrict__ blk_counts, int nblk, int E, int cap, int32_t* counts,
+    int32_t* offsets, int32_t* base, int32_t* user_counts) {
   __shared__ int sh[17];
-  __shared__ int off_sh[65];
+  __shared__ int off_sh[65];   // unclamped group starts
+  __shared__ int offc_sh[65];  // group starts from the clamped sizes
   const long n = (long)nblk * E;
   const int tid = threadIdx.x;
   const long per = (n + kScanThreads - 1) / kScanThreads;
@@ -31,16 +39,31 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     local += blk_counts[(size_t)b * E + e];
   }
   int total;
-  int run = block_exclusive_scan(local, sh, &total);
+  const int run0 = block_exclusive_scan(local, sh, &total);
+  int run = run0;
   for (long q = qb; q < qe; ++q) {
     const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
     if (b == 0) off_sh[e] = run;
-    base[(size_t)b * E + e] = run;
     run += blk_counts[(size_t)b * E + e];
   }
   if (tid == 0) off_sh[E] = total;
   __syncthreads();
-  if (tid <= E) offsets[tid] = off_sh[tid];
+  if (tid == 0) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+      offc_sh[e] = acc;
+      acc += min(off_sh[e + 1] - off_sh[e], cap);
+    }
+    offc_sh[E] = acc;
+  }
+  __syncthreads();
+  run = run0;
+  for (long q = qb; q < qe; ++q) {
+    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
+    base[(size_t)b * E + e] = offc_sh[e] + (run - off_sh[e]);
+    run += blk_counts[(size_t)b * E + e];
+  }
+  if (tid <= E) offsets[tid] = offc_sh[tid];
   if (tid < E) {
     const int c = off_sh[tid + 1] - off_sh[tid];
     counts[tid] = c;
@@ -49,12 +72,19 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 }
 
 // One wave per token: slots first (pos, src), then the row copy to every slot's row.
+// With an expert capacity (cap < INT_MAX) a slot whose rank among its expert's slots
+// (flattened token order) is cap or more is dropped: pos = -1, weight 0, and when the
+// token lost a slot its kept weights are divided by their sum (renorm) — the capacity
+// routing of 机器学习基础系列——混合专家模型 (expert_capacity_routing). x_perm == nullptr:
+// slots and weights only (routing without the layer).
 template <int EB>
 __global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict__ x, int T, int d,
                                                          int E, int k, const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ lrank,
                                                          const int32_t* __restrict__ base,
-                                                         int32_t* pos, int32_t* src,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int cap, int renorm, int32_t* pos,
+                                                         int32_t* src, float* w,
                                                          char* __restrict__ x_perm) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -64,10 +94,25 @@ __global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict_
   if (lane < k) {
     const int e = idx[(size_t)t * k + lane];
     p = base[(size_t)(t / kRouterTokens) * E + e] + lrank[(size_t)t * k + lane];
+    if (p - offsets[e] >= cap) p = -1;  // dropped by the capacity
     if (p < 0 || p >= R) p = -1;  // unreachable for consistent tables; never write outside
     pos[(size_t)t * k + lane] = p;
     if (p >= 0) src[p] = t;
   }
+  if (cap != INT_MAX) {
+    const uint64_t slots = __ballot(lane < k), kept = __ballot(lane < k && p >= 0);
+    if (kept != slots) {  // the token lost a slot (uniform over the wave)
+      const float wj = lane < k ? w[(size_t)t * k + lane] : 0.f;
+      float sk = p >= 0 ? wj : 0.f;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) sk += __shfl_xor(sk, o);  // lanes 0..7, fixed tree
+      if (lane < k) {
+        const float wk = renorm ? (sk > 0.f ? wj / sk : 0.f) : wj;
+        w[(size_t)t * k + lane] = p >= 0 ? wk : 0.f;
+      }
+    }
+  }
+  if (!x_perm) return;
   const size_t row_bytes = (size_t)d * EB;
   const int nch = (int)(row_bytes / 16);
   const char* xr = x + (size_t)t * row_bytes;
@@ -108,24 +153,27 @@ __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict_
 
 }  // namespace
 
-hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int32_t* counts,
-                                int32_t* offsets, int32_t* base, int32_t* user_counts,
-                                hipStream_t s) {
-  dispatch_scan_kernel<<<1, kScanThreads, 0, s>>>(blk_counts, nblk, E, counts, offsets, base,
+hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int cap,
+                                int32_t* counts, int32_t* offsets, int32_t* base,
+                                int32_t* user_counts, hipStream_t s) {
+  dispatch_scan_kernel<<<1, kScanThreads, 0, s>>>(blk_counts, nblk, E, cap, counts, offsets, base,
                                                   user_counts);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
-                             int32_t* pos, int32_t* src, void* x_perm, hipStream_t s) {
+                             const int32_t* offsets, int cap, int renorm, int32_t* pos,
+                             int32_t* src, float* w, void* x_perm, hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
   if (elt_bytes == 2)
     permute_tc_kernel<2><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
-                                                base, pos, src, static_cast<char*>(x_perm));
+                                                base, offsets, cap, renorm, pos, src, w,
+                                                static_cast<char*>(x_perm));
   else
     permute_tc_kernel<4><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
-                                                base, pos, src, static_cast<char*>(x_perm));
+                                                base, offsets, cap, renorm, pos, src, w,
+                                                static_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

@@ -30,16 +30,22 @@ hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, hipStream_t s);
 
-// Dispatch prefix sum over per-block counts: counts[E], offsets[E+1],
-// base[nblk, E] (first row of each (block, expert) pair), optional user counts.
-hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int32_t* counts,
-                                int32_t* offsets, int32_t* base, int32_t* user_counts,
-                                hipStream_t s);
+// Dispatch prefix sum over per-block counts: counts[E] (unclamped), offsets[E+1] (group
+// starts; with an expert capacity cap the groups hold min(count, cap) rows),
+// base[nblk, E] (row of each (block, expert) pair's first slot), optional user counts.
+// cap = INT_MAX: no capacity.
+hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int cap,
+                                int32_t* counts, int32_t* offsets, int32_t* base,
+                                int32_t* user_counts, hipStream_t s);
 
-// Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t].
+// Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t]. With a
+// capacity (cap < INT_MAX) slots ranked cap or later in their expert get pos = -1 and
+// weight 0, and the token's kept weights w are renormalised when renorm is set.
+// x_perm == nullptr: slots and weights only.
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
-                             int32_t* pos, int32_t* src, void* x_perm, hipStream_t s);
+                             const int32_t* offsets, int cap, int renorm, int32_t* pos,
+                             int32_t* src, float* w, void* x_perm, hipStream_t s);
 
 // Expert choice: row e*C + c takes token idx[e, c].
 hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,

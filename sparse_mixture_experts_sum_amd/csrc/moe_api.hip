@@ -1,5 +1,6 @@
 // Host side of the C ABI (include/moe.h): argument checks, workspace layout and the
 // launch sequence on the caller's stream. No allocation, no synchronisation.
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -28,19 +29,42 @@ int64_t ec_capacity(const moe_shape& s) {
   return (int64_t)c;
 }
 
+// Token choice with an expert capacity: int((T / E) * cf * k), the product taken in that
+// order in double (机器学习基础系列——混合专家模型, expert_capacity_routing).
+int64_t tc_capacity(const moe_shape& s) {
+  const double c = floor((double)s.T / (double)s.E * (double)s.capacity_factor * (double)s.k);
+  if (!(c >= 0.0) || c > 9.0e18) return -1;
+  return (int64_t)c;
+}
+
+bool is_tc(int32_t mode) { return mode == MOE_TOKEN_CHOICE || mode == MOE_TOKEN_CHOICE_CAPACITY; }
+
+// Per-expert slot limit handed to the dispatch: INT_MAX without a capacity.
+int tc_cap_limit(const moe_shape& s) {
+  if (s.mode != MOE_TOKEN_CHOICE_CAPACITY) return INT_MAX;
+  const int64_t c = tc_capacity(s);
+  return c >= (int64_t)INT_MAX ? INT_MAX - 1 : (int)c;
+}
+
 moe_status check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_NULL_ARG;
   if (s->dtype != MOE_FP32 && s->dtype != MOE_BF16) return MOE_ERR_BAD_SHAPE;
-  if (s->mode != MOE_TOKEN_CHOICE && s->mode != MOE_EXPERT_CHOICE) return MOE_ERR_BAD_SHAPE;
+  if (s->mode != MOE_TOKEN_CHOICE && s->mode != MOE_EXPERT_CHOICE &&
+      s->mode != MOE_TOKEN_CHOICE_CAPACITY)
+    return MOE_ERR_BAD_SHAPE;
   if (s->T < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->E < 1) return MOE_ERR_BAD_SHAPE;
   if (s->d_model % 64 || s->d_ff % 64) return MOE_ERR_BAD_SHAPE;
   if (s->d_model > (1 << 20) || s->d_ff > (1 << 20)) return MOE_ERR_BAD_SHAPE;
   if (s->E > 64) return MOE_ERR_UNSUPPORTED;
-  if (s->mode == MOE_TOKEN_CHOICE) {
+  if (is_tc(s->mode)) {
     if (s->k < 1 || s->k > s->E) return MOE_ERR_BAD_SHAPE;
     if (s->k > 8) return MOE_ERR_UNSUPPORTED;
     if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_BAD_SHAPE;
     if (s->T * (int64_t)s->k >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+    if (s->mode == MOE_TOKEN_CHOICE_CAPACITY) {
+      if (!(s->capacity_factor > 0.0f) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
+      if (tc_capacity(*s) < 0) return MOE_ERR_BAD_SHAPE;
+    }
   } else {
     if (!(s->capacity_factor > 0.0f) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
     const int64_t C = ec_capacity(*s);
@@ -61,7 +85,7 @@ Layout make_layout(const moe_shape& s) {
     return at;
   };
   L.nblk = (int)((T + 63) / 64);
-  if (s.mode == MOE_TOKEN_CHOICE) {
+  if (is_tc(s.mode)) {
     const int64_t k = s.k;
     L.R = T * k;
     L.idx = take(T * k * 4);
@@ -175,7 +199,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
   a.E = s.E;
   a.k = s.k;
   a.renorm = s.renormalize;
-  if (s.mode == MOE_TOKEN_CHOICE) {
+  if (is_tc(s.mode)) {
     a.idx = idx;
     a.w = w;
     a.probs = probs;
@@ -184,7 +208,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     a.blk_psum = at<float>(ws, L.blk_psum);
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 0, stream));
     MOE_LAUNCH(MOE_STAGE_SCAN,
-               launch_dispatch_scan(at<int32_t>(ws, L.blk_counts), L.nblk, s.E,
+               launch_dispatch_scan(at<int32_t>(ws, L.blk_counts), L.nblk, s.E, tc_cap_limit(s),
                                     at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                                     at<int32_t>(ws, L.base), user_counts, stream));
   } else {
@@ -216,10 +240,11 @@ const char* moe_status_string(int32_t status) {
 
 moe_status moe_capacity(const moe_shape* shape, int64_t* capacity) {
   if (!shape || !capacity) return MOE_ERR_NULL_ARG;
-  if (shape->mode != MOE_EXPERT_CHOICE) return MOE_ERR_BAD_SHAPE;
+  if (shape->mode != MOE_EXPERT_CHOICE && shape->mode != MOE_TOKEN_CHOICE_CAPACITY)
+    return MOE_ERR_BAD_SHAPE;
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  *capacity = ec_capacity(*shape);
+  *capacity = shape->mode == MOE_EXPERT_CHOICE ? ec_capacity(*shape) : tc_capacity(*shape);
   return MOE_OK;
 }
 
@@ -239,7 +264,7 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
   switch (which) {
     case MOE_WS_OFFSETS: *offset = L.offsets; return MOE_OK;
     case MOE_WS_POS:
-      if (shape->mode != MOE_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+      if (!is_tc(shape->mode)) return MOE_ERR_UNSUPPORTED;
       *offset = L.pos;
       return MOE_OK;
     case MOE_WS_SRC: *offset = L.src; return MOE_OK;
@@ -262,7 +287,16 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, stream);
-  return run_router(s, L, x, W_g, b_g, idx, w, probs, counts, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, idx, w, probs, counts, ws, stream);
+  if (st != MOE_OK || s.mode != MOE_TOKEN_CHOICE_CAPACITY) return st;
+  // capacity: the dispatch decides which slots stay; weights only, no row copies
+  MOE_LAUNCH(MOE_STAGE_PERMUTE,
+             launch_permute_tc(nullptr, s.dtype == MOE_BF16 ? 2 : 4, (int)s.T, (int)s.d_model, s.E,
+                               s.k, idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.base),
+                               at<int32_t>(ws, L.offsets), tc_cap_limit(s), s.renormalize,
+                               at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w, nullptr,
+                               stream));
+  return MOE_OK;
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
@@ -292,11 +326,12 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
 
   st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, ws, stream);
   if (st != MOE_OK) return st;
-  if (s.mode == MOE_TOKEN_CHOICE) {
+  if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_PERMUTE,
                launch_permute_tc(x, eb, T, d, E, s.k, idx_b, at<int32_t>(ws, L.lrank),
-                                 at<int32_t>(ws, L.base), at<int32_t>(ws, L.pos),
-                                 at<int32_t>(ws, L.src), at<void>(ws, L.x_perm), stream));
+                                 at<int32_t>(ws, L.base), offsets, tc_cap_limit(s), s.renormalize,
+                                 at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w_b,
+                                 at<void>(ws, L.x_perm), stream));
   } else {
     MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
                                                     at<int32_t>(ws, L.src),
@@ -307,7 +342,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
                                 at<void>(ws, L.h), h_lo, stream));
   MOE_LAUNCH(MOE_STAGE_GEMM_DOWN, launch_gemm_down(bf, at<void>(ws, L.h), h_lo, W_down, offsets, E,
                                                    R, ff, d, at<float>(ws, L.o), stream));
-  if (s.mode == MOE_TOKEN_CHOICE) {
+  if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
     if (f || p || loss)
@@ -327,7 +362,7 @@ moe_status moe_aux_loss(const moe_shape* shape, const float* probs, const int32_
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
-  if (s.mode != MOE_TOKEN_CHOICE) return MOE_ERR_UNSUPPORTED;
+  if (!is_tc(s.mode)) return MOE_ERR_UNSUPPORTED;
   if (!f || !p || !loss) return MOE_ERR_NULL_ARG;
   if (s.T > 0 && (!probs || !idx || !ws)) return MOE_ERR_NULL_ARG;
   if (!aligned16(ws)) return MOE_ERR_MISALIGNED;

@@ -84,6 +84,31 @@ def test_capacity(M):
         M.capacity(M.make_shape(64, 64, 64, 8, mode="tc"))
 
 
+def test_token_choice_capacity_host_checks(M):
+    # the page's example call of the capacity routing: T=100, E=8, k=2, cf=1.25 -> 31
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "page_values.json")) as fh:
+        g = json.load(fh)["p5_capacity_of_page_call"]
+    s = M.make_shape(g["T"], 64, 64, g["E"], g["k"], mode="tc_capacity",
+                     capacity_factor=g["capacity_factor"])
+    assert M.capacity(s) == g["value"]
+    # int((T / E) * cf * k) in double, the product in that order
+    for T, E, k, cf in ((8192, 8, 2, 1.0), (4096, 64, 4, 0.5), (7, 8, 1, 1.0), (1000, 3, 2, 1.1)):
+        s = M.make_shape(T, 64, 64, E, k, mode="tc_capacity", capacity_factor=cf)
+        assert M.capacity(s) == int((T / E) * float(ctypes.c_float(cf).value) * k)
+    assert M.capacity(M.make_shape(7, 64, 64, 8, 1, mode="tc_capacity")) == 0  # valid: drops all
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(M.MoEError) as ei:
+            M.workspace_size(M.make_shape(64, 64, 64, 8, 2, mode="tc_capacity",
+                                          capacity_factor=bad))
+        assert ei.value.status == 2
+    s = M.make_shape(1000, 256, 512, 8, 2, mode="tc_capacity", capacity_factor=1.0)
+    assert M.workspace_size(s) == M.workspace_size(M.make_shape(1000, 256, 512, 8, 2, mode="tc"))
+    assert M.workspace_offset(s, M.WS_POS) >= 0
+    with pytest.raises(ValueError):
+        M.make_shape(64, 64, 64, 8, 2, mode="capacity")
+
+
 def test_workspace_offsets_are_inside(M):
     for mode in ("tc", "ec"):
         s = M.make_shape(1000, 256, 512, 8, 2, mode=mode)
