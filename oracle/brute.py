@@ -168,3 +168,22 @@ def forward_tc_capacity(x, Wg, b, Wgate, Wup, Wdown, k, cf, renormalize=True):
         kepts.append(keep)
     return {"y": ys, "idx": idxs, "w": ws, "kept": kepts, "load": load}
 
+
+
+def router_z_loss(x, Wg, b):
+    """Mean over tokens of (log sum_e exp(s_te))^2 with s = x W_g (+ b), token by
+    token with scalar exp and log (P3 ``router_z_loss``)."""
+    T = len(x)
+    if T == 0:
+        return 0.0
+    acc = 0.0
+    for t in range(T):
+        s = _vecmat(x[t], Wg)
+        if b is not None:
+            s = [s[e] + float(b[e]) for e in range(len(s))]
+        z = 0.0
+        for v in s:
+            z += math.exp(v)
+        lz = math.log(z)
+        acc += lz * lz
+    return acc / T

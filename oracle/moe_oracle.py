@@ -36,6 +36,10 @@ Readings where the pages leave a step open or disagree:
   * expert choice: softmax over tokens of each expert's logit column, top-C
     tokens per expert with C = floor(T*cf/E), outputs combined with the
     selected scores and no renormalisation; a token no expert picks gets 0.
+  * router z-loss (P3 ``router_z_loss``) is taken on the logits the softmax sees,
+    bias included, for every routing mode (it depends on the logits only); with
+    no tokens it is 0. P5 prints another quantity under the same name (a mean
+    sum of squared gates); it conflicts with P3 and is not provided.
   * token choice with an expert capacity (P5 ``expert_capacity_routing``):
     capacity = int((T / E) * cf * k); assignments are taken token by token and
     kept while the expert is below capacity. The page walks a token's slots
@@ -180,6 +184,17 @@ def aux_stats(probs, idx, E, k):
     p = probs.mean(axis=0)
     loss = E * np.sum((f / k) * p)
     return f, p, float(loss), c
+
+
+def router_z_loss(s):
+    """Router z-loss (P3 ``router_z_loss``, the ST-MoE form): the mean over tokens
+    of the squared log-partition log(sum_e exp(s_te)) of the router logits. The
+    logits are the ones the softmax normalises, bias included. No tokens: 0."""
+    s = _f64(s)
+    if s.shape[0] == 0:
+        return 0.0
+    lse = np.log(np.exp(s).sum(axis=1))
+    return float(np.mean(lse ** 2))
 
 
 # --------------------------------------------------------------------------

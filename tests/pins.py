@@ -457,4 +457,43 @@ def pin_capacity_keeps_earliest_tokens(O):
     assert np.all(sums[~kept.any(axis=1)] == 0.0)
 
 
+# ----------------------------------------------------------------------------
+# router z-loss
+# ----------------------------------------------------------------------------
+
+def pin_zloss_brute(O):
+    """Equals the token-by-token scalar computation, with and without a bias."""
+    for seed, T, E, bias in [(41, 7, 4, True), (42, 5, 8, False), (43, 1, 3, True)]:
+        c = _case(seed, T=T, E=E, bias=bias, wg_std=1.3)
+        s = O.router_logits(c["x"], c["Wg"], c["b"])
+        ref = B.router_z_loss(_lists(c["x"]), _lists(c["Wg"]), _lists(c["b"]))
+        assert math.isclose(O.router_z_loss(s), ref, rel_tol=1e-12), (seed, ref)
+
+
+def pin_zloss_library(O):
+    """Equals torch.logsumexp squared and averaged over tokens."""
+    r = _rng(44)
+    for T, E in [(33, 8), (5, 64), (16, 1)]:
+        s = r.standard_normal((T, E)) * 3.0
+        ref = float((torch.logsumexp(torch.from_numpy(s), dim=-1) ** 2).mean())
+        assert math.isclose(O.router_z_loss(s), ref, rel_tol=1e-12)
+
+
+def pin_zloss_closed_forms(O):
+    """Equal logits c: (c + log E)^2 per token; one expert: mean of s^2; a per-token
+    shift c_t moves each log-partition by c_t; no tokens: 0."""
+    for E, c in [(8, 0.0), (4, -2.5), (64, 1.25)]:
+        assert math.isclose(O.router_z_loss(np.full((3, E), c)), (c + math.log(E)) ** 2,
+                            rel_tol=1e-13)
+    s1 = np.array([[0.5], [-2.0], [3.0]])
+    assert math.isclose(O.router_z_loss(s1), (0.25 + 4.0 + 9.0) / 3, rel_tol=1e-14)
+    r = _rng(45)
+    s = r.standard_normal((6, 5))
+    lse = [math.log(sum(math.exp(v) for v in row)) for row in s.tolist()]
+    shift = r.standard_normal(6)
+    want = sum((a + b) ** 2 for a, b in zip(lse, shift.tolist())) / 6
+    assert math.isclose(O.router_z_loss(s + shift[:, None]), want, rel_tol=1e-12)
+    assert O.router_z_loss(np.zeros((0, 4))) == 0.0
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -42,6 +42,11 @@ MUTANTS = {
     "ec_score_unweighted": ("y[tt] += _f64(score[e])[:, None] * out", "y[tt] += out"),
     "margin_off_by_one": ("return ps[:, k - 1] - ps[:, k]", "return ps[:, k] - ps[:, k + 1 if k + 1 < E else k]"),
     "tc_capacity_keeps_one_more": ("if load[e] < cap:", "if load[e] <= cap:"),
+    "zloss_no_square": ("return float(np.mean(lse ** 2))", "return float(np.mean(lse))"),
+    "zloss_no_log": ("lse = np.log(np.exp(s).sum(axis=1))", "lse = np.exp(s).sum(axis=1)"),
+    "zloss_sum_not_mean": ("return float(np.mean(lse ** 2))", "return float(np.sum(lse ** 2))"),
+    "zloss_over_tokens": ("lse = np.log(np.exp(s).sum(axis=1))", "lse = np.log(np.exp(s).sum(axis=0))"),
+    "zloss_max_not_lse": ("lse = np.log(np.exp(s).sum(axis=1))", "lse = s.max(axis=1)"),
     "tc_capacity_no_zero_guard": ("rows[rows == 0] = 1.0", "rows = rows"),
     "tc_capacity_dropped_keep_gate": ("g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)",
                                       "g = np.take_along_axis(p, idx, axis=1)"),
