@@ -14,6 +14,8 @@
  *   - load-balancing statistics f_i, p_i and loss = E * sum_i (f_i / k) p_i
  *     ("Mixture of Experts（MoE）の理論と実装", load_balancing_loss; the Korean page's
  *     compute_load_balancing_loss);
+ *   - router z-loss z = mean_t (log sum_e exp(s_te))^2 over the router logits s (the
+ *     Korean page's router_z_loss);
  *   - expert-choice routing with capacity C = floor(T * cf / E): each expert takes the
  *     C tokens of largest softmax-over-tokens score (the Korean page's
  *     ExpertChoiceGating);
@@ -144,16 +146,20 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
  * Optional outputs (NULL to skip):
  *   probs  [T, E] fp32    softmax probabilities (expert choice: over tokens, per column)
  *   counts [E] int32      assignments per expert (expert choice: C each)
+ *   z_loss [1] fp32       router z-loss: mean over tokens of (log sum_e exp(s_te))^2, s the
+ *                         logits with the bias (every mode; 0 when T = 0). Computed in the
+ *                         router's pass over x: one fp32 log-partition per token, fixed-order
+ *                         fp32 sums per 64 tokens, then an fp64 sum over those.
  * Token choice with capacity: idx and counts are those of plain token choice (counts
  * before any drop); w holds the weights after the capacity: 0 for a dropped slot, and
  * for a token that lost a slot its kept weights divided by their sum when renormalize
  * = 1 (a token that lost every slot gets zeros), unchanged when renormalize = 0. An
  * expert keeps the assignments of lowest token index; a token's slots go to distinct
  * experts, so the order of slots within a token decides nothing.
- * idx and w are required. */
+ * idx and w are required when T > 0 (with T = 0 there is nothing to write). */
 moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                     int32_t* idx, float* w, float* probs, int32_t* counts, void* ws,
-                     size_t ws_bytes, hipStream_t stream);
+                     int32_t* idx, float* w, float* probs, int32_t* counts, float* z_loss,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Whole layer forward: router, dispatch (histogram, prefix sum, stable permutation of
  * token rows into expert-contiguous order), grouped SwiGLU gate/up GEMM, grouped down
@@ -163,8 +169,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
  *   W_down        [E, d_ff, d_model] dtype
  *   y             [T, d_model] fp32   y_t = sum over the token's experts of
  *                 weight * E_e(x_t); in expert choice a token no expert takes gets 0
- * Optional outputs (NULL to skip): idx, w, probs, counts as in moe_route, and, token
- * choice only (with capacity: computed from the assignments before any drop):
+ * Optional outputs (NULL to skip): idx, w, probs, counts, z_loss as in moe_route, and,
+ * token choice only (with capacity: computed from the assignments before any drop):
  *   f     [E] fp32   counts / T (sums to k)
  *   p     [E] fp32   mean over tokens of probs
  *   loss  [1] fp32   E * sum_e (f_e / k) * p_e (1 under uniform routing)
@@ -179,7 +185,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
                        const void* W_gate, const void* W_up, const void* W_down, float* y,
                        int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
-                       float* loss, void* ws, size_t ws_bytes, hipStream_t stream);
+                       float* loss, float* z_loss, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
 
 /* Load-balancing statistics from router outputs (Mixture of Experts（MoE）の理論と実装,
  * load_balancing_loss; the Korean page's compute_load_balancing_loss), token choice:

@@ -78,8 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_capacity.argtypes = [S, ctypes.POINTER(I64)]
     lib.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_workspace_offset.argtypes = [S, I32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.moe_route.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_route.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_aux_loss.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_profile_enable.argtypes = [I32]
     lib.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
@@ -163,9 +163,9 @@ def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch
 
 
 def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormalize=True,
-              want_probs=True, want_counts=True, workspace=None) -> dict:
+              want_probs=True, want_counts=True, want_z_loss=False, workspace=None) -> dict:
     """Router only. Token choice (with or without capacity) returns idx/w [T,k];
-    expert choice idx/w [E,C]."""
+    expert choice idx/w [E,C]. want_z_loss adds the router z-loss (fp32 [1])."""
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
@@ -184,17 +184,18 @@ def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormal
         w = torch.empty(E, C, dtype=torch.float32, device=dev)
     probs = torch.empty(T, E, dtype=torch.float32, device=dev) if want_probs else None
     counts = torch.empty(E, dtype=torch.int32, device=dev) if want_counts else None
+    z = torch.empty(1, dtype=torch.float32, device=dev) if want_z_loss else None
     _check("moe_route", load_library().moe_route(
         ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(idx), _ptr(w), _ptr(probs),
-        _ptr(counts), _ptr(ws), ws.numel(), _stream(dev)))
-    return {"idx": idx, "w": w, "probs": probs, "counts": counts}
+        _ptr(counts), _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
+    return {"idx": idx, "w": w, "probs": probs, "counts": counts, "z_loss": z}
 
 
 def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_factor=1.0,
                 renormalize=True, want_routing=True, want_probs=True, want_stats=True,
-                workspace=None, y=None) -> dict:
+                want_z_loss=False, workspace=None, y=None) -> dict:
     """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
-    counts and (token choice) f, p, loss."""
+    counts, (token choice) f, p, loss, and the router z-loss."""
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
@@ -227,12 +228,13 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
         fo = torch.empty(E, dtype=torch.float32, device=dev)
         po = torch.empty(E, dtype=torch.float32, device=dev)
         lo = torch.empty(1, dtype=torch.float32, device=dev)
+    z = torch.empty(1, dtype=torch.float32, device=dev) if want_z_loss else None
     _check("moe_forward", load_library().moe_forward(
         ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
         _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo), _ptr(po), _ptr(lo),
-        _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
     return {"y": y, "idx": idx, "w": w, "probs": probs, "counts": counts, "f": fo, "p": po,
-            "loss": lo, "workspace": ws, "shape": shape}
+            "loss": lo, "z_loss": z, "workspace": ws, "shape": shape}
 
 
 def moe_aux_loss(probs, idx, *, workspace=None) -> dict:

@@ -129,9 +129,12 @@ constexpr int kAuxParts = 16;
 __global__ __launch_bounds__(1024) void aux_final_kernel(const int32_t* __restrict__ blk_counts,
                                                          const float* __restrict__ blk_psum, int nblk,
                                                          int T, int E, int k, float* f, float* p,
-                                                         float* loss, int32_t* counts) {
+                                                         float* loss, int32_t* counts,
+                                                         const float* __restrict__ blk_zsum,
+                                                         float* z_loss) {
   __shared__ long long csum[kAuxParts][64];
   __shared__ double psum[kAuxParts][64];
+  __shared__ double zsum[kAuxParts];
   __shared__ double term[64];
   const int e = threadIdx.x & 63, part = threadIdx.x >> 6;
   const int per = (nblk + kAuxParts - 1) / kAuxParts;
@@ -146,7 +149,18 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const int32_t* __restri
   }
   csum[part][e] = c;
   psum[part][e] = ps;
+  if (e == 0) {
+    double zs = 0.0;
+    if (blk_zsum)
+      for (int b = b0; b < b1; ++b) zs += (double)blk_zsum[b];
+    zsum[part] = zs;
+  }
   __syncthreads();
+  if (threadIdx.x == 64 && z_loss && blk_zsum) {
+    double zt = 0.0;
+    for (int i = 0; i < kAuxParts; ++i) zt += zsum[i];
+    *z_loss = (float)(zt / (double)T);
+  }
   if (part == 0 && e < E) {
     long long ct = 0;
     double pt = 0.0;
@@ -197,8 +211,9 @@ hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, in
 
 hipError_t launch_aux_final(const int32_t* blk_counts, const float* blk_psum, int nblk, int T,
                             int E, int k, float* f, float* p, float* loss, int32_t* counts,
-                            hipStream_t s) {
-  aux_final_kernel<<<1, 1024, 0, s>>>(blk_counts, blk_psum, nblk, T, E, k, f, p, loss, counts);
+                            const float* blk_zsum, float* z_loss, hipStream_t s) {
+  aux_final_kernel<<<1, 1024, 0, s>>>(blk_counts, blk_psum, nblk, T, E, k, f, p, loss, counts,
+                                      blk_zsum, z_loss);
   return hipGetLastError();
 }
 

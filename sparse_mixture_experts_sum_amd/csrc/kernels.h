@@ -17,12 +17,15 @@ struct RouterArgs {
   int32_t* lrank;       // [T, k] rank of the slot among equal experts within its block
   int32_t* blk_counts;  // [nblk, E]
   float* blk_psum;      // [nblk, E] column sums of probs over the block's tokens
+  // both modes, optional: per block, sum over its tokens of logsumexp(logits)^2
+  float* blk_zsum;      // [nblk] or nullptr
   // expert choice output
   float* logitsT;       // [E, T] (expert choice only)
 };
 
 // Token-choice router (logits, softmax, top-k, weights, per-block histogram and
-// slot ranks, per-block probability sums) or, with ec = 1, expert-choice logits.
+// slot ranks, per-block probability sums) or, with ec = 1, expert-choice logits; in
+// either mode, when blk_zsum is set, the per-block z-loss partials.
 hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
 
 // Expert choice: per expert, softmax over tokens, top-C tokens (ascending token
@@ -73,9 +76,10 @@ hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* sc
 // Per-block counts and probability sums from router outputs (standalone aux loss).
 hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,
                                int32_t* blk_counts, float* blk_psum, hipStream_t s);
-// f, p, loss (and optional counts) from per-block partials.
+// f, p, loss (and optional counts) from per-block partials (E = 0: none of them), and
+// z_loss = sum of blk_zsum / T when both are set.
 hipError_t launch_aux_final(const int32_t* blk_counts, const float* blk_psum, int nblk, int T,
                             int E, int k, float* f, float* p, float* loss, int32_t* counts,
-                            hipStream_t s);
+                            const float* blk_zsum, float* z_loss, hipStream_t s);
 // Zero-fill helper (device memory), used for empty inputs.
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);

@@ -20,7 +20,8 @@ struct Layout {
   int64_t R = 0, C = 0;
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
-         offsets = 0, counts = 0, logitsT = 0, x_perm = 0, h = 0, h_lo = 0, o = 0, total = 0;
+         offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
+         total = 0;
 };
 
 int64_t ec_capacity(const moe_shape& s) {
@@ -102,6 +103,7 @@ Layout make_layout(const moe_shape& s) {
     L.idx = take(L.R * 4);
     L.w = take(L.R * 4);
   }
+  L.blk_zsum = take((size_t)L.nblk * 4);
   L.offsets = take((E + 1) * 4);
   L.counts = take(E * 4);
   L.src = take(L.R * 4);
@@ -176,7 +178,9 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
-moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, hipStream_t stream) {
+moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, float* z_loss,
+                      hipStream_t stream) {
+  if (z_loss) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(z_loss, 4, stream));
   if (f) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(f, (size_t)E * 4, stream));
   if (p) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(p, (size_t)E * 4, stream));
   if (loss) MOE_LAUNCH(MOE_STAGE_AUX, launch_fill_zero(loss, 4, stream));
@@ -185,10 +189,11 @@ moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, h
 }
 
 // Router stage shared by moe_route and moe_forward. Token choice writes idx/w and the
-// dispatch tables; expert choice writes idx/score and the group offsets.
+// dispatch tables; expert choice writes idx/score and the group offsets. With want_z the
+// router also leaves the per-block z-loss partials in the workspace.
 moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
                       const float* b_g, int32_t* idx, float* w, float* probs,
-                      int32_t* user_counts, void* ws, hipStream_t stream) {
+                      int32_t* user_counts, bool want_z, void* ws, hipStream_t stream) {
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
   a.x = x;
@@ -199,6 +204,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
   a.E = s.E;
   a.k = s.k;
   a.renorm = s.renormalize;
+  a.blk_zsum = want_z ? at<float>(ws, L.blk_zsum) : nullptr;
   if (is_tc(s.mode)) {
     a.idx = idx;
     a.w = w;
@@ -276,19 +282,23 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
 }
 
 moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                     int32_t* idx, float* w, float* probs, int32_t* counts, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+                     int32_t* idx, float* w, float* probs, int32_t* counts, float* z_loss,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
-  if (!idx || !w) return MOE_ERR_NULL_ARG;
-  if (s.T > 0 && (!x || !W_g || !ws)) return MOE_ERR_NULL_ARG;
+  if (s.T > 0 && (!idx || !w || !x || !W_g || !ws)) return MOE_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_g) || !aligned16(ws)) return MOE_ERR_MISALIGNED;
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, stream);
-  st = run_router(s, L, x, W_g, b_g, idx, w, probs, counts, ws, stream);
-  if (st != MOE_OK || s.mode != MOE_TOKEN_CHOICE_CAPACITY) return st;
+  if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, z_loss, stream);
+  st = run_router(s, L, x, W_g, b_g, idx, w, probs, counts, z_loss != nullptr, ws, stream);
+  if (st != MOE_OK) return st;
+  if (z_loss)
+    MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, (int)s.T, 0, s.k, nullptr,
+                                               nullptr, nullptr, nullptr,
+                                               at<float>(ws, L.blk_zsum), z_loss, stream));
+  if (s.mode != MOE_TOKEN_CHOICE_CAPACITY) return MOE_OK;
   // capacity: the dispatch decides which slots stay; weights only, no row copies
   MOE_LAUNCH(MOE_STAGE_PERMUTE,
              launch_permute_tc(nullptr, s.dtype == MOE_BF16 ? 2 : 4, (int)s.T, (int)s.d_model, s.E,
@@ -302,7 +312,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
                        const void* W_gate, const void* W_up, const void* W_down, float* y,
                        int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
-                       float* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+                       float* loss, float* z_loss, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
@@ -313,7 +324,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
     return MOE_ERR_MISALIGNED;
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, stream);
+  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, z_loss, stream);
 
   const int bf = s.dtype == MOE_BF16;
   const int eb = bf ? 2 : 4;
@@ -324,7 +335,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
   void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
-  st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, z_loss != nullptr, ws, stream);
   if (st != MOE_OK) return st;
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_PERMUTE,
@@ -345,13 +356,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
-    if (f || p || loss)
+    if (f || p || loss || z_loss)
       MOE_LAUNCH(MOE_STAGE_AUX,
                  launch_aux_final(at<int32_t>(ws, L.blk_counts), at<float>(ws, L.blk_psum),
-                                  L.nblk, T, E, s.k, f, p, loss, nullptr, stream));
+                                  L.nblk, T, E, s.k, f, p, loss, nullptr,
+                                  at<float>(ws, L.blk_zsum), z_loss, stream));
   } else {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, T, d, E,
                                                     (int)L.C, y, stream));
+    if (z_loss)
+      MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, T, 0, s.k, nullptr,
+                                                 nullptr, nullptr, nullptr,
+                                                 at<float>(ws, L.blk_zsum), z_loss, stream));
   }
   return MOE_OK;
 }
@@ -368,12 +384,13 @@ moe_status moe_aux_loss(const moe_shape* shape, const float* probs, const int32_
   if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, stream);
+  if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, nullptr, stream);
   MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_partials(probs, idx, (int)s.T, s.E, s.k,
                                                 at<int32_t>(ws, L.blk_counts),
                                                 at<float>(ws, L.blk_psum), stream));
   MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(at<int32_t>(ws, L.blk_counts), at<float>(ws, L.blk_psum),
-                                             L.nblk, (int)s.T, s.E, s.k, f, p, loss, counts, stream));
+                                             L.nblk, (int)s.T, s.E, s.k, f, p, loss, counts,
+                                             nullptr, nullptr, stream));
   return MOE_OK;
 }
 

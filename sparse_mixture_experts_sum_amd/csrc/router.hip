@@ -128,6 +128,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   __shared__ __attribute__((aligned(16))) TI Wl[EP * LDW];
   __shared__ float Ls[kRT * LSP];
   __shared__ float red[256];
+  __shared__ float zred[4];
   __shared__ float bias_s[64];
   __shared__ int sel[kRT * 8];
   __shared__ int running[64];
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
         if (t < T) a.logitsT[(size_t)e * T + t] = acc[nb][r] + bz;
       }
     }
-    return;
+    if (!a.blk_zsum) return;  // else on to the per-token log-partition below
   }
 
 #pragma unroll
@@ -236,6 +237,21 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   }
   lsum += __shfl_xor(lsum, 1);
   lsum += __shfl_xor(lsum, 2);
+
+  // z-loss partial: sum over the block's tokens of (log sum_e exp(s_e))^2, in a fixed
+  // order (xor tree over the 16 tokens of a wave, then the four waves in order)
+  if (a.blk_zsum) {
+    const float lse = lmax + logf(lsum);
+    float zv = (valid && part == 0) ? lse * lse : 0.f;
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) zv += __shfl_xor(zv, off);
+    if (lane == 0) zred[wave] = zv;
+    if (ec) {
+      __syncthreads();
+      if (tid == 0) a.blk_zsum[blockIdx.x] = ((zred[0] + zred[1]) + zred[2]) + zred[3];
+      return;
+    }
+  }
 
   // top-k by (logit desc, expert asc); every thread of the token ends with the same picks
   uint32_t taken = 0;
@@ -289,6 +305,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     }
   }
   block_expert_sums<PER>(pv, PER, E, red, a.blk_psum + (size_t)blockIdx.x * E);
+  // (block_expert_sums' barrier also orders the zred writes above before this read)
+  if (a.blk_zsum && tid == 0) a.blk_zsum[blockIdx.x] = ((zred[0] + zred[1]) + zred[2]) + zred[3];
 
   const int nvalid = min(kRT, T - t0);
   // slot ranks within the block: wave 0 walks the slots in flattened order, 64 at a time

@@ -132,20 +132,21 @@ def test_forward_argument_errors_before_any_hip_call(M):
         a = dict(args)
         a.update(over)
         return lib.moe_forward(ctypes.byref(shape), a["x"], a["Wg"], a["b"], a["Wgate"], a["Wup"],
-                               a["Wdown"], a["y"], None, None, None, None, None, None, None, ws,
-                               ws_bytes, None)
+                               a["Wdown"], a["y"], None, None, None, None, None, None, None, None,
+                               ws, ws_bytes, None)
 
     assert call(x=None) == 1
     assert call(Wdown=None) == 1
     assert call(ws=None) == 1
     assert call(y=P(4100)) == 5                      # misaligned
     assert call(ws_bytes=n - 1) == 4                 # workspace too small
-    assert lib.moe_forward(None, *([None] * 15), 0, None) == 1
+    assert lib.moe_forward(None, *([None] * 16), 0, None) == 1
     ec = M.make_shape(64, 128, 256, 8, mode="ec")
     f = P(8192)
     assert lib.moe_forward(ctypes.byref(ec), good, good, None, good, good, good, good, None, None,
-                           None, None, f, None, None, good, n, None) == 3
-    assert lib.moe_route(ctypes.byref(s), good, good, None, None, good, None, None, good, n, None) == 1
+                           None, None, f, None, None, None, good, n, None) == 3
+    assert lib.moe_route(ctypes.byref(s), good, good, None, None, good, None, None, None, good, n,
+                         None) == 1
     assert lib.moe_aux_loss(ctypes.byref(ec), good, good, good, good, good, None, good, n, None) == 3
     assert lib.moe_aux_loss(ctypes.byref(s), good, good, None, good, good, None, good, n, None) == 1
 

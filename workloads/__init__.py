@@ -43,8 +43,9 @@ class Workload:
     f: int                     # d_ff per expert
     E: int                     # experts
     k: int = 2                 # top-k (token choice)
-    mode: str = "tc"           # "tc" token choice, "ec" expert choice
-    cf: float = 1.0            # capacity factor (expert choice)
+    mode: str = "tc"           # "tc" token choice, "ec" expert choice,
+                               # "tc_capacity" token choice with an expert capacity
+    cf: float = 1.0            # capacity factor (expert choice, token choice with capacity)
     renormalize: bool = True   # renormalise the selected top-k weights
     x_std: float = 1.0
     wg_std: float = 0.02
@@ -59,8 +60,9 @@ class Workload:
 
     @property
     def rows(self) -> int:
-        """Routed rows R: T*k (token choice) or E*C (expert choice)."""
-        return self.T * self.k if self.mode == "tc" else self.E * self.capacity
+        """Rows the dispatch lays out: T*k (token choice; with a capacity, the kept
+        rows are a prefix of them) or E*C (expert choice)."""
+        return self.E * self.capacity if self.mode == "ec" else self.T * self.k
 
 
 CONFIGS = {
