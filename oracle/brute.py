@@ -71,14 +71,21 @@ def _best_subset(values, size):
     return list(best)
 
 
-def forward_tc(x, Wg, b, Wgate, Wup, Wdown, k, renormalize=True):
-    """Token-choice forward by literal loops. Returns dict(y, idx, w, probs)."""
+def forward_tc(x, Wg, b, Wgate, Wup, Wdown, k, renormalize=True, Wn=None, eps=None):
+    """Token-choice forward by literal loops. Returns dict(y, idx, w, probs).
+    With eps, the training noise of P3 ``TopKGating`` is added to each logit:
+    log(1 + e^z) * eps with z = x W_noise, or eps alone when Wn is None."""
     T, E = len(x), len(Wg[0])
     ys, idxs, ws, ps = [], [], [], []
     for t in range(T):
         s = _vecmat(x[t], Wg)
         if b is not None:
             s = [s[e] + float(b[e]) for e in range(E)]
+        if eps is not None:
+            zn = _vecmat(x[t], Wn) if Wn is not None else None
+            for e in range(E):
+                scale = math.log(1.0 + math.exp(zn[e])) if zn is not None else 1.0
+                s[e] = s[e] + scale * float(eps[t][e])
         p = _softmax(s)
         chosen = _best_subset(p, k)
         # slot order: descending probability, lower index first on ties

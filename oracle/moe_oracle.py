@@ -36,6 +36,10 @@ Readings where the pages leave a step open or disagree:
   * expert choice: softmax over tokens of each expert's logit column, top-C
     tokens per expert with C = floor(T*cf/E), outputs combined with the
     selected scores and no renormalisation; a token no expert picks gets 0.
+  * noisy top-k gating (P3 ``TopKGating`` training branch): the noise is added
+    to the logits, bias included, before the softmax; the normal draw eps is an
+    input. P5's fixed-scale noise is the same with Wn = None and eps scaled by
+    the caller. Token choice only (P3's ``ExpertChoiceGating`` has no noise).
   * router z-loss (P3 ``router_z_loss``) is taken on the logits the softmax sees,
     bias included, for every routing mode (it depends on the logits only); with
     no tokens it is 0. P5 prints another quantity under the same name (a mean
@@ -102,6 +106,36 @@ def gate_weights(p, idx, renormalize=True):
 def route_tc(x, Wg, b, k, renormalize=True):
     """Token-choice routing: returns (idx [T,k], w [T,k], probs [T,E], logits [T,E])."""
     s = router_logits(x, Wg, b)
+    p = softmax_rows(s)
+    idx = topk_experts(p, k)
+    w = gate_weights(p, idx, renormalize)
+    return idx, w, p, s
+
+
+def softplus(z):
+    """softplus(z) = log(1 + exp(z)), the noise scale of P3 ``TopKGating``."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return np.log1p(np.exp(z))
+
+
+def noisy_logits(x, Wg, b, Wn, eps):
+    """Router logits with training noise. P3 ``TopKGating`` (training branch):
+    s + softplus(x W_noise) * eps, eps a standard normal draw per (token,
+    expert). P5 ``MoELayer`` (training branch) adds noise_std * eps instead: that
+    is Wn = None with the scaled draw passed as eps. The draw is an input, so
+    that every implementation sees the same numbers."""
+    s = router_logits(x, Wg, b)
+    if Wn is None:
+        return s + _f64(eps)
+    return s + softplus(_f64(x) @ _f64(Wn)) * _f64(eps)
+
+
+def route_tc_noisy(x, Wg, b, Wn, eps, k, renormalize=True):
+    """Noisy top-k gating (P3 ``TopKGating`` training branch): softmax, top-k
+    and weights as in ``route_tc``, on the noisy logits. Returns (idx, w,
+    probs, logits)."""
+    s = noisy_logits(x, Wg, b, Wn, eps)
     p = softmax_rows(s)
     idx = topk_experts(p, k)
     w = gate_weights(p, idx, renormalize)

@@ -496,4 +496,62 @@ def pin_zloss_closed_forms(O):
     assert O.router_z_loss(np.zeros((0, 4))) == 0.0
 
 
+# ----------------------------------------------------------------------------
+# noisy top-k gating
+# ----------------------------------------------------------------------------
+
+def _noise_case(seed, T=6, d=5, E=4, bias=True, eps_std=1.0):
+    c = _case(seed, T=T, E=E, d=d, bias=bias, wg_std=0.8)
+    r = _rng(seed + 1000)
+    c["Wn"] = r.standard_normal((d, E)) * 0.6
+    c["eps"] = r.standard_normal((T, E)) * eps_std
+    return c
+
+
+def pin_softplus_library(O):
+    """softplus equals torch's (whose linear cut-off is moved past the range), log 2
+    at 0, and softplus(z) - softplus(-z) = z."""
+    z = np.linspace(-30.0, 30.0, 241)
+    ref = F.softplus(torch.from_numpy(z), beta=1.0, threshold=100.0).numpy()
+    assert np.allclose(O.softplus(z), ref, rtol=1e-12, atol=1e-300)
+    assert math.isclose(float(O.softplus(np.array(0.0))), math.log(2.0), rel_tol=1e-15)
+    assert np.allclose(O.softplus(z) - O.softplus(-z), z, rtol=1e-12, atol=1e-12)
+
+
+def pin_noisy_brute(O):
+    """Noisy routing and layer equal the literal-loop brute force, with the P3
+    softplus scale and with additive noise (Wn = None)."""
+    for seed, T, E, k, use_wn in [(51, 6, 4, 2, True), (52, 7, 5, 1, True), (53, 5, 4, 3, False)]:
+        c = _noise_case(seed, T=T, E=E, eps_std=2.0)
+        Wn = c["Wn"] if use_wn else None
+        ref = B.forward_tc(_lists(c["x"]), _lists(c["Wg"]), _lists(c["b"]), _lists(c["Wgate"]),
+                           _lists(c["Wup"]), _lists(c["Wdown"]), k, True, _lists(Wn),
+                           _lists(c["eps"]))
+        idx, w, p, s = O.route_tc_noisy(c["x"], c["Wg"], c["b"], Wn, c["eps"], k)
+        assert idx.tolist() == ref["idx"]
+        assert np.allclose(w, np.array(ref["w"]), rtol=1e-12, atol=1e-15)
+        assert np.allclose(p, np.array(ref["probs"]), rtol=1e-12, atol=1e-15)
+        y = O.mix(c["x"], idx, w, c["Wgate"], c["Wup"], c["Wdown"])
+        assert np.allclose(y, np.array(ref["y"]), rtol=1e-10, atol=1e-12)
+
+
+def pin_noisy_special_cases(O):
+    """eps = 0 is plain routing; W_noise = 0 scales the draw by log 2; a draw that
+    is constant over a token's experts changes none of its probabilities; a large
+    draw on one expert selects it."""
+    c = _noise_case(54, T=8, E=6)
+    plain = O.route_tc(c["x"], c["Wg"], c["b"], 2)
+    zero = O.route_tc_noisy(c["x"], c["Wg"], c["b"], c["Wn"], np.zeros((8, 6)), 2)
+    assert np.array_equal(zero[0], plain[0]) and np.allclose(zero[2], plain[2], rtol=1e-15)
+    s0 = O.noisy_logits(c["x"], c["Wg"], c["b"], np.zeros((5, 6)), c["eps"])
+    s_ref = torch.from_numpy(c["x"]) @ torch.from_numpy(c["Wg"]) + torch.from_numpy(c["b"])
+    assert np.allclose(s0, s_ref.numpy() + math.log(2.0) * c["eps"], rtol=1e-13, atol=1e-14)
+    shift = np.repeat(_rng(55).standard_normal((8, 1)) * 5.0, 6, axis=1)
+    moved = O.route_tc_noisy(c["x"], c["Wg"], c["b"], None, shift, 2)
+    assert np.allclose(moved[2], plain[2], rtol=1e-12, atol=1e-15)
+    spike = np.zeros((8, 6))
+    spike[:, 4] = 50.0
+    assert np.all(O.route_tc_noisy(c["x"], c["Wg"], c["b"], c["Wn"], spike, 1)[0][:, 0] == 4)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

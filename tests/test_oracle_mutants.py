@@ -42,6 +42,17 @@ MUTANTS = {
     "ec_score_unweighted": ("y[tt] += _f64(score[e])[:, None] * out", "y[tt] += out"),
     "margin_off_by_one": ("return ps[:, k - 1] - ps[:, k]", "return ps[:, k] - ps[:, k + 1 if k + 1 < E else k]"),
     "tc_capacity_keeps_one_more": ("if load[e] < cap:", "if load[e] <= cap:"),
+    "noise_no_softplus": ("return s + softplus(_f64(x) @ _f64(Wn)) * _f64(eps)",
+                          "return s + (_f64(x) @ _f64(Wn)) * _f64(eps)"),
+    "noise_subtracted": ("return s + softplus(_f64(x) @ _f64(Wn)) * _f64(eps)",
+                         "return s - softplus(_f64(x) @ _f64(Wn)) * _f64(eps)"),
+    "noise_from_gate_weights": ("return s + softplus(_f64(x) @ _f64(Wn)) * _f64(eps)",
+                                "return s + softplus(_f64(x) @ _f64(Wg)) * _f64(eps)"),
+    "softplus_is_exp": ("return np.log1p(np.exp(z))", "return np.exp(z)"),
+    "noise_on_probs": ("    s = noisy_logits(x, Wg, b, Wn, eps)\n    p = softmax_rows(s)",
+                       "    s = noisy_logits(x, Wg, b, Wn, eps)\n    p = softmax_rows(router_logits(x, Wg, b)) + (s - router_logits(x, Wg, b))"),
+    "additive_noise_dropped": ("    if Wn is None:\n        return s + _f64(eps)",
+                               "    if Wn is None:\n        return s"),
     "zloss_no_square": ("return float(np.mean(lse ** 2))", "return float(np.mean(lse))"),
     "zloss_no_log": ("lse = np.log(np.exp(s).sum(axis=1))", "lse = np.exp(s).sum(axis=1)"),
     "zloss_sum_not_mean": ("return float(np.mean(lse ** 2))", "return float(np.sum(lse ** 2))"),
