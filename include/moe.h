@@ -16,6 +16,9 @@
  *     compute_load_balancing_loss);
  *   - router z-loss z = mean_t (log sum_e exp(s_te))^2 over the router logits s (the
  *     Korean page's router_z_loss);
+ *   - noisy top-k gating for training: s + softplus(x W_noise) * eps before the softmax
+ *     (the Korean page's TopKGating, training branch), or s + eps (the fixed-scale noise
+ *     of "机器学习基础系列——混合专家模型", MoELayer, with eps scaled by the caller);
  *   - expert-choice routing with capacity C = floor(T * cf / E): each expert takes the
  *     C tokens of largest softmax-over-tokens score (the Korean page's
  *     ExpertChoiceGating);
@@ -95,6 +98,18 @@ typedef struct moe_shape {
                             * k), > 0 and finite; ignored in plain token choice */
 } moe_shape;
 
+/* Training noise of noisy top-k gating, token choice only (both token-choice modes).
+ *   W_noise [d_model, E] dtype, layout of W_g; or NULL for additive noise
+ *   eps     [T, E] fp32, the normal draw (one per token and expert), required
+ * The router's logits become s + softplus(x W_noise) * eps (softplus(z) = log(1 + e^z)),
+ * or s + eps without W_noise, with s = x W_g (+ b_g). Everything downstream — softmax,
+ * top-k, weights, probs, counts, f, p, loss, z_loss — sees the noisy logits. The draw is
+ * an input so that a caller controls its generator (e.g. torch.randn on the stream). */
+typedef struct moe_noise {
+  const void* W_noise;
+  const float* eps;
+} moe_noise;
+
 /* Human-readable name of a status code. Never NULL; the string is static. */
 const char* moe_status_string(int32_t status);
 
@@ -137,6 +152,8 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
  *   x      [T, d_model]   dtype
  *   W_g    [d_model, E]   dtype (the x @ W layout of MoELayer.__init__)
  *   b_g    [E] fp32 router bias added to the logits, or NULL for none
+ *   noise  training noise (moe_noise), or NULL for none; MOE_ERR_UNSUPPORTED in expert
+ *          choice, MOE_ERR_NULL_ARG without eps
  * Token choice outputs:
  *   idx    [T, k] int32   selected experts, descending probability
  *   w      [T, k] fp32    gate weights of the selected experts
@@ -158,13 +175,14 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
  * experts, so the order of slots within a token decides nothing.
  * idx and w are required when T > 0 (with T = 0 there is nothing to write). */
 moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                     int32_t* idx, float* w, float* probs, int32_t* counts, float* z_loss,
-                     void* ws, size_t ws_bytes, hipStream_t stream);
+                     const moe_noise* noise, int32_t* idx, float* w, float* probs,
+                     int32_t* counts, float* z_loss, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* Whole layer forward: router, dispatch (histogram, prefix sum, stable permutation of
  * token rows into expert-contiguous order), grouped SwiGLU gate/up GEMM, grouped down
  * GEMM, weighted combine, and (token choice) the load-balancing statistics.
- *   x, W_g, b_g   as in moe_route
+ *   x, W_g, b_g, noise   as in moe_route
  *   W_gate, W_up  [E, d_model, d_ff] dtype, expert e's matrix at offset e*d_model*d_ff
  *   W_down        [E, d_ff, d_model] dtype
  *   y             [T, d_model] fp32   y_t = sum over the token's experts of
@@ -183,7 +201,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
  * the output RMS on the 16-expert workload; the pair costs one extra down-projection
  * pass. */
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                       const void* W_gate, const void* W_up, const void* W_down, float* y,
+                       const moe_noise* noise, const void* W_gate, const void* W_up,
+                       const void* W_down, float* y,
                        int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
                        float* loss, float* z_loss, void* ws, size_t ws_bytes,
                        hipStream_t stream);

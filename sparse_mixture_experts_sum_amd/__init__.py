@@ -58,6 +58,10 @@ class MoeShape(ctypes.Structure):
     ]
 
 
+class MoeNoise(ctypes.Structure):
+    _fields_ = [("W_noise", ctypes.c_void_p), ("eps", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -78,8 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_capacity.argtypes = [S, ctypes.POINTER(I64)]
     lib.moe_workspace_size.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_workspace_offset.argtypes = [S, I32, ctypes.POINTER(ctypes.c_size_t)]
-    lib.moe_route.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    N = ctypes.POINTER(MoeNoise)
+    lib.moe_route.argtypes = [S, P, P, P, N, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward.argtypes = [S, P, P, P, N, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                ctypes.c_size_t, P]
     lib.moe_aux_loss.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_profile_enable.argtypes = [I32]
     lib.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
@@ -155,6 +161,19 @@ def _need(t, name, dtype=None, dev=None):
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
+def _noise(x, W_noise, eps, dev):
+    """moe_noise for training noise: eps [T,E] fp32 (required for any noise) and
+    optionally W_noise [d,E] of x's dtype; None when eps is None."""
+    if eps is None:
+        if W_noise is not None:
+            raise ValueError("W_noise needs eps, the normal draw")
+        return None
+    _need(eps, "eps", torch.float32, dev)
+    _need(W_noise, "W_noise", x.dtype, dev)
+    return ctypes.byref(MoeNoise(W_noise=None if W_noise is None else W_noise.data_ptr(),
+                                 eps=eps.data_ptr()))
+
+
 def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     n = workspace_size(shape)
     if workspace is not None and workspace.numel() * workspace.element_size() >= n:
@@ -163,9 +182,11 @@ def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch
 
 
 def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormalize=True,
-              want_probs=True, want_counts=True, want_z_loss=False, workspace=None) -> dict:
+              want_probs=True, want_counts=True, want_z_loss=False, W_noise=None, eps=None,
+              workspace=None) -> dict:
     """Router only. Token choice (with or without capacity) returns idx/w [T,k];
-    expert choice idx/w [E,C]. want_z_loss adds the router z-loss (fp32 [1])."""
+    expert choice idx/w [E,C]. want_z_loss adds the router z-loss (fp32 [1]); eps
+    (and W_noise) add the training noise of noisy top-k gating."""
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
@@ -185,17 +206,19 @@ def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormal
     probs = torch.empty(T, E, dtype=torch.float32, device=dev) if want_probs else None
     counts = torch.empty(E, dtype=torch.int32, device=dev) if want_counts else None
     z = torch.empty(1, dtype=torch.float32, device=dev) if want_z_loss else None
+    noise = _noise(x, W_noise, eps, dev)
     _check("moe_route", load_library().moe_route(
-        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(idx), _ptr(w), _ptr(probs),
+        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), noise, _ptr(idx), _ptr(w), _ptr(probs),
         _ptr(counts), _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
     return {"idx": idx, "w": w, "probs": probs, "counts": counts, "z_loss": z}
 
 
 def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_factor=1.0,
                 renormalize=True, want_routing=True, want_probs=True, want_stats=True,
-                want_z_loss=False, workspace=None, y=None) -> dict:
+                want_z_loss=False, W_noise=None, eps=None, workspace=None, y=None) -> dict:
     """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
-    counts, (token choice) f, p, loss, and the router z-loss."""
+    counts, (token choice) f, p, loss, and the router z-loss. eps (and W_noise) add
+    the training noise of noisy top-k gating."""
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
@@ -229,8 +252,10 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
         po = torch.empty(E, dtype=torch.float32, device=dev)
         lo = torch.empty(1, dtype=torch.float32, device=dev)
     z = torch.empty(1, dtype=torch.float32, device=dev) if want_z_loss else None
+    noise = _noise(x, W_noise, eps, dev)
     _check("moe_forward", load_library().moe_forward(
-        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), noise, _ptr(W_gate), _ptr(W_up),
+        _ptr(W_down),
         _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo), _ptr(po), _ptr(lo),
         _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
     return {"y": y, "idx": idx, "w": w, "probs": probs, "counts": counts, "f": fo, "p": po,

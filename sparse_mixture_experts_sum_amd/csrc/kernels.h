@@ -9,6 +9,10 @@ struct RouterArgs {
   const void* x;        // [T, d] dtype
   const void* Wg;       // [d, E] dtype
   const float* bias;    // [E] or nullptr
+  // token choice, optional training noise: logits + softplus(x Wn) * eps, or + eps
+  // when Wn is nullptr; none when eps is nullptr
+  const void* Wn;       // [d, E] dtype or nullptr
+  const float* eps;     // [T, E] or nullptr
   int T, d, E, k, renorm;
   // token choice outputs
   int32_t* idx;         // [T, k]

@@ -118,6 +118,15 @@ Layout make_layout(const moe_shape& s) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Training noise: token choice only; the draw is required, W_noise optional.
+moe_status check_noise(const moe_shape& s, const moe_noise* noise) {
+  if (!noise) return MOE_OK;
+  if (!is_tc(s.mode)) return MOE_ERR_UNSUPPORTED;
+  if (s.T > 0 && !noise->eps) return MOE_ERR_NULL_ARG;
+  if (!aligned16(noise->W_noise) || !aligned16(noise->eps)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
 // ---- stage timing ----------------------------------------------------------------
 struct ProfRec {
   int stage;
@@ -192,13 +201,16 @@ moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, f
 // dispatch tables; expert choice writes idx/score and the group offsets. With want_z the
 // router also leaves the per-block z-loss partials in the workspace.
 moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
-                      const float* b_g, int32_t* idx, float* w, float* probs,
-                      int32_t* user_counts, bool want_z, void* ws, hipStream_t stream) {
+                      const float* b_g, const moe_noise* noise, int32_t* idx, float* w,
+                      float* probs, int32_t* user_counts, bool want_z, void* ws,
+                      hipStream_t stream) {
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
   a.x = x;
   a.Wg = W_g;
   a.bias = b_g;
+  a.Wn = noise ? noise->W_noise : nullptr;
+  a.eps = noise ? noise->eps : nullptr;
   a.T = (int)s.T;
   a.d = (int)s.d_model;
   a.E = s.E;
@@ -282,17 +294,20 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
 }
 
 moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                     int32_t* idx, float* w, float* probs, int32_t* counts, float* z_loss,
-                     void* ws, size_t ws_bytes, hipStream_t stream) {
+                     const moe_noise* noise, int32_t* idx, float* w, float* probs,
+                     int32_t* counts, float* z_loss, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
+  st = check_noise(s, noise);
+  if (st != MOE_OK) return st;
   if (s.T > 0 && (!idx || !w || !x || !W_g || !ws)) return MOE_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_g) || !aligned16(ws)) return MOE_ERR_MISALIGNED;
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, z_loss, stream);
-  st = run_router(s, L, x, W_g, b_g, idx, w, probs, counts, z_loss != nullptr, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, noise, idx, w, probs, counts, z_loss != nullptr, ws, stream);
   if (st != MOE_OK) return st;
   if (z_loss)
     MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, (int)s.T, 0, s.k, nullptr,
@@ -310,7 +325,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                       const void* W_gate, const void* W_up, const void* W_down, float* y,
+                       const moe_noise* noise, const void* W_gate, const void* W_up,
+                       const void* W_down, float* y,
                        int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
                        float* loss, float* z_loss, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
@@ -318,6 +334,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   if (s.mode == MOE_EXPERT_CHOICE && (f || p || loss)) return MOE_ERR_UNSUPPORTED;
+  st = check_noise(s, noise);
+  if (st != MOE_OK) return st;
   if (s.T > 0 && (!x || !W_g || !W_gate || !W_up || !W_down || !y || !ws)) return MOE_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_g) || !aligned16(W_gate) || !aligned16(W_up) ||
       !aligned16(W_down) || !aligned16(y) || !aligned16(ws))
@@ -335,7 +353,8 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
   void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
-  st = run_router(s, L, x, W_g, b_g, idx_b, w_b, probs, counts, z_loss != nullptr, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss != nullptr, ws,
+                  stream);
   if (st != MOE_OK) return st;
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_PERMUTE,

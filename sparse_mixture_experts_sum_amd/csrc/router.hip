@@ -13,6 +13,12 @@
 //
 // Expert choice (the Korean page's ExpertChoiceGating): the same GEMM writes the
 // logits transposed, [E, T]; a second kernel takes one expert per workgroup.
+//
+// Noisy top-k gating (the Korean page's TopKGating, training branch): the noise
+// projection x W_noise runs as E more MFMA columns over the same x fragments (W_noise
+// staged beside W_g), and each logit becomes s + softplus(x W_noise) * eps before the
+// softmax; eps, the normal draw, is an input. Without W_noise the draw is added as is
+// (the fixed-scale noise of 机器学习基础系列——混合专家模型, MoELayer).
 #include <float.h>
 #include <limits.h>
 
@@ -114,18 +120,27 @@ __device__ __forceinline__ void stage_wg_transposed(const TI* __restrict__ src, 
   }
 }
 
-template <typename TI, int EP>
+// softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that e^z never overflows
+__device__ __forceinline__ float softplus_f(float z) {
+  return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
+}
+
+// NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added
+template <typename TI, int EP, int NOISE>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   using M = RouterMma<TI>;
   constexpr int VEC = M::VEC;
   constexpr int ITK = 16 * VEC;                                  // k per iteration
-  constexpr int KC = kRouterWgBytes / (EP * (int)sizeof(TI));    // k per LDS stage of W_g
+  constexpr int NG = EP / 16;                                    // 16-column blocks of W_g
+  constexpr int NB = NOISE == 2 ? 2 * NG : NG;                   // plus those of W_noise
+  constexpr int KC = kRouterWgBytes / (NB * 16 * (int)sizeof(TI));  // k per LDS stage
   constexpr int LDW = KC + 16 / (int)sizeof(TI);                 // padded row (16 bytes)
   constexpr int LSP = EP + 1;
   constexpr int PF = kRouterPF;
   static_assert(KC % ITK == 0, "stage must hold whole iterations");
 
-  __shared__ __attribute__((aligned(16))) TI Wl[EP * LDW];
+  // rows [0, EP): W_g transposed; rows [EP, 2 EP): W_noise transposed (NOISE == 2)
+  __shared__ __attribute__((aligned(16))) TI Wl[NB * 16 * LDW];
   __shared__ float Ls[kRT * LSP];
   __shared__ float red[256];
   __shared__ float zred[4];
@@ -141,12 +156,26 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   const int trow = t0 + wave * 16 + (lane & 15);
   const TI* xrow = x + (size_t)min(trow, T - 1) * d;
 
-  f32x4 acc[EP / 16];
+  f32x4 acc[NB];
 #pragma unroll
-  for (int nb = 0; nb < EP / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the bias is loaded now and stored to LDS after the logits pass, so that its load
   // latency hides behind that pass
   const float bias_r = (a.bias && tid < E) ? a.bias[tid] : 0.f;
+  // so is the noise draw of this lane's logits: token wave*16 + 4g + r, expert
+  // nb*16 + lane%16 (the accumulator layout below)
+  float epsv[NOISE ? NG : 1][4];
+  if constexpr (NOISE != 0) {
+#pragma unroll
+    for (int nb = 0; nb < NG; ++nb) {
+      const int e = nb * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wave * 16 + 4 * g + r;
+        epsv[nb][r] = (t < T && e < E) ? a.eps[(size_t)t * E + e] : 0.f;
+      }
+    }
+  }
 
   // W_g is staged transposed in LDS (one slice of up to KC rows of k at a time; at most
   // a few slices: d / KC); x is streamed from HBM into registers, PF iterations ahead.
@@ -164,6 +193,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     for (int p = 0; p < PF - 1; ++p) router_load_x<VEC>(xs, p, kn, g, av[p]);
     lds_barrier();  // the previous slice's fragment reads are done
     stage_wg_transposed<TI>(Wg + (size_t)kc * E, kn, E, LDW, Wl, tid);
+    if constexpr (NOISE == 2)
+      stage_wg_transposed<TI>(static_cast<const TI*>(a.Wn) + (size_t)kc * E, kn, E, LDW,
+                              Wl + EP * LDW, tid);
     lds_barrier();  // the slice is in LDS
     for (int it0 = 0; it0 < nit; it0 += PF) {
 #pragma unroll
@@ -174,8 +206,10 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
         for (int u = 0; u < 4; ++u) {
           const int kx = it * ITK + (4 * u + g) * VEC;
 #pragma unroll
-          for (int nb = 0; nb < EP / 16; ++nb) {
-            const u32x4 bv = ld16(&Wl[min(nb * 16 + (lane & 15), E - 1) * LDW + min(kx, kn - VEC)]);
+          for (int nb = 0; nb < NB; ++nb) {
+            // W_noise blocks (nb >= NG) sit EP rows further down
+            const int row = (nb >= NG ? EP : 0) + min((nb % NG) * 16 + (lane & 15), E - 1);
+            const u32x4 bv = ld16(&Wl[row * LDW + min(kx, kn - VEC)]);
             M::step(acc[nb], av[j][u], bv);
           }
         }
@@ -201,10 +235,19 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     if (!a.blk_zsum) return;  // else on to the per-token log-partition below
   }
 
+  // logits with the bias (and the training noise) into LDS; padding experts (>= E) have
+  // bias 0 and are never read
 #pragma unroll
-  for (int nb = 0; nb < EP / 16; ++nb)
+  for (int nb = 0; nb < NG; ++nb) {
+    const float bz = bias_s[nb * 16 + (lane & 15)];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Ls[(wave * 16 + 4 * g + r) * LSP + nb * 16 + (lane & 15)] = acc[nb][r];
+    for (int r = 0; r < 4; ++r) {
+      float v = acc[nb][r] + bz;
+      if constexpr (NOISE == 1) v += epsv[nb][r];
+      if constexpr (NOISE == 2) v += softplus_f(acc[NG + nb][r]) * epsv[nb][r];
+      Ls[(wave * 16 + 4 * g + r) * LSP + nb * 16 + (lane & 15)] = v;
+    }
+  }
   if (tid < 64) running[tid] = 0;
   __syncthreads();
 
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     const int e = part + 4 * i;
     lv[i] = -FLT_MAX;
     if (e < E) {
-      lv[i] = Ls[tok * LSP + e] + bias_s[e];
+      lv[i] = Ls[tok * LSP + e];
       lmax = fmaxf(lmax, lv[i]);
     }
   }
@@ -449,16 +492,27 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
 hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s) {
   const int nblk = (a.T + kRT - 1) / kRT;
   const int ep = a.E <= 16 ? 16 : (a.E <= 32 ? 32 : 64);
+  const int noise = a.eps ? (a.Wn ? 2 : 1) : 0;
+  if (noise && ec) return hipErrorInvalidValue;  // noise is a token-choice feature
   dim3 grid(nblk), block(256);
+#define MOE_ROUTER(TI, EP, NOISE) router_kernel<TI, EP, NOISE><<<grid, block, 0, s>>>(a, ec)
+#define MOE_ROUTER_EP(TI, NOISE)                        \
+  do {                                                  \
+    if (ep == 16) MOE_ROUTER(TI, 16, NOISE);            \
+    else if (ep == 32) MOE_ROUTER(TI, 32, NOISE);       \
+    else MOE_ROUTER(TI, 64, NOISE);                     \
+  } while (0)
   if (bf16in) {
-    if (ep == 16) router_kernel<bf16, 16><<<grid, block, 0, s>>>(a, ec);
-    else if (ep == 32) router_kernel<bf16, 32><<<grid, block, 0, s>>>(a, ec);
-    else router_kernel<bf16, 64><<<grid, block, 0, s>>>(a, ec);
+    if (noise == 0) MOE_ROUTER_EP(bf16, 0);
+    else if (noise == 1) MOE_ROUTER_EP(bf16, 1);
+    else MOE_ROUTER_EP(bf16, 2);
   } else {
-    if (ep == 16) router_kernel<float, 16><<<grid, block, 0, s>>>(a, ec);
-    else if (ep == 32) router_kernel<float, 32><<<grid, block, 0, s>>>(a, ec);
-    else router_kernel<float, 64><<<grid, block, 0, s>>>(a, ec);
+    if (noise == 0) MOE_ROUTER_EP(float, 0);
+    else if (noise == 1) MOE_ROUTER_EP(float, 1);
+    else MOE_ROUTER_EP(float, 2);
   }
+#undef MOE_ROUTER_EP
+#undef MOE_ROUTER
   return hipGetLastError();
 }
 

@@ -131,7 +131,8 @@ def test_forward_argument_errors_before_any_hip_call(M):
     def call(shape=s, ws=good, ws_bytes=n, **over):
         a = dict(args)
         a.update(over)
-        return lib.moe_forward(ctypes.byref(shape), a["x"], a["Wg"], a["b"], a["Wgate"], a["Wup"],
+        return lib.moe_forward(ctypes.byref(shape), a["x"], a["Wg"], a["b"], a.get("noise"),
+                               a["Wgate"], a["Wup"],
                                a["Wdown"], a["y"], None, None, None, None, None, None, None, None,
                                ws, ws_bytes, None)
 
@@ -140,13 +141,21 @@ def test_forward_argument_errors_before_any_hip_call(M):
     assert call(ws=None) == 1
     assert call(y=P(4100)) == 5                      # misaligned
     assert call(ws_bytes=n - 1) == 4                 # workspace too small
-    assert lib.moe_forward(None, *([None] * 16), 0, None) == 1
+    assert lib.moe_forward(None, *([None] * 17), 0, None) == 1
     ec = M.make_shape(64, 128, 256, 8, mode="ec")
     f = P(8192)
-    assert lib.moe_forward(ctypes.byref(ec), good, good, None, good, good, good, good, None, None,
-                           None, None, f, None, None, None, good, n, None) == 3
-    assert lib.moe_route(ctypes.byref(s), good, good, None, None, good, None, None, None, good, n,
-                         None) == 1
+    assert lib.moe_forward(ctypes.byref(ec), good, good, None, None, good, good, good, good, None,
+                           None, None, None, f, None, None, None, good, n, None) == 3
+    assert lib.moe_route(ctypes.byref(s), good, good, None, None, None, good, None, None, None, good,
+                         n, None) == 1
+    # training noise: expert choice refuses it, a missing draw is a null argument, and a
+    # misaligned projection is caught
+    ecn = M.make_shape(64, 128, 256, 8, mode="ec", capacity_factor=1.0)
+    nz = M.MoeNoise(W_noise=None, eps=8192)
+    assert lib.moe_route(ctypes.byref(ecn), good, good, None, ctypes.byref(nz), good, good, None,
+                         None, None, good, n * 4, None) == 3
+    assert call(noise=ctypes.byref(M.MoeNoise(W_noise=8192, eps=None))) == 1
+    assert call(noise=ctypes.byref(M.MoeNoise(W_noise=8196, eps=8192))) == 5
     assert lib.moe_aux_loss(ctypes.byref(ec), good, good, good, good, good, None, good, n, None) == 3
     assert lib.moe_aux_loss(ctypes.byref(s), good, good, None, good, good, None, good, n, None) == 1
 

@@ -1,0 +1,169 @@
+"""GPU parity of noisy top-k gating (the Korean page's TopKGating, training branch:
+logits + softplus(x W_noise) * eps; additive eps for the fixed-scale form) against
+the fp64 oracle, through the C ABI. The normal draw eps is an input that both sides
+read; routing follows the near-tie rules of the plain token-choice tests.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_oracle as O
+from tests import parity as PR
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_mixture_experts_sum_amd as M
+    M.load_library()
+    return M
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def _dev_noise(nz, w):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return (PR.to_dev(nz["Wn"], dt) if nz["Wn"] is not None else None,
+            PR.to_dev(nz["eps"], torch.float32))
+
+
+def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0):
+    _say(w, "noise", "softplus" if nz["Wn"] is not None else "additive", mode)
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    Wn, eps = _dev_noise(nz, w)
+    out = M.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        k=w.k, mode=mode, capacity_factor=cf, renormalize=w.renormalize,
+                        want_z_loss=True, W_noise=Wn, eps=eps)
+    torch.cuda.synchronize()
+    idx, wd, probs, counts = (_np(out[n]) for n in ("idx", "w", "probs", "counts"))
+    idx_ref, w_ref, p_ref, s_ref = O.route_tc_noisy(inp["x"], inp["Wg"], inp["b"], nz["Wn"],
+                                                    nz["eps"], w.k, w.renormalize)
+    np.testing.assert_allclose(probs, p_ref, rtol=0, atol=1e-5 if w.dtype == "bf16" else 1e-6)
+    capacity = mode == "tc_capacity"
+    exempt = PR.check_tc_routing(idx, None if capacity else wd, p_ref, w.k, w.renormalize)
+    PR.check_counts(counts, idx, idx_ref, exempt, w.E)
+    idx64 = idx.astype(np.int64)
+    if capacity:
+        kept, _ = O.capacity_keep(idx64, w.E, O.tc_capacity(w.T, w.E, w.k, cf))
+        w_use = O.capacity_weights(p_ref, idx64, kept, w.renormalize)
+        assert np.max(np.abs(wd - w_use)) <= 1e-5
+    else:
+        w_use = O.gate_weights(p_ref, idx64, w.renormalize)
+    toks = np.arange(w.T)
+    if sample is not None and sample < w.T:
+        toks = np.sort(np.random.default_rng(7).choice(w.T, size=sample, replace=False))
+    y_ref = O.mix(inp["x"][toks], idx64[toks], w_use[toks], inp["Wgate"], inp["Wup"], inp["Wdown"])
+    err = PR.check_y(_np(out["y"])[toks], y_ref, w.dtype)
+    f_ref, pm_ref, loss_ref, _ = O.aux_stats(p_ref, idx64, w.E, w.k)
+    np.testing.assert_allclose(_np(out["f"]), f_ref, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(_np(out["p"]), pm_ref, rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(_np(out["loss"])[0], loss_ref, rtol=1e-5)
+    z_ref = O.router_z_loss(s_ref)
+    assert abs(float(_np(out["z_loss"])[0]) - z_ref) <= 1e-5 * abs(z_ref)
+    # the noise must have moved some routing, or the case tests nothing
+    plain = O.topk_experts(O.softmax_rows(O.router_logits(inp["x"], inp["Wg"], inp["b"])), w.k)
+    moved = int(np.sum(np.any(np.sort(plain, 1) != np.sort(idx_ref, 1), axis=1)))
+    assert moved > 0
+    _say(f"  ok: y err {err:.3e}, tokens rerouted by the noise {moved}, exempt {int(exempt.sum())}")
+    return out, inp, dev
+
+
+def test_noisy_mid_bf16(moe):
+    w = W.CONFIGS[2]
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05))
+
+
+def test_noisy_fine_grained_e64_top4(moe):
+    w = W.custom("noisy_e64_top4", T=2048, d=512, f=256, E=64, k=4, seed=(42, 301))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05))
+
+
+def test_additive_noise_fp32_ragged(moe):
+    # the fixed-scale form: logits + noise_std * eps, noise_std = 0.1
+    w = W.custom("additive_fp32", dtype="fp32", T=1000, d=128, f=64, E=8, k=2, x_std=0.5,
+                 wg_std=0.1, renormalize=False, seed=(42, 302))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=None, eps_scale=0.1))
+
+
+@pytest.mark.parametrize("T", [1, 65])
+def test_noisy_small_fp32(moe, T):
+    w = W.custom(f"noisy_fp32_{T}", dtype="fp32", T=T, d=64, f=64, E=16, k=2, x_std=1.0,
+                 wg_std=0.3, seed=(42, 303 + T))
+    nz = W.make_noise(w, wn_std=0.3, eps_scale=3.0)
+    if T == 1:  # one token: a large draw on an unselected expert with a large noise
+        # scale softplus(x W_noise) moves it
+        inp = W.make_inputs(w, experts=False)
+        top = O.topk_experts(O.softmax_rows(O.router_logits(inp["x"], inp["Wg"], inp["b"])), 2)
+        scale = (inp["x"].astype(np.float64) @ nz["Wn"].astype(np.float64))[0]
+        scale[top[0]] = -np.inf
+        nz["eps"][0, :] = 0.0
+        nz["eps"][0, int(np.argmax(scale))] = 40.0
+    run_noisy_case(moe, w, nz)
+
+
+def test_noisy_with_capacity(moe):
+    w = W.custom("noisy_capacity", T=1024, d=256, f=128, E=8, k=2, bias_std=0.5, seed=(42, 305))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05), mode="tc_capacity", cf=0.75)
+
+
+def test_noisy_mixtral_layer_sampled(moe):
+    w = W.CONFIGS[3]
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02), sample=32)
+
+
+def test_zero_draw_is_bitwise_plain_routing(moe):
+    # eps = 0: softplus(x W_noise) * 0 adds exactly 0, so every output equals the
+    # noiseless call bit for bit (the noise variant also stages its LDS slices
+    # differently; the MFMA accumulation order over k is the same)
+    w = W.custom("zero_draw", T=777, d=512, f=128, E=16, k=2, bias_std=0.5, seed=(42, 306))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    nz = W.make_noise(w, wn_std=0.05)
+    nz["eps"][:] = 0.0
+    Wn, eps = _dev_noise(nz, w)
+    _say(w, "zero draw")
+    a = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        k=2, want_z_loss=True, W_noise=Wn, eps=eps)
+    b = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        k=2, want_z_loss=True)
+    torch.cuda.synchronize()
+    for n in ("y", "idx", "w", "probs", "counts", "f", "p", "loss", "z_loss"):
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_route_only_matches_forward(moe):
+    w = W.custom("noisy_route", T=500, d=256, f=128, E=8, k=2, seed=(42, 307))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    Wn, eps = _dev_noise(W.make_noise(w, wn_std=0.05), w)
+    _say(w, "route vs forward")
+    r = moe.moe_route(dev["x"], dev["Wg"], dev["b"], k=2, want_z_loss=True, W_noise=Wn, eps=eps)
+    f = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                        k=2, want_z_loss=True, W_noise=Wn, eps=eps)
+    torch.cuda.synchronize()
+    for n in ("idx", "w", "probs", "counts", "z_loss"):
+        assert torch.equal(r[n], f[n]), n
+
+
+def test_expert_choice_refuses_noise(moe):
+    w = W.custom("noisy_ec", T=256, d=64, f=64, E=4, k=1, mode="ec", seed=(42, 308))
+    inp = W.make_inputs(w, experts=False)
+    dev = PR.device_inputs(inp, w)
+    _, eps = _dev_noise(W.make_noise(w, wn_std=None), w)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route(dev["x"], dev["Wg"], None, mode="ec", eps=eps)
+    assert ei.value.status == 3

@@ -134,5 +134,18 @@ def make_inputs(w: Workload, experts: bool = True) -> dict:
         return {k: f.result() for k, f in futs.items()}
 
 
+def make_noise(w: Workload, wn_std: Optional[float] = 0.02, eps_scale: float = 1.0) -> dict:
+    """Training-noise inputs of a workload: ``Wn [d,E]`` (the noise projection, drawn
+    like W_g and rounded like it; None when ``wn_std`` is None) and ``eps [T,E]``, a
+    standard normal draw times ``eps_scale`` (float32). Streams: the workload's seed
+    with a trailing 1, spawned into two (Wn, eps), so the layer's own inputs are the
+    same with or without noise."""
+    kids = np.random.SeedSequence(list(w.seed) + [1]).spawn(2)
+    r_wn, r_eps = (np.random.default_rng(k) for k in kids)
+    Wn = _draw(r_wn, (w.d, w.E), wn_std, w.dtype == "bf16") if wn_std is not None else None
+    eps = r_eps.standard_normal((w.T, w.E), dtype=np.float32) * np.float32(eps_scale)
+    return {"Wn": Wn, "eps": eps}
+
+
 def with_seed(w: Workload, seed) -> Workload:
     return replace(w, seed=tuple(seed))
