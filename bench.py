@@ -6,8 +6,12 @@ tokens already resident in HBM. Default workload: the Mixtral 8x7B layer shape
 (T=16384 tokens, d_model=4096, d_ff=14336, E=8, top-2, bf16, router bias
 N(0,1) per expert giving a skewed load).
 
-Prints one JSON line (rank 0). Per-kernel durations come from HIP events the
-library records around each launch on the stream it launches on.
+Prints one JSON line (rank 0). The timed steps run with no per-stage events; the
+per-kernel durations come from a second pass of the same steps in which the library
+records HIP events around each launch on the stream it launches on.
+
+Options select the other workloads (--config) and the token-choice variants at a
+workload's shape (--variant capacity | noisy | zloss).
 """
 from __future__ import annotations
 
@@ -29,19 +33,32 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def stage_work(w):
+def stage_work(w, R=None, noisy=False):
     """Algorithmic work per stage for one layer call: FLOP for the GEMMs, bytes for the
-    streaming stages (minimum each stage must move)."""
+    streaming stages (minimum each stage must move). R: rows the GEMMs run (the kept
+    rows under an expert capacity); noisy: the router also reads W_noise and the draw."""
     s = 2 if w.dtype == "bf16" else 4
-    T, d, f, E, R = w.T, w.d, w.f, w.E, w.rows
-    kk = w.k if w.mode == "tc" else 1
-    return {
+    T, d, f, E = w.T, w.d, w.f, w.E
+    R = w.rows if R is None else R
+    work = {
         "gemm_gate_up": ("flop", 4.0 * d * f * R),
         "gemm_down": ("flop", 2.0 * f * d * R),
-        "router": ("bytes", T * d * s + d * E * s + T * kk * 8 + T * E * 4),
-        "permute": ("bytes", T * d * s + R * d * s + R * 4 + T * kk * 4),
-        "combine": ("bytes", R * d * 4 + T * kk * 8 + T * d * 4),
     }
+    if w.mode == "ec":
+        # logits written once [E, T]; each chosen row gathered and written; o, the
+        # choice lists and y for the combine
+        work["router"] = ("bytes", T * d * s + d * E * s + T * E * 4)
+        work["permute"] = ("bytes", 2 * R * d * s + R * 4)
+        work["combine"] = ("bytes", R * d * 4 + R * 8 + T * d * 4)
+        return work
+    k = w.k
+    router = T * d * s + d * E * s + T * k * 8 + T * E * 4
+    if noisy:
+        router += d * E * s + T * E * 4
+    work["router"] = ("bytes", router)
+    work["permute"] = ("bytes", T * d * s + R * d * s + R * 4 + T * k * 4)
+    work["combine"] = ("bytes", R * d * 4 + T * k * 8 + T * d * 4)
+    return work
 
 
 def gemm_traffic_from_profile():
@@ -98,6 +115,10 @@ def main():
     ap.add_argument("--config", type=int, default=3, help="workload id (1-5); default 3")
     ap.add_argument("--cpu-sample", type=int, default=16384,
                     help="tokens the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--variant", default="plain", choices=("plain", "capacity", "noisy", "zloss"),
+                    help="token-choice variant: an expert capacity (--cf), training noise "
+                         "softplus(x W_noise) * eps, or the router z-loss as an extra output")
+    ap.add_argument("--cf", type=float, default=1.0, help="capacity factor of --variant capacity")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
@@ -126,10 +147,24 @@ def main():
     y = torch.empty(w.T, w.d, dtype=torch.float32, device=dev)
     kw = dict(k=w.k, mode=w.mode, capacity_factor=w.cf, renormalize=w.renormalize,
               want_stats=(w.mode == "tc"))
+    if args.variant != "plain" and w.mode != "tc":
+        print("bench.py: --variant applies to token-choice workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.variant == "capacity":
+        kw.update(mode="tc_capacity", capacity_factor=args.cf)
+    elif args.variant == "noisy":
+        nz = W.make_noise(w, wn_std=0.02)
+        kw.update(W_noise=to_dev(nz["Wn"]), eps=to_dev(nz["eps"], torch.float32))
+    elif args.variant == "zloss":
+        kw.update(want_z_loss=True)
     out = M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, **kw)
     ws = out["workspace"]
     torch.cuda.synchronize()
     counts = out["counts"].cpu().numpy()
+    R_run = None
+    if args.variant == "capacity":
+        C = M.capacity(out["shape"])
+        R_run = int(np.minimum(counts, C).sum())
 
     if args.copy_calibration:
         # a plain streaming kernel of known traffic (reads and writes 256 MiB each) so that
@@ -143,8 +178,8 @@ def main():
     for _ in range(args.warmup):
         M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
     torch.cuda.synchronize()
-    M.profile_enable(True)
-    M.profile_read()  # clear
+    # the timed steps run without per-stage events; a second pass of the same steps
+    # records HIP events around every kernel launch for the per-stage figures
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -152,13 +187,18 @@ def main():
         M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
     stop.record()
     torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    M.profile_enable(True)
+    M.profile_read()  # clear
+    for _ in range(args.steps):
+        M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
+    torch.cuda.synchronize()
     M.profile_enable(False)
     stages = M.profile_read()
-    ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     tokens_s = w.T / (ms_step * 1e-3)
 
-    work = stage_work(w)
+    work = stage_work(w, R_run, noisy=args.variant == "noisy")
     peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     st_out = {}
     for name, (tot, n) in stages.items():
@@ -184,7 +224,7 @@ def main():
     gu_tf = work["gemm_gate_up"][1] / (gu_ms * 1e-3) / 1e12
 
     cpu = None
-    if args.cpu_sample > 0:
+    if args.cpu_sample > 0 and args.variant == "plain":
         cpu = cpu_baseline(w, inp, args.cpu_sample)
 
     line = {
@@ -209,10 +249,15 @@ def main():
         "expert_gemm_frac_of_peak": round(gemm_tf / peak_tf, 4),
         "roofline": {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(gu_tf, 1),
                      "peak": peak_tf, "unit": "TFLOP/s", "frac": round(gu_tf / peak_tf, 4),
-                     "traffic": gemm_traffic_from_profile() if args.config == 3 else None},
+                     "traffic": (gemm_traffic_from_profile()
+                                 if args.config == 3 and args.variant == "plain" else None)},
         "stages": st_out,
         "cpu_baseline": cpu,
     }
+    if args.variant != "plain":
+        line["config"]["variant"] = args.variant
+        if args.variant == "capacity":
+            line["config"].update(capacity_factor=args.cf, capacity=C, rows_kept=R_run)
     print(json.dumps(line), flush=True)
 
 

@@ -385,61 +385,97 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 //   radix select (4 x 8 bits, most significant first) of the C-th largest logit key,
 //   then a stable compaction in token order: every key above the threshold plus the
 //   first (C - above) keys equal to it.
+// The column is read from HBM once, into LDS (INLDS, T <= kEcLdsTokens); every pass
+// after that reads LDS. Each wave counts digits into its own histogram (the logits of
+// one expert share their leading key bits, so one shared histogram would take
+// thousands of same-address atomics), and wave 0 finds the digit holding the C-th key
+// with a prefix sum across its lanes.
 // ---------------------------------------------------------------------------------
 constexpr int kEcThreads = 1024;
+constexpr int kEcWaves = kEcThreads / 64;
+constexpr int kEcLdsTokens = 32768;
 
+template <bool INLDS>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __restrict__ logitsT,
                                                                int T, int E, int C, int32_t* idx,
                                                                float* score, float* probs,
                                                                int32_t* offsets, int32_t* counts) {
-  __shared__ float redf[kEcThreads / 64];
-  __shared__ int hist[256];
+  __shared__ float colsh[INLDS ? kEcLdsTokens : 1];
+  __shared__ int whist[kEcWaves][256];
+  __shared__ float redf[kEcWaves];
   __shared__ int scan_sh[17];
   __shared__ int sel_digit, sel_need;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float* col = logitsT + (size_t)e * T;
+  if constexpr (INLDS) {
+    for (int t = tid; t < T; t += kEcThreads) colsh[t] = col[t];
+    __syncthreads();
+  }
+  auto logit = [&](int t) -> float {
+    if constexpr (INLDS) return colsh[t];
+    else return col[t];
+  };
 
   // contiguous token range of this thread
   const int per = (T + kEcThreads - 1) / kEcThreads;
   const int tb = min(T, tid * per), te = min(T, tb + per);
 
   float m = -FLT_MAX;
-  for (int t = tb; t < te; ++t) m = fmaxf(m, col[t]);
+  for (int t = tb; t < te; ++t) m = fmaxf(m, logit(t));
   m = warp_max(m);
   if (lane == 0) redf[wid] = m;
   __syncthreads();
   m = redf[0];
-  for (int i = 1; i < kEcThreads / 64; ++i) m = fmaxf(m, redf[i]);
+  for (int i = 1; i < kEcWaves; ++i) m = fmaxf(m, redf[i]);
   __syncthreads();
   float s = 0.f;
-  for (int t = tb; t < te; ++t) s += expf(col[t] - m);
+  for (int t = tb; t < te; ++t) s += expf(logit(t) - m);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
   if (lane == 0) redf[wid] = s;
   __syncthreads();
   float sum = 0.f;
-  for (int i = 0; i < kEcThreads / 64; ++i) sum += redf[i];
+  for (int i = 0; i < kEcWaves; ++i) sum += redf[i];
 
   // radix select of the C-th largest key
   uint32_t prefix = 0, mask = 0;
   int need = C;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kEcThreads) hist[i] = 0;
-    __syncthreads();
+    for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
+    __builtin_amdgcn_wave_barrier();
     for (int t = tb; t < te; ++t) {
-      const uint32_t key = float_key(col[t]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      const uint32_t key = float_key(logit(t));
+      if ((key & mask) == prefix) atomicAdd(&whist[wid][(key >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, b = 255;
-      for (; b > 0; --b) {
-        if (cum + hist[b] >= need) break;
-        cum += hist[b];
+    if (wid == 0) {
+      // lane l owns digits 255 - 4l .. 252 - 4l (descending), summed over the waves
+      int c[4], cl = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int dg = 255 - 4 * lane - j;
+        int v = 0;
+        for (int w = 0; w < kEcWaves; ++w) v += whist[w][dg];
+        c[j] = v;
+        cl += v;
       }
-      sel_digit = b;
-      sel_need = need - cum;
+      int incl = cl;  // keys in digits above and at this lane's (inclusive scan)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+      }
+      const int excl = incl - cl;
+      if (excl < need && need <= incl) {  // exactly one lane: the C-th key is here
+        int cum = excl, j = 0;
+        for (; j < 3; ++j) {
+          if (cum + c[j] >= need) break;
+          cum += c[j];
+        }
+        sel_digit = 255 - 4 * lane - j;
+        sel_need = need - cum;
+      }
     }
     __syncthreads();
     prefix |= (uint32_t)sel_digit << shift;
@@ -450,14 +486,14 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   const uint32_t thr = prefix;  // key of the C-th largest logit
   // `need` = how many keys equal to thr are taken (lowest token indices first)
   int neq = 0;
-  for (int t = tb; t < te; ++t) neq += float_key(col[t]) == thr;
+  for (int t = tb; t < te; ++t) neq += float_key(logit(t)) == thr;
   int tot;
   int eq_base = block_exclusive_scan(neq, scan_sh, &tot);
   int ntake = 0;
   {
     int eqr = eq_base;
     for (int t = tb; t < te; ++t) {
-      const uint32_t key = float_key(col[t]);
+      const uint32_t key = float_key(logit(t));
       if (key > thr) ++ntake;
       else if (key == thr) ntake += (eqr++ < need);
     }
@@ -466,7 +502,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   {
     int eqr = eq_base;
     for (int t = tb; t < te; ++t) {
-      const float l = col[t];
+      const float l = logit(t);
       const uint32_t key = float_key(l);
       bool take = false;
       if (key > thr) take = true;
@@ -518,6 +554,11 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, hipStream_t s) {
-  ec_select_kernel<<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets, counts);
+  if (T <= kEcLdsTokens)
+    ec_select_kernel<true><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                    counts);
+  else
+    ec_select_kernel<false><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                     counts);
   return hipGetLastError();
 }
