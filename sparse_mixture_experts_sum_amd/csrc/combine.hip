@@ -39,17 +39,42 @@ __global__ __launch_bounds__(256) void combine_tc_kernel(const float* __restrict
   }
   const int nch = d / 4;
   float* yr = y + (size_t)t * d;
-  for (int c = lane; c < nch; c += 64) {
+  // four 16-byte chunks per lane and slot in flight at once; o is read and y written
+  // once, so both bypass the caches' retention (non-temporal), which leaves the
+  // last-level cache to the data the next kernels reuse
+  int c = lane;
+  for (; c + 192 < nch; c += 256) {
+    f32x4 v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[u][j] = (j < k && prow[j] >= 0)
+                      ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
+                            o + (size_t)prow[j] * d + 4 * (c + 64 * u)))
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) acc += pw[j] * v[u][j];
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * (c + 64 * u)));
+    }
+  }
+  for (; c < nch; c += 64) {
     f32x4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      v[j] = (j < k && prow[j] >= 0) ? *reinterpret_cast<const f32x4*>(o + (size_t)prow[j] * d + 4 * c)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[j] = (j < k && prow[j] >= 0)
+                 ? __builtin_nontemporal_load(
+                       reinterpret_cast<const f32x4*>(o + (size_t)prow[j] * d + 4 * c))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (j < k) acc += pw[j] * v[j];
-    *reinterpret_cast<f32x4*>(yr + 4 * c) = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * c));
   }
 }
 
@@ -88,9 +113,9 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
       m &= m - 1;
       const int r = __shfl(row, e);
       const float s = __shfl(sc, e);
-      acc += s * *reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c);
+      acc += s * __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c));
     }
-    *reinterpret_cast<f32x4*>(yr + 4 * c) = acc;
+    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * c));
   }
 }
 
