@@ -134,6 +134,9 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
  *   MOE_WS_XPERM   [R, d_model]  dtype, x rows in expert-contiguous order
  *   MOE_WS_H       [R, d_ff]     dtype, silu(x W_gate) * (x W_up) per row
  *   MOE_WS_O       [R, d_model]  fp32, expert output per row (before weighting)
+ * Expert choice in bf16 carries h's bf16 rounding residual: the MOE_WS_H region then holds
+ * 2R rows (h, then the residual), MOE_WS_O 2R rows (their down projections; the expert output
+ * is the sum of rows r and R + r), and MOE_WS_OFFSETS 2E+1 entries (g*C).
  * R = T*k (token choice) or E*C (expert choice). With an expert capacity only rows
  * [0, offsets[E]) hold kept slots, offsets[E] = sum_e min(counts_e, C). MOE_WS_POS is
  * MOE_ERR_UNSUPPORTED in expert choice. */

@@ -25,8 +25,9 @@
 //     behind kWaves256 = 8: two waves per SIMD in a ping-pong schedule (pp_step).
 //     Smaller tiles (256 x 128, 256 x 64) use the plain ring (ring_step);
 //   * gate and up tiles share the A tile; the SwiGLU epilogue silu(g) * u runs in
-//     registers and writes h in bf16 (plus its bf16 residual when asked). The down
-//     projection writes o in fp32.
+//     registers and writes h in bf16 (plus its bf16 residual when asked: SPLIT). The
+//     down projection writes o in fp32; group e takes weight matrix e % EW, so that the
+//     residual rows can run as groups of their own against the same weights.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 outputs per thread).
 #include "common.h"
@@ -142,7 +143,6 @@ struct Geo {
 template <class G, bool SWIGLU, bool SPLIT>
 struct StageLoader {
   const bf16* Ab;                 // A rows of this tile (h or x_perm)
-  const bf16* Ab2;                // second A half (SPLIT down projection)
   const bf16* b_base[G::B_PW];    // weight matrix each B instruction reads
   int a_src[G::A_PW];             // per-lane element offsets (row, chunk)
   int b_src[G::B_PW];
@@ -151,11 +151,9 @@ struct StageLoader {
   // load j (0 .. LPS-1: A loads, then B loads; a constant at every call) of stage kt
   // into stage buffer st
   __device__ __forceinline__ void issue_one(int j, int kt, char* st) const {
-    const bool second = (SPLIT && !SWIGLU) && kt >= nk;
-    const int kk = (second ? kt - nk : kt) * G::BK;
+    const int kk = kt * G::BK;
     if (j < G::A_PW) {
-      const bf16* As = second ? Ab2 : Ab;
-      __builtin_amdgcn_global_load_lds(As + kk + a_src[j],
+      __builtin_amdgcn_global_load_lds(Ab + kk + a_src[j],
                                        (lds_void*)(st + (wave * G::A_PW + j) * 1024), 16, 0, 0);
     } else {
       const int jb = j - G::A_PW;
@@ -165,21 +163,16 @@ struct StageLoader {
     }
   }
   __device__ __forceinline__ void issue(int kt, char* st) const {
+    const int kk = kt * G::BK;
 #pragma unroll
-    for (int j = 0; j < G::A_PW; ++j) {
-      const bool second = (SPLIT && !SWIGLU) && kt >= nk;
-      const int kk = (second ? kt - nk : kt) * G::BK;
-      __builtin_amdgcn_global_load_lds((second ? Ab2 : Ab) + kk + a_src[j],
+    for (int j = 0; j < G::A_PW; ++j)
+      __builtin_amdgcn_global_load_lds(Ab + kk + a_src[j],
                                        (lds_void*)(st + (wave * G::A_PW + j) * 1024), 16, 0, 0);
-    }
 #pragma unroll
-    for (int j = 0; j < G::B_PW; ++j) {
-      const bool second = (SPLIT && !SWIGLU) && kt >= nk;
-      const int kk = (second ? kt - nk : kt) * G::BK;
+    for (int j = 0; j < G::B_PW; ++j)
       __builtin_amdgcn_global_load_lds(b_base[j] + (size_t)kk * N + b_src[j],
                                        (lds_void*)(st + G::A_BYTES + (wave * G::B_PW + j) * 1024),
                                        16, 0, 0);
-    }
   }
 };
 
@@ -459,13 +452,13 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
 // Kernel arguments shared by the tile helpers.
 struct GemmArgs {
   const bf16* A;         // rows (x_perm or h), [R, K]
-  const bf16* A2;        // second row set of the split down projection (h_lo)
   const bf16* B0;        // W_gate or W_down, [E, K, N]
   const bf16* B1;        // W_up (SwiGLU)
   const int32_t* offsets;
   int E, K, N;
+  int EW;                // weight matrices: group e uses matrix e % EW
   void* out;             // h (bf16) or o (fp32)
-  void* out2;            // h_lo (bf16, split)
+  void* out2;            // h_lo (bf16, SPLIT): the bf16 rounding residual of h
 };
 
 // One output tile: expert e, rows [row0, row0 + rows), output columns from n0.
@@ -543,12 +536,12 @@ __device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmA
                                                                     int wave, int nk) {
   StageLoader<G, SWIGLU, SPLIT> ld;
   ld.Ab = a.A + (size_t)t.row0 * a.K;
-  ld.Ab2 = (SPLIT && !SWIGLU) ? a.A2 + (size_t)t.row0 * a.K : ld.Ab;
   ld.nk = nk;
   ld.N = a.N;
   ld.wave = wave;
-  const bf16* W0 = a.B0 + (size_t)t.e * a.K * a.N;
-  const bf16* W1 = SWIGLU ? a.B1 + (size_t)t.e * a.K * a.N : W0;
+  const int ew = t.e < a.EW ? t.e : t.e % a.EW;
+  const bf16* W0 = a.B0 + (size_t)ew * a.K * a.N;
+  const bf16* W1 = SWIGLU ? a.B1 + (size_t)ew * a.K * a.N : W0;
 #pragma unroll
   for (int j = 0; j < G::A_PW; ++j) {
     const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
@@ -583,7 +576,7 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[G::NBW][G::MB]) {
 
 // Epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
 // ncol = 8q + 4 * (lane / 32) inside 32-column block nb. SwiGLU: h = silu(gate) * up in
-// bf16 (and the bf16 residual of h when split); down projection: o in fp32.
+// bf16 (and the bf16 residual of h when SPLIT); down projection: o in fp32.
 template <class G, bool SWIGLU, bool SPLIT>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t, int ln, int wm,
                                            int wn, const f32x16 (&acc)[G::NBW][G::MB]) {
@@ -702,8 +695,8 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
 
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ A2, const bf16* __restrict__ B0,
-    const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N,
+    const bf16* __restrict__ A, const bf16* __restrict__ B0,
+    const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
     void* __restrict__ out, void* __restrict__ out2) {
   using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
   // one array per ring stage, so that the compiler can tell a stage's LDS reads from
@@ -744,9 +737,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     my_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
   }
   const int nk = K / G::BK;
-  const int nk_total = (SPLIT && !SWIGLU) ? 2 * nk : nk;
+  const int nk_total = nk;
 
-  const GemmArgs args{A, A2, B0, B1, offsets, E, K, N, out, out2};
+  const GemmArgs args{A, B0, B1, offsets, E, K, N, EW, out, out2};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
       if (slot < my_total)
@@ -855,13 +848,12 @@ int device_cu_count() {
 }
 
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
-hipError_t launch_bf16(const void* A, const void* A2, const void* B0, const void* B1,
-                       const int32_t* offsets, int E, int K, int N, void* out, void* out2,
-                       hipStream_t s) {
+hipError_t launch_bf16(const void* A, const void* B0, const void* B1, const int32_t* offsets, int E,
+                       int EW, int K, int N, void* out, void* out2, hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW><<<grid, 64 * NW, 0, s>>>(
-      static_cast<const bf16*>(A), static_cast<const bf16*>(A2), static_cast<const bf16*>(B0),
-      static_cast<const bf16*>(B1), offsets, E, K, N, out, out2);
+      static_cast<const bf16*>(A), static_cast<const bf16*>(B0), static_cast<const bf16*>(B1),
+      offsets, E, K, N, EW, out, out2);
   return hipGetLastError();
 }
 
@@ -869,18 +861,21 @@ template <bool SPLIT>
 hipError_t gateup_bf16(const void* xp, const void* Wgate, const void* Wup, const int32_t* offsets,
                        int E, int d, int f, void* h, void* h_lo, hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
-  return launch_bf16<256, 128, true, SPLIT, 4>(xp, nullptr, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, Wgate, Wup, offsets, E, E, d, f, h,
+                                                         h_lo, s);
+  return launch_bf16<256, 128, true, SPLIT, 4>(xp, Wgate, Wup, offsets, E, E, d, f, h, h_lo, s);
 }
 
-template <bool SPLIT>
-hipError_t down_bf16(const void* h, const void* h_lo, const void* Wdown, const int32_t* offsets,
-                     int E, int f, int d, float* o, hipStream_t s) {
+hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int EW,
+                     int f, int d, float* o, hipStream_t s) {
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, SPLIT, kWaves256>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+    return launch_bf16<256, 256, false, false, kWaves256>(h, Wdown, nullptr, offsets, E, EW, f, d,
+                                                          o, nullptr, s);
   if (d % 128 == 0)
-    return launch_bf16<256, 128, false, SPLIT, 4>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
-  return launch_bf16<256, 64, false, SPLIT, 4>(h, h_lo, Wdown, nullptr, offsets, E, f, d, o, nullptr, s);
+    return launch_bf16<256, 128, false, false, 4>(h, Wdown, nullptr, offsets, E, EW, f, d, o,
+                                                  nullptr, s);
+  return launch_bf16<256, 64, false, false, 4>(h, Wdown, nullptr, offsets, E, EW, f, d, o, nullptr,
+                                               s);
 }
 
 }  // namespace
@@ -900,13 +895,10 @@ hipError_t launch_gemm_gateup(int bf16in, const void* xp, const void* Wgate, con
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down(int bf16in, const void* h, const void* h_lo, const void* Wdown,
-                            const int32_t* offsets, int E, int R_max, int f, int d, float* o,
-                            hipStream_t s) {
-  if (bf16in) {
-    if (h_lo) return down_bf16<true>(h, h_lo, Wdown, offsets, E, f, d, o, s);
-    return down_bf16<false>(h, nullptr, Wdown, offsets, E, f, d, o, s);
-  }
+hipError_t launch_gemm_down(int bf16in, const void* h, const void* Wdown, const int32_t* offsets,
+                            int E, int EW, int R_max, int f, int d, float* o, hipStream_t s) {
+  if (bf16in) return down_bf16(h, Wdown, offsets, E, EW, f, d, o, s);
+  if (EW != E) return hipErrorInvalidValue;  // the fp32 path runs one matrix per group
   dim3 grid(d / 64, R_max / 64 + E);
   gemm_f32_kernel<false><<<grid, 256, 0, s>>>(static_cast<const float*>(h),
                                               static_cast<const float*>(Wdown), nullptr, offsets,

@@ -33,9 +33,11 @@ struct RouterArgs {
 hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
 
 // Expert choice: per expert, softmax over tokens, top-C tokens (ascending token
-// order) and scores. Also writes offsets[e] = e*C and counts (optional).
+// order) and scores. Also writes offsets[g] = g*C for g <= ngroups (E, or 2E when the
+// down projection runs the residual rows as groups of their own) and counts (optional).
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
-                            float* probs, int32_t* offsets, int32_t* counts, hipStream_t s);
+                            float* probs, int32_t* offsets, int ngroups, int32_t* counts,
+                            hipStream_t s);
 
 // Dispatch prefix sum over per-block counts: counts[E] (unclamped), offsets[E+1] (group
 // starts; with an expert capacity cap the groups hold min(count, cap) rows),
@@ -62,20 +64,22 @@ hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
 //   gate/up: h[r] = silu(x_perm[r] W_gate[e]) * (x_perm[r] W_up[e])  -> h [R, f]
 //   down:    o[r] = h[r] W_down[e]                                   -> o [R, d] fp32
 // With h_lo non-null (bf16 only) the gate/up epilogue also writes the bf16 rounding
-// residual of h, and the down GEMM consumes h + h_lo. R_max bounds the routed rows.
+// residual of h. The down GEMM's group e uses W_down[e % EW] (EW = E normally; the
+// residual rows run as E more groups, EW = E, E' = 2E). R_max bounds the routed rows.
 hipError_t launch_gemm_gateup(int bf16, const void* xp, const void* Wgate, const void* Wup,
                               const int32_t* offsets, int E, int R_max, int d, int f, void* h,
                               void* h_lo, hipStream_t s);
-hipError_t launch_gemm_down(int bf16, const void* h, const void* h_lo, const void* Wdown,
-                            const int32_t* offsets, int E, int R_max, int f, int d, float* o,
-                            hipStream_t s);
+hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
+                            int E, int EW, int R_max, int f, int d, float* o, hipStream_t s);
 
 // y[t] = sum_j w[t,j] * o[pos[t,j]]  (j in slot order)
 hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,
                              int k, float* y, hipStream_t s);
-// y[t] = sum over experts e (ascending) that chose t of score[e,c] * o[e*C + c]; else 0
-hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
-                             int E, int C, float* y, hipStream_t s);
+// y[t] = sum over experts e (ascending) that chose t of score[e,c] * o[e*C + c]; else 0.
+// With o_lo (the residual rows' outputs) the row is o[r] + o_lo[r].
+hipError_t launch_combine_ec(const float* o, const float* o_lo, const int32_t* idx,
+                             const float* score, int T, int d, int E, int C, float* y,
+                             hipStream_t s);
 
 // Per-block counts and probability sums from router outputs (standalone aux loss).
 hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,

@@ -21,7 +21,8 @@ struct Layout {
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
          offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
-         total = 0;
+         o_lo = 0, total = 0;
+  int ngroups = 0;  // groups of the down projection: E, or 2E with the residual rows
 };
 
 int64_t ec_capacity(const moe_shape& s) {
@@ -104,14 +105,20 @@ Layout make_layout(const moe_shape& s) {
     L.w = take(L.R * 4);
   }
   L.blk_zsum = take((size_t)L.nblk * 4);
-  L.offsets = take((E + 1) * 4);
+  // expert choice, bf16: h's bf16 rounding residual is carried as rows R .. 2R-1 of the
+  // h region, and the down projection runs them as E more groups (same weights) into
+  // rows R .. 2R-1 of the o region; the combine adds the two halves
+  const bool resid = s.mode == MOE_EXPERT_CHOICE && s.dtype == MOE_BF16;
+  const int64_t hrows = resid ? 2 * L.R : L.R;
+  L.ngroups = resid ? 2 * s.E : s.E;
+  L.offsets = take((size_t)(L.ngroups + 1) * 4);
   L.counts = take(E * 4);
   L.src = take(L.R * 4);
   L.x_perm = take((size_t)L.R * d * eb);
-  L.h = take((size_t)L.R * f * eb);
-  // expert choice, bf16: the residual of h's rounding (see launch_gemm_gateup)
-  if (s.mode == MOE_EXPERT_CHOICE && s.dtype == MOE_BF16) L.h_lo = take((size_t)L.R * f * eb);
-  L.o = take((size_t)L.R * d * 4);
+  L.h = take((size_t)hrows * f * eb);
+  if (resid) L.h_lo = L.h + (size_t)L.R * f * eb;
+  L.o = take((size_t)hrows * d * 4);
+  if (resid) L.o_lo = L.o + (size_t)L.R * d * 4;
   L.total = cur;
   return L;
 }
@@ -234,7 +241,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
     MOE_LAUNCH(MOE_STAGE_EC_SELECT,
                launch_ec_select(at<float>(ws, L.logitsT), (int)s.T, s.E, (int)L.C, idx, w, probs,
-                                at<int32_t>(ws, L.offsets), user_counts, stream));
+                                at<int32_t>(ws, L.offsets), L.ngroups, user_counts, stream));
   }
   return MOE_OK;
 }
@@ -370,8 +377,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
              launch_gemm_gateup(bf, at<void>(ws, L.x_perm), W_gate, W_up, offsets, E, R, d, ff,
                                 at<void>(ws, L.h), h_lo, stream));
-  MOE_LAUNCH(MOE_STAGE_GEMM_DOWN, launch_gemm_down(bf, at<void>(ws, L.h), h_lo, W_down, offsets, E,
-                                                   R, ff, d, at<float>(ws, L.o), stream));
+  MOE_LAUNCH(MOE_STAGE_GEMM_DOWN,
+             launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, L.ngroups, E,
+                              L.h_lo ? 2 * R : R, ff, d, at<float>(ws, L.o), stream));
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
@@ -381,7 +389,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
                                   L.nblk, T, E, s.k, f, p, loss, nullptr,
                                   at<float>(ws, L.blk_zsum), z_loss, stream));
   } else {
-    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, T, d, E,
+    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o),
+                                                    L.o_lo ? at<float>(ws, L.o_lo) : nullptr,
+                                                    idx_b, w_b, T, d, E,
                                                     (int)L.C, y, stream));
     if (z_loss)
       MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, T, 0, s.k, nullptr,

@@ -399,7 +399,8 @@ template <bool INLDS>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __restrict__ logitsT,
                                                                int T, int E, int C, int32_t* idx,
                                                                float* score, float* probs,
-                                                               int32_t* offsets, int32_t* counts) {
+                                                               int32_t* offsets, int ngroups,
+                                                               int32_t* counts) {
   __shared__ float colsh[INLDS ? kEcLdsTokens : 1];
   __shared__ int whist[kEcWaves][256];
   __shared__ float redf[kEcWaves];
@@ -518,7 +519,8 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   }
   if (tid == 0) {
     offsets[e] = e * C;
-    if (e == E - 1) offsets[E] = E * C;
+    if (ngroups > E) offsets[E + e] = (E + e) * C;  // the residual rows' groups
+    if (e == E - 1) offsets[ngroups] = ngroups * C;
     if (counts) counts[e] = C;
   }
 }
@@ -553,12 +555,14 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
 }
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
-                            float* probs, int32_t* offsets, int32_t* counts, hipStream_t s) {
+                            float* probs, int32_t* offsets, int ngroups, int32_t* counts,
+                            hipStream_t s) {
+  if (ngroups != E && ngroups != 2 * E) return hipErrorInvalidValue;
   if (T <= kEcLdsTokens)
     ec_select_kernel<true><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                    counts);
+                                                    ngroups, counts);
   else
     ec_select_kernel<false><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                     counts);
+                                                     ngroups, counts);
   return hipGetLastError();
 }
