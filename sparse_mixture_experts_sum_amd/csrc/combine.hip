@@ -149,67 +149,30 @@ __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restri
   }
   block_expert_sums<16>(v, (E + 3) / 4, E, red, blk_psum + (size_t)blockIdx.x * E);
   __syncthreads();
-  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
+  if (tid < E) blk_counts[(size_t)tid * gridDim.x + blockIdx.x] = cnt[tid];
 }
 
-// 1024 threads: thread (part, e) sums a contiguous range of blocks for expert e;
-// the 16 partial sums per expert are then added in part order (deterministic).
-constexpr int kAuxParts = 16;
+// 1024 threads: assignment totals per expert from the per-block counts ([E, nblk],
+// expert-major), then the statistics in the shared fixed order (aux_stats_block).
 __global__ __launch_bounds__(1024) void aux_final_kernel(const int32_t* __restrict__ blk_counts,
                                                          const float* __restrict__ blk_psum, int nblk,
                                                          int T, int E, int k, float* f, float* p,
                                                          float* loss, int32_t* counts,
                                                          const float* __restrict__ blk_zsum,
                                                          float* z_loss) {
-  __shared__ long long csum[kAuxParts][64];
-  __shared__ double psum[kAuxParts][64];
-  __shared__ double zsum[kAuxParts];
-  __shared__ double term[64];
-  const int e = threadIdx.x & 63, part = threadIdx.x >> 6;
-  const int per = (nblk + kAuxParts - 1) / kAuxParts;
-  const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
-  long long c = 0;
-  double ps = 0.0;
-  if (e < E) {
-    for (int b = b0; b < b1; ++b) {
-      c += blk_counts[(size_t)b * E + e];
-      ps += (double)blk_psum[(size_t)b * E + e];
-    }
-  }
-  csum[part][e] = c;
-  psum[part][e] = ps;
-  if (e == 0) {
-    double zs = 0.0;
-    if (blk_zsum)
-      for (int b = b0; b < b1; ++b) zs += (double)blk_zsum[b];
-    zsum[part] = zs;
+  __shared__ int cnt[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave w totals experts w, w + 16, ...: a lane-strided sum, then an xor tree
+  for (int e = wave; e < E; e += 16) {
+    int c = 0;
+    for (int b = lane; b < nblk; b += 64) c += blk_counts[(size_t)e * nblk + b];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) c += __shfl_xor(c, o);
+    if (lane == 0) cnt[e] = c;
   }
   __syncthreads();
-  if (threadIdx.x == 64 && z_loss && blk_zsum) {
-    double zt = 0.0;
-    for (int i = 0; i < kAuxParts; ++i) zt += zsum[i];
-    *z_loss = (float)(zt / (double)T);
-  }
-  if (part == 0 && e < E) {
-    long long ct = 0;
-    double pt = 0.0;
-    for (int i = 0; i < kAuxParts; ++i) {
-      ct += csum[i][e];
-      pt += psum[i][e];
-    }
-    const float fe = (float)((double)ct / (double)T);
-    const float pe = (float)(pt / (double)T);
-    if (f) f[e] = fe;
-    if (p) p[e] = pe;
-    if (counts) counts[e] = (int32_t)ct;
-    term[e] = ((double)fe / (double)k) * (double)pe;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && loss) {
-    double sacc = 0.0;
-    for (int i = 0; i < E; ++i) sacc += term[i];
-    *loss = (float)((double)E * sacc);
-  }
+  if (counts && threadIdx.x < E) counts[threadIdx.x] = cnt[threadIdx.x];
+  aux_stats_block(cnt, blk_psum, blk_zsum, nblk, T, E, k, f, p, loss, z_loss);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {

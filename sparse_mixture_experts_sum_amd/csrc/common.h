@@ -88,3 +88,47 @@ __device__ __forceinline__ void block_expert_sums(float (&v)[NMAX], int nper, in
   if (tid < E) out[tid] = ((red[tid] + red[64 + tid]) + red[128 + tid]) + red[192 + tid];
 }
 
+// Load-balancing statistics from per-block partials (Mixture of Experts（MoE）の理論と実装,
+// load_balancing_loss; the Korean page's compute_load_balancing_loss and router_z_loss):
+//   f[e] = cnt[e] / T, p[e] = (sum over blocks of blk_psum[b, e]) / T,
+//   loss = E * sum_e (f[e] / k) * p[e], z_loss = (sum over blocks of blk_zsum[b]) / T.
+// One fixed order whichever kernel calls it: item i (expert i < E, the z-loss for i = E)
+// belongs to wave i % 16, whose lane l adds blocks l, l + 64, ... in double, then an xor
+// tree over the lanes; thread 0 adds the loss terms in expert order. cnt: the E
+// assignment totals, in LDS, visible to all threads. 1024 threads; every thread must call
+// it. Null outputs are skipped.
+__device__ inline void aux_stats_block(const int* cnt, const float* __restrict__ blk_psum,
+                                       const float* __restrict__ blk_zsum, int nblk, int T, int E,
+                                       int k, float* f, float* p, float* loss, float* z_loss) {
+  __shared__ double item[65];
+  __shared__ double term[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = wave; i <= E; i += 16) {
+    double v = 0.0;
+    if (i < E) {
+      if (blk_psum)
+        for (int b = lane; b < nblk; b += 64) v += (double)blk_psum[(size_t)b * E + i];
+    } else if (blk_zsum) {
+      for (int b = lane; b < nblk; b += 64) v += (double)blk_zsum[b];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    if (lane == 0) item[i] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 64 && z_loss && blk_zsum) *z_loss = (float)(item[E] / (double)T);
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    const float fe = (float)((double)cnt[e] / (double)T);
+    const float pe = (float)(item[e] / (double)T);
+    if (f) f[e] = fe;
+    if (p) p[e] = pe;
+    term[e] = ((double)fe / (double)k) * (double)pe;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && loss) {
+    double sacc = 0.0;
+    for (int i = 0; i < E; ++i) sacc += term[i];
+    *loss = (float)((double)E * sacc);
+  }
+}

@@ -15,60 +15,96 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
-// One workgroup. Entry (e, b) of the expert-major sequence q = e*nblk + b holds
-// blk_counts[b, e]; its exclusive prefix is the first slot of block b's slots for
-// expert e in the expert's flattened (token, slot) order, and the prefix at (e, 0) is
-// the start of expert e's group. With an expert capacity `cap`, expert e keeps only
-// the first cap of its slots: its group shrinks to min(count, cap) rows, the groups
+// One workgroup. Entry q = e*nblk + b of the per-block counts (expert-major, [E, nblk])
+// holds block b's slots for expert e; its exclusive prefix is the first slot of block b's
+// slots for expert e in the expert's flattened (token, slot) order, and the prefix at
+// (e, 0) is the start of expert e's group. With an expert capacity `cap`, expert e keeps
+// only the first cap of its slots: its group shrinks to min(count, cap) rows, the groups
 // are laid out from those sizes, and base[b, e] is the clamped group start plus the
 // block's unclamped prefix (rows at or past start + cap are dropped by the permute).
 // counts stay the unclamped assignments. cap = INT_MAX: no capacity.
-__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
-    const int32_t* __restrict__ blk_counts, int nblk, int E, int cap, int32_t* counts,
-    int32_t* offsets, int32_t* base, int32_t* user_counts) {
+// When any of f, p, loss, z_loss is given, the load-balancing statistics follow from the
+// same totals (aux_stats_block: the order of the standalone statistics kernel).
+constexpr int kScanCache = 16;  // entries per thread kept in registers between the passes
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(ScanArgs a) {
   __shared__ int sh[17];
   __shared__ int off_sh[65];   // unclamped group starts
   __shared__ int offc_sh[65];  // group starts from the clamped sizes
+  __shared__ int cnt_sh[64];
+  const int nblk = a.nblk, E = a.E;
   const long n = (long)nblk * E;
   const int tid = threadIdx.x;
   const long per = (n + kScanThreads - 1) / kScanThreads;
   const long qb = min(n, (long)tid * per), qe = min(n, qb + per);
+  const bool cached = per <= kScanCache;
+  int v[kScanCache];
   int local = 0;
-  for (long q = qb; q < qe; ++q) {
-    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
-    local += blk_counts[(size_t)b * E + e];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kScanCache; ++i) {
+      v[i] = qb + i < qe ? a.blk_counts[qb + i] : 0;
+      local += v[i];
+    }
+  } else {
+    for (long q = qb; q < qe; ++q) local += a.blk_counts[q];
   }
   int total;
   const int run0 = block_exclusive_scan(local, sh, &total);
   int run = run0;
-  for (long q = qb; q < qe; ++q) {
-    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
-    if (b == 0) off_sh[e] = run;
-    run += blk_counts[(size_t)b * E + e];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kScanCache; ++i) {
+      const long q = qb + i;
+      if (q < qe && q % nblk == 0) off_sh[q / nblk] = run;
+      run += v[i];
+    }
+  } else {
+    for (long q = qb; q < qe; ++q) {
+      if (q % nblk == 0) off_sh[q / nblk] = run;
+      run += a.blk_counts[q];
+    }
   }
   if (tid == 0) off_sh[E] = total;
   __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      offc_sh[e] = acc;
-      acc += min(off_sh[e + 1] - off_sh[e], cap);
+  if (tid < 64) {  // wave 0: clamped sizes and their exclusive prefix (E <= 64)
+    const int c = tid < E ? off_sh[tid + 1] - off_sh[tid] : 0;
+    cnt_sh[tid] = c;
+    const int cc = min(c, a.cap);
+    int incl = cc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (tid >= o) incl += u;
     }
-    offc_sh[E] = acc;
+    if (tid < E) offc_sh[tid] = incl - cc;
+    if (tid == E - 1) offc_sh[E] = incl;
   }
   __syncthreads();
   run = run0;
-  for (long q = qb; q < qe; ++q) {
-    const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
-    base[(size_t)b * E + e] = offc_sh[e] + (run - off_sh[e]);
-    run += blk_counts[(size_t)b * E + e];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kScanCache; ++i) {
+      const long q = qb + i;
+      if (q < qe) {
+        const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
+        a.base[(size_t)b * E + e] = offc_sh[e] + (run - off_sh[e]);
+      }
+      run += v[i];
+    }
+  } else {
+    for (long q = qb; q < qe; ++q) {
+      const int e = (int)(q / nblk), b = (int)(q - (long)e * nblk);
+      a.base[(size_t)b * E + e] = offc_sh[e] + (run - off_sh[e]);
+      run += a.blk_counts[q];
+    }
   }
-  if (tid <= E) offsets[tid] = offc_sh[tid];
+  if (tid <= E) a.offsets[tid] = offc_sh[tid];
   if (tid < E) {
-    const int c = off_sh[tid + 1] - off_sh[tid];
-    counts[tid] = c;
-    if (user_counts) user_counts[tid] = c;
+    a.counts[tid] = cnt_sh[tid];
+    if (a.user_counts) a.user_counts[tid] = cnt_sh[tid];
   }
+  if (a.f || a.p || a.loss || a.z_loss)
+    aux_stats_block(cnt_sh, a.blk_psum, a.blk_zsum, nblk, a.T, E, a.k, a.f, a.p, a.loss, a.z_loss);
 }
 
 // One wave per token: slots first (pos, src), then the row copy to every slot's row.
@@ -153,11 +189,9 @@ __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict_
 
 }  // namespace
 
-hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int cap,
-                                int32_t* counts, int32_t* offsets, int32_t* base,
-                                int32_t* user_counts, hipStream_t s) {
-  dispatch_scan_kernel<<<1, kScanThreads, 0, s>>>(blk_counts, nblk, E, cap, counts, offsets, base,
-                                                  user_counts);
+hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s) {
+  if (a.E < 1 || a.E > 64) return hipErrorInvalidValue;
+  dispatch_scan_kernel<<<1, kScanThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ struct RouterArgs {
   float* w;             // [T, k]
   float* probs;         // [T, E] or nullptr
   int32_t* lrank;       // [T, k] rank of the slot among equal experts within its block
-  int32_t* blk_counts;  // [nblk, E]
+  int32_t* blk_counts;  // [E, nblk] (expert-major)
   float* blk_psum;      // [nblk, E] column sums of probs over the block's tokens
   // both modes, optional: per block, sum over its tokens of logsumexp(logits)^2
   float* blk_zsum;      // [nblk] or nullptr
@@ -39,13 +39,26 @@ hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* 
                             float* probs, int32_t* offsets, int ngroups, int32_t* counts,
                             hipStream_t s);
 
-// Dispatch prefix sum over per-block counts: counts[E] (unclamped), offsets[E+1] (group
-// starts; with an expert capacity cap the groups hold min(count, cap) rows),
-// base[nblk, E] (row of each (block, expert) pair's first slot), optional user counts.
-// cap = INT_MAX: no capacity.
-hipError_t launch_dispatch_scan(const int32_t* blk_counts, int nblk, int E, int cap,
-                                int32_t* counts, int32_t* offsets, int32_t* base,
-                                int32_t* user_counts, hipStream_t s);
+// Dispatch prefix sum over per-block counts blk_counts [E, nblk] (expert-major):
+// counts[E] (unclamped), offsets[E+1] (group starts; with an expert capacity cap the
+// groups hold min(count, cap) rows), base[nblk, E] (row of each (block, expert) pair's
+// first slot), optional user counts; cap = INT_MAX: no capacity. Optionally also the
+// load-balancing statistics f, p, loss and z_loss from the per-block partials, in the
+// same order as launch_aux_final.
+struct ScanArgs {
+  const int32_t* blk_counts;  // [E, nblk]
+  int nblk, E, cap;
+  int32_t* counts;            // [E]
+  int32_t* offsets;           // [E+1]
+  int32_t* base;              // [nblk, E]
+  int32_t* user_counts;       // [E] or nullptr
+  // statistics (all optional)
+  const float* blk_psum;      // [nblk, E]
+  const float* blk_zsum;      // [nblk]
+  int T, k;
+  float *f, *p, *loss, *z_loss;
+};
+hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s);
 
 // Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t]. With a
 // capacity (cap < INT_MAX) slots ranked cap or later in their expert get pos = -1 and
@@ -81,7 +94,7 @@ hipError_t launch_combine_ec(const float* o, const float* o_lo, const int32_t* i
                              const float* score, int T, int d, int E, int C, float* y,
                              hipStream_t s);
 
-// Per-block counts and probability sums from router outputs (standalone aux loss).
+// Per-block counts ([E, nblk]) and probability sums from router outputs (standalone aux loss).
 hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,
                                int32_t* blk_counts, float* blk_psum, hipStream_t s);
 // f, p, loss (and optional counts) from per-block partials (E = 0: none of them), and

@@ -205,12 +205,14 @@ moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, f
 }
 
 // Router stage shared by moe_route and moe_forward. Token choice writes idx/w and the
-// dispatch tables; expert choice writes idx/score and the group offsets. With want_z the
-// router also leaves the per-block z-loss partials in the workspace.
+// dispatch tables (and, in token choice, the requested statistics f, p, loss, z_loss in the
+// dispatch scan); expert choice writes idx/score and the group offsets, and with z_loss
+// leaves the per-block z-loss partials in the workspace for launch_aux_final.
 moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
                       const float* b_g, const moe_noise* noise, int32_t* idx, float* w,
-                      float* probs, int32_t* user_counts, bool want_z, void* ws,
-                      hipStream_t stream) {
+                      float* probs, int32_t* user_counts, float* f, float* p, float* loss,
+                      float* z_loss, void* ws, hipStream_t stream) {
+  const bool want_z = z_loss != nullptr;
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
   a.x = x;
@@ -232,10 +234,24 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     a.blk_counts = at<int32_t>(ws, L.blk_counts);
     a.blk_psum = at<float>(ws, L.blk_psum);
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 0, stream));
-    MOE_LAUNCH(MOE_STAGE_SCAN,
-               launch_dispatch_scan(at<int32_t>(ws, L.blk_counts), L.nblk, s.E, tc_cap_limit(s),
-                                    at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
-                                    at<int32_t>(ws, L.base), user_counts, stream));
+    ScanArgs sa{};
+    sa.blk_counts = at<int32_t>(ws, L.blk_counts);
+    sa.nblk = L.nblk;
+    sa.E = s.E;
+    sa.cap = tc_cap_limit(s);
+    sa.counts = at<int32_t>(ws, L.counts);
+    sa.offsets = at<int32_t>(ws, L.offsets);
+    sa.base = at<int32_t>(ws, L.base);
+    sa.user_counts = user_counts;
+    sa.blk_psum = at<float>(ws, L.blk_psum);
+    sa.blk_zsum = want_z ? at<float>(ws, L.blk_zsum) : nullptr;
+    sa.T = (int)s.T;
+    sa.k = s.k;
+    sa.f = f;
+    sa.p = p;
+    sa.loss = loss;
+    sa.z_loss = z_loss;
+    MOE_LAUNCH(MOE_STAGE_SCAN, launch_dispatch_scan(sa, stream));
   } else {
     a.logitsT = at<float>(ws, L.logitsT);
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
@@ -314,9 +330,10 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, z_loss, stream);
-  st = run_router(s, L, x, W_g, b_g, noise, idx, w, probs, counts, z_loss != nullptr, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, noise, idx, w, probs, counts, nullptr, nullptr, nullptr,
+                  z_loss, ws, stream);
   if (st != MOE_OK) return st;
-  if (z_loss)
+  if (z_loss && !is_tc(s.mode))
     MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, (int)s.T, 0, s.k, nullptr,
                                                nullptr, nullptr, nullptr,
                                                at<float>(ws, L.blk_zsum), z_loss, stream));
@@ -360,7 +377,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
   void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
-  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss != nullptr, ws,
+  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, f, p, loss, z_loss, ws,
                   stream);
   if (st != MOE_OK) return st;
   if (is_tc(s.mode)) {
@@ -383,11 +400,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
-    if (f || p || loss || z_loss)
-      MOE_LAUNCH(MOE_STAGE_AUX,
-                 launch_aux_final(at<int32_t>(ws, L.blk_counts), at<float>(ws, L.blk_psum),
-                                  L.nblk, T, E, s.k, f, p, loss, nullptr,
-                                  at<float>(ws, L.blk_zsum), z_loss, stream));
+    // (f, p, loss and z_loss came out of the dispatch scan)
   } else {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o),
                                                     L.o_lo ? at<float>(ws, L.o_lo) : nullptr,

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     }
   }
   __syncthreads();
-  if (tid < E) a.blk_counts[(size_t)blockIdx.x * E + tid] = running[tid];
+  if (tid < E) a.blk_counts[(size_t)tid * gridDim.x + blockIdx.x] = running[tid];
 }
 
 // ---------------------------------------------------------------------------------
