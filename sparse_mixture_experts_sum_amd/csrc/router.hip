@@ -63,10 +63,12 @@ constexpr int kRouterPF = 4;            // iterations of x loads in flight per w
 
 // x chunks of iteration `it` of a stage: lane group g takes chunks 4u + g, u = 0..3 (the
 // k ranges of the four 32-deep MFMA steps). Loads stay in bounds (clamped to the last
-// chunk of the stage) and are always issued, so that the compiler sees the same number
-// of loads in flight on every path; chunks past the stage's end read as zero, and so
-// does everything of an iteration past the last (the loop then runs whole groups of PF
-// iterations with no branch).
+// chunk of the stage, in the same row) and are always issued, so that the compiler sees
+// the same number of loads in flight on every path; the loop then runs whole groups of
+// PF iterations with no branch. The data is used as loaded: chunks past the stage's end
+// meet a zero W_g fragment in the MFMA instead (see the loop). Masking the loaded
+// values here would make the compiler wait for every load in flight, prefetches
+// included, at each group's end.
 template <int VEC, typename TI>
 __device__ __forceinline__ void router_load_x(const TI* xs, int it, int kn, int g,
                                               u32x4 (&av)[4]) {
@@ -74,8 +76,7 @@ __device__ __forceinline__ void router_load_x(const TI* xs, int it, int kn, int 
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int kx = it * ITK + (4 * u + g) * VEC;
-    const u32x4 v = ld16(xs + min(kx, kn - VEC));
-    av[u] = kx < kn ? v : u32x4{0u, 0u, 0u, 0u};
+    av[u] = ld16(xs + min(kx, kn - VEC));
   }
 }
 
@@ -179,9 +180,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 
   // W_g is staged transposed in LDS (one slice of up to KC rows of k at a time; at most
   // a few slices: d / KC); x is streamed from HBM into registers, PF iterations ahead.
-  // Nothing is zeroed: B fragments of padding experts (>= E) read expert E-1's row (their
-  // logits are never used), and reads past the slice's last k are clamped into it (the
-  // matching x chunks are zero).
+  // B fragments of padding experts (>= E) read expert E-1's row (their logits are never
+  // used); x and W_g reads past the slice's last k are clamped into it, and the W_g
+  // fragment of such a k is replaced by zeros.
   for (int kc = 0; kc < d; kc += KC) {
     const int kn = min(KC, d - kc);
     // the first x loads of the slice go out before W_g is staged, so that the two
@@ -209,7 +210,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
           for (int nb = 0; nb < NB; ++nb) {
             // W_noise blocks (nb >= NG) sit EP rows further down
             const int row = (nb >= NG ? EP : 0) + min((nb % NG) * 16 + (lane & 15), E - 1);
-            const u32x4 bv = ld16(&Wl[row * LDW + min(kx, kn - VEC)]);
+            const u32x4 bw = ld16(&Wl[row * LDW + min(kx, kn - VEC)]);
+            const u32x4 bv = kx < kn ? bw : u32x4{0u, 0u, 0u, 0u};  // k past the stage: 0
             M::step(acc[nb], av[j][u], bv);
           }
         }
