@@ -137,6 +137,13 @@ def test_capacity_fine_grained_top4(moe):
     run_capacity_case(moe, w, 1.0)
 
 
+def test_capacity_max_k_64_experts(moe):
+    # k = 8 of 64 experts with a tight capacity: every token loses some slots
+    w = W.custom("cap_k8_e64", T=600, d=128, f=128, E=64, k=8, bias_std=1.0, seed=(42, 107))
+    out, kept = run_capacity_case(moe, w, 0.5)
+    assert (~kept).any(axis=1).mean() > 0.2
+
+
 def test_capacity_that_drops_nothing_is_plain_token_choice(moe):
     # cf = E / k gives C = T: no expert can overflow, so the layer is plain token choice
     w = W.custom("cap_none_dropped", T=512, d=256, f=256, E=8, k=2, bias_std=1.0, seed=(42, 104))

@@ -120,6 +120,13 @@ def test_noisy_with_capacity(moe):
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05), mode="tc_capacity", cf=0.75)
 
 
+def test_noisy_capacity_fp32_raw_gates(moe):
+    # fp32, softplus noise, an expert capacity, and no renormalisation
+    w = W.custom("noisy_cap_fp32", dtype="fp32", T=500, d=128, f=64, E=8, k=2, x_std=0.5,
+                 wg_std=0.2, bias_std=0.5, renormalize=False, seed=(42, 309))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.2), mode="tc_capacity", cf=0.6)
+
+
 def test_noisy_mixtral_layer_sampled(moe):
     w = W.CONFIGS[3]
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02), sample=32)

@@ -181,6 +181,20 @@ def test_expert_choice_shapes(moe, T, E, cf):
                               k=1, seed=(42, 300 + T + E)))
 
 
+@pytest.mark.parametrize("d,f", [(64, 128), (192, 320)])
+def test_expert_choice_narrow_tiles_bf16(moe, d, f):
+    # d_model 64 / 192: the down projection's 256 x 64 column tiles, which also
+    # run the residual rows of h as groups of their own; d_ff 320 takes the 256 x 128
+    # gate/up tiles
+    run_ec_case(moe, W.custom(f"ec_d{d}_f{f}", T=700, d=d, f=f, E=6, mode="ec", cf=1.5, k=1,
+                              bias_std=0.5, seed=(42, 320 + d)))
+
+
+def test_expert_choice_fp32_bias_ragged(moe):
+    run_ec_case(moe, W.custom("ec_fp32", dtype="fp32", T=333, d=128, f=192, E=5, mode="ec",
+                              cf=2.0, k=1, x_std=0.5, wg_std=0.2, bias_std=1.0, seed=(42, 330)))
+
+
 def test_determinism_bitwise(moe):
     w = W.custom("det", T=777, d=256, f=256, E=8, k=2, seed=(42, 207))
     inp = W.make_inputs(w)
