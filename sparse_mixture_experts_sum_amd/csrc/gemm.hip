@@ -574,6 +574,15 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[G::NBW][G::MB]) {
       for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.f;
 }
 
+// Two 8-byte pieces per lane -> one 16-byte piece: lane l < 32 keeps v[0] and takes the
+// v[0] of lane l + 32; lane l + 32 takes the v[1] of lane l and keeps its own v[1].
+__device__ __forceinline__ u32x4 swap_halves(const u32x2 (&v)[2], bool hi) {
+  const u32x2 snd = hi ? v[0] : v[1];
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)snd[0], 32);
+  const uint32_t r1 = (uint32_t)__shfl_xor((int)snd[1], 32);
+  return hi ? u32x4{r0, r1, v[1][0], v[1][1]} : u32x4{v[0][0], v[0][1], r0, r1};
+}
+
 // Epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
 // ncol = 8q + 4 * (lane / 32) inside 32-column block nb. SwiGLU: h = silu(gate) * up in
 // bf16 (and the bf16 residual of h when SPLIT); down projection: o in fp32.
@@ -587,27 +596,57 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
     const size_t rowoff = (size_t)(t.row0 + m) * a.N + t.n0;
     if constexpr (SWIGLU) {
       constexpr int H = G::NBW / 2;
+      if constexpr (!SPLIT) {
 #pragma unroll
-      for (int nb = 0; nb < H; ++nb)
+        for (int nb = 0; nb < H; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (ln >> 5);
-          bf16x4 hv, lv;
+          for (int q = 0; q < 4; ++q) {
+            const int ncol = wn * (G::WNL / 2) + nb * 32 + 8 * q + 4 * (ln >> 5);
+            bf16x4 hv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float hf = silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
-            hv[i] = (bf16)hf;
-            if constexpr (SPLIT) lv[i] = (bf16)(hf - (float)hv[i]);
+            for (int i = 0; i < 4; ++i) {
+              const float hf =
+                  silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
+              hv[i] = (bf16)hf;
+            }
+            *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.out) + rowoff + ncol) =
+                __builtin_bit_cast(u32x2, hv);
+            // one group of 4 outputs at a time: keeps the accumulator copies out of
+            // AGPRs from piling up in VGPRs
+            __builtin_amdgcn_sched_barrier(0);
           }
-          *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.out) + rowoff + ncol) =
-              __builtin_bit_cast(u32x2, hv);
-          if constexpr (SPLIT)
-            *reinterpret_cast<u32x2*>(static_cast<bf16*>(a.out2) + rowoff + ncol) =
-                __builtin_bit_cast(u32x2, lv);
-          // one group of 4 outputs at a time: keeps the accumulator copies out of
-          // AGPRs from piling up in VGPRs
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      } else {
+        // h and its residual: lanes l and l + 32 swap halves so that every lane stores
+        // 16 contiguous bytes of each (half the store instructions of two arrays)
+#pragma unroll
+        for (int nb = 0; nb < H; ++nb)
+#pragma unroll
+          for (int qp = 0; qp < 2; ++qp) {
+            // outputs q = 2qp, 2qp + 1: lane l < 32 holds columns 16qp + 0..3 and
+            // 16qp + 8..11 of its row, lane l + 32 columns 16qp + 4..7 and 16qp + 12..15;
+            // one exchange leaves 16qp + 0..7 in lane l and 16qp + 8..15 in lane l + 32
+            const bool hi = ln >= 32;
+            u32x2 hq[2], lq[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int q = 2 * qp + j;
+              bf16x4 hv, lv;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float hf =
+                    silu_bf16_path(acc[nb][mb][4 * q + i]) * acc[nb + H][mb][4 * q + i];
+                hv[i] = (bf16)hf;
+                lv[i] = (bf16)(hf - (float)hv[i]);
+              }
+              hq[j] = __builtin_bit_cast(u32x2, hv);
+              lq[j] = __builtin_bit_cast(u32x2, lv);
+            }
+            const int ncol = wn * (G::WNL / 2) + nb * 32 + 16 * qp + (hi ? 8 : 0);
+            st16(static_cast<bf16*>(a.out) + rowoff + ncol, swap_halves(hq, hi));
+            st16(static_cast<bf16*>(a.out2) + rowoff + ncol, swap_halves(lq, hi));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
     } else {
 #pragma unroll
       for (int nb = 0; nb < G::NBW; ++nb)
