@@ -195,6 +195,20 @@ def test_expert_choice_fp32_bias_ragged(moe):
                               cf=2.0, k=1, x_std=0.5, wg_std=0.2, bias_std=1.0, seed=(42, 330)))
 
 
+def test_expert_choice_long_column(moe):
+    # T = 40000 > 32768: the select kernel reads each logit column from HBM in every pass
+    # instead of staging it in LDS
+    run_ec_case(moe, W.custom("ec_T40000", T=40000, d=64, f=64, E=4, mode="ec", cf=1.0, k=1,
+                              bias_std=0.3, seed=(42, 340)))
+
+
+def test_dispatch_scan_many_blocks(moe):
+    # 313 router blocks x 64 experts = 20032 count entries: more than 16 per scan thread,
+    # so the scan re-reads its entries instead of keeping them in registers
+    run_tc_case(moe, W.custom("scan_T20000_E64", T=20000, d=64, f=64, E=64, k=2, wg_std=0.3,
+                              seed=(42, 341)))
+
+
 def test_determinism_bitwise(moe):
     w = W.custom("det", T=777, d=256, f=256, E=8, k=2, seed=(42, 207))
     inp = W.make_inputs(w)
