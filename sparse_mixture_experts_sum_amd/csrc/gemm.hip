@@ -576,11 +576,13 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[G::NBW][G::MB]) {
 
 // Two 8-byte pieces per lane -> one 16-byte piece: lane l < 32 keeps v[0] and takes the
 // v[0] of lane l + 32; lane l + 32 takes the v[1] of lane l and keeps its own v[1].
-__device__ __forceinline__ u32x4 swap_halves(const u32x2 (&v)[2], bool hi) {
-  const u32x2 snd = hi ? v[0] : v[1];
-  const uint32_t r0 = (uint32_t)__shfl_xor((int)snd[0], 32);
-  const uint32_t r1 = (uint32_t)__shfl_xor((int)snd[1], 32);
-  return hi ? u32x4{r0, r1, v[1][0], v[1][1]} : u32x4{v[0][0], v[0][1], r0, r1};
+// v_permlane32_swap exchanges the upper half-wave of its first operand with the lower
+// half-wave of its second (lane layout checked on the device), so two swaps, one per
+// dword, do it with no LDS traffic and no select.
+__device__ __forceinline__ u32x4 swap_halves(const u32x2 (&v)[2]) {
+  const auto r0 = __builtin_amdgcn_permlane32_swap(v[0][0], v[1][0], false, false);
+  const auto r1 = __builtin_amdgcn_permlane32_swap(v[0][1], v[1][1], false, false);
+  return u32x4{r0[0], r1[0], r0[1], r1[1]};
 }
 
 // Epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
@@ -642,8 +644,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
               lq[j] = __builtin_bit_cast(u32x2, lv);
             }
             const int ncol = wn * (G::WNL / 2) + nb * 32 + 16 * qp + (hi ? 8 : 0);
-            st16(static_cast<bf16*>(a.out) + rowoff + ncol, swap_halves(hq, hi));
-            st16(static_cast<bf16*>(a.out2) + rowoff + ncol, swap_halves(lq, hi));
+            st16(static_cast<bf16*>(a.out) + rowoff + ncol, swap_halves(hq));
+            st16(static_cast<bf16*>(a.out2) + rowoff + ncol, swap_halves(lq));
             __builtin_amdgcn_sched_barrier(0);
           }
       }
