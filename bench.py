@@ -1,7 +1,7 @@
 """Benchmark: sparse MoE layer forward on one MI355X.
 
-A step is one full layer forward (router, dispatch scan, permute, grouped SwiGLU
-gate/up GEMM, grouped down GEMM, combine, f/p/loss) over one batch of synthetic
+A step is one full layer forward (router, dispatch scan with f/p/loss, permute, grouped
+SwiGLU gate/up GEMM, grouped down GEMM, combine) over one batch of synthetic
 tokens already resident in HBM. Default workload: the Mixtral 8x7B layer shape
 (T=16384 tokens, d_model=4096, d_ff=14336, E=8, top-2, bf16, router bias
 N(0,1) per expert giving a skewed load).
@@ -45,10 +45,11 @@ def stage_work(w, R=None, noisy=False):
         "gemm_down": ("flop", 2.0 * f * d * R),
     }
     if w.mode == "ec":
-        # logits written once [E, T]; each chosen row gathered and written; o, the
+        # logits written once [E, T]; each chosen row gathered (copied in fp32); o, the
         # choice lists and y for the combine
         work["router"] = ("bytes", T * d * s + d * E * s + T * E * 4)
-        work["permute"] = ("bytes", 2 * R * d * s + R * 4)
+        if w.dtype != "bf16" or T * d >= 2 ** 31:
+            work["permute"] = ("bytes", 2 * R * d * s + R * 4)
         work["combine"] = ("bytes", R * d * 4 + R * 8 + T * d * 4)
         return work
     k = w.k
@@ -56,7 +57,10 @@ def stage_work(w, R=None, noisy=False):
     if noisy:
         router += d * E * s + T * E * 4
     work["router"] = ("bytes", router)
-    work["permute"] = ("bytes", T * d * s + R * d * s + R * 4 + T * k * 4)
+    if w.dtype != "bf16" or T * d >= 2 ** 31:
+        # rows copied into expert order (bf16 layers otherwise gather them inside the
+        # gate/up GEMM, and the permute only writes row indices: a latency-bound stage)
+        work["permute"] = ("bytes", T * d * s + R * d * s + R * 4 + T * k * 4)
     work["combine"] = ("bytes", R * d * 4 + T * k * 8 + T * d * 4)
     return work
 

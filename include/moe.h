@@ -131,7 +131,10 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
  *   MOE_WS_POS     [T, k] int32  token choice: row of each (token, slot), -1 when the
  *                                expert capacity dropped the slot
  *   MOE_WS_SRC     [R] int32     token of each row
- *   MOE_WS_XPERM   [R, d_model]  dtype, x rows in expert-contiguous order
+ *   MOE_WS_XPERM   [R, d_model]  dtype, x rows in expert-contiguous order; only where rows are
+ *                                copied: fp32, or T * d_model >= 2^31 (otherwise the gate/up
+ *                                GEMM reads the rows of x through MOE_WS_SRC and this returns
+ *                                MOE_ERR_UNSUPPORTED)
  *   MOE_WS_H       [R, d_ff]     dtype, silu(x W_gate) * (x W_up) per row
  *   MOE_WS_O       [R, d_model]  fp32, expert output per row (before weighting)
  * Expert choice in bf16 carries h's bf16 rounding residual: the MOE_WS_H region then holds

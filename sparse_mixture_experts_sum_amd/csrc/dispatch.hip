@@ -181,6 +181,7 @@ __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict_
   if (r >= R) return;
   const int t = idx[r];
   if (lane == 0) src[r] = t;
+  if (!x_perm) return;
   const int nch = (int)(row_bytes / 16);
   const char* xr = x + (size_t)t * row_bytes;
   char* dst = x_perm + (size_t)r * row_bytes;

@@ -451,7 +451,8 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
 
 // Kernel arguments shared by the tile helpers.
 struct GemmArgs {
-  const bf16* A;         // rows (x_perm or h), [R, K]
+  const bf16* A;         // rows (x, x_perm or h), [*, K]
+  const int32_t* gather; // row r of the grouped problem is row gather[r] of A; nullptr: row r
   const bf16* B0;        // W_gate or W_down, [E, K, N]
   const bf16* B1;        // W_up (SwiGLU)
   const int32_t* offsets;
@@ -529,13 +530,32 @@ __device__ __forceinline__ void frag_offsets(int ln, int wm, int wn, int (&a_fra
   }
 }
 
-// Direct-load sources of tile t for this lane (element offsets, without the K step).
+// Gathered rows (row r of the tile is row gather[row0 + r] of A; rows past the tile's end
+// repeat its last row). A wave's A loads cover 64 consecutive rows of the tile: lane l
+// fetches the index of row 64 * wave + l (one load, which can be issued long before its
+// use), and each load's lanes take their rows' indices from those lanes (gather_rows).
+template <class G>
+__device__ __forceinline__ int gather_fetch(const GemmArgs& a, const TileCoord& t, int ln, int wave) {
+  static_assert(G::A_PW * G::A_RPI == 64, "a wave's A loads cover 64 rows");
+  return a.gather[t.row0 + min(64 * wave + ln, t.rows - 1)];
+}
+template <class G>
+__device__ __forceinline__ void gather_rows(int fetched, int ln, int (&gv)[G::A_PW]) {
+#pragma unroll
+  for (int j = 0; j < G::A_PW; ++j) gv[j] = __shfl(fetched, j * G::A_RPI + ln / G::A_CPR);
+}
+
+// Direct-load sources of tile t for this lane (element offsets, without the K step). With
+// gathered rows, gv holds gather_rows(t).
 template <class G, bool SWIGLU, bool SPLIT, int BNL>
 __device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmArgs& a,
                                                                     const TileCoord& t, int ln,
-                                                                    int wave, int nk) {
+                                                                    int wave, int nk,
+                                                                    const int (&gv)[G::A_PW]) {
   StageLoader<G, SWIGLU, SPLIT> ld;
-  ld.Ab = a.A + (size_t)t.row0 * a.K;
+  // gathered rows: offsets from A itself (the caller keeps every A offset below 2^31
+  // elements); contiguous rows: offsets from the tile's first row
+  ld.Ab = a.gather ? a.A : a.A + (size_t)t.row0 * a.K;
   ld.nk = nk;
   ld.N = a.N;
   ld.wave = wave;
@@ -546,7 +566,8 @@ __device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmA
   for (int j = 0; j < G::A_PW; ++j) {
     const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
     const int c = (ln % G::A_CPR) ^ a_swz<G::A_CPR>(row);
-    ld.a_src[j] = min(row, t.rows - 1) * a.K + c * 8;
+    const int ar = a.gather ? gv[j] : min(row, t.rows - 1);
+    ld.a_src[j] = ar * a.K + c * 8;
   }
 #pragma unroll
   for (int j = 0; j < G::B_PW; ++j) {
@@ -679,7 +700,9 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
   TileCoord t = locate_tile<BM>(first, a.offsets, NT, G::BN_OUT, xcd);
-  StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk);
+  int gv[G::A_PW] = {};
+  if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
+  StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk, gv);
 #define MOE_SSTEP(J, RL, RSTAGE)                                                             \
   PipeStep<G, SWIGLU, SPLIT, J, true>::run(0, true, true, RL, RSTAGE, ring, a_frag, b_frag, acc, \
                                        (J) % 2 ? F1 : F0, (J) % 2 ? F0 : F1)
@@ -698,6 +721,15 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
 #pragma unroll
     for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
       read_frag<G>(r, ring[0], a_frag, b_frag, F0);
+    // the next tile (this one again after the last: its loads below are unused but in
+    // bounds)
+    const int inext = i + nslot;
+    const bool has_next = inext < my_total;
+    const TileCoord tn = has_next ? locate_tile<BM>(inext, a.offsets, NT, G::BN_OUT, xcd) : t;
+    // gathered rows: the next tile's row indices, fetched now so that the load is long
+    // complete when they are needed (a vector load completes in order with the ring's
+    // loads; one issued just before its use would wait for all of them)
+    const int gnext = (SWIGLU && a.gather) ? gather_fetch<G>(a, tn, fresh_lane(), wave) : 0;
     int kt = 0;
     for (; kt + 2 * S <= nk_total; kt += S) {  // refills from this tile
       MOE_SSTEP(0, ld, kt + S);
@@ -709,15 +741,9 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
     // stages; after the last tile they load this tile's first stages again, unused but
     // in bounds, so that every path into the loop above has the same loads in flight
     // (the compiler then needs no extra wait there). The last step reads nothing.
-    const int inext = i + nslot;
-    const bool has_next = inext < my_total;
-    TileCoord tn = t;
-    StageLoader<G, SWIGLU, SPLIT> ldn = ld;
-    if (has_next) {
-      ln = fresh_lane();
-      tn = locate_tile<BM>(inext, a.offsets, NT, G::BN_OUT, xcd);
-      ldn = make_loader<G, SWIGLU, SPLIT, BNL>(a, tn, ln, wave, nk);
-    }
+    ln = fresh_lane();
+    if (SWIGLU && a.gather) gather_rows<G>(gnext, ln, gv);
+    const StageLoader<G, SWIGLU, SPLIT> ldn = make_loader<G, SWIGLU, SPLIT, BNL>(a, tn, ln, wave, nk, gv);
     MOE_SSTEP(0, ldn, 0);
     MOE_SSTEP(1, ldn, 1);
     MOE_SSTEP(2, ldn, 2);
@@ -736,7 +762,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
 
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B0,
+    const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
     void* __restrict__ out, void* __restrict__ out2) {
   using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
@@ -780,7 +806,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int nk = K / G::BK;
   const int nk_total = nk;
 
-  const GemmArgs args{A, B0, B1, offsets, E, K, N, EW, out, out2};
+  const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, EW, out, out2};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
       if (slot < my_total)
@@ -794,7 +820,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
     const TileCoord t = locate_tile<BM>(i, offsets, NT, G::BN_OUT, xcd);
-    const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk);
+    int gv[G::A_PW] = {};
+    if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
+    const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, gv);
     f32x16 acc[G::NBW][G::MB];
     zero_acc<G>(acc);
 
@@ -889,45 +917,49 @@ int device_cu_count() {
 }
 
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
-hipError_t launch_bf16(const void* A, const void* B0, const void* B1, const int32_t* offsets, int E,
-                       int EW, int K, int N, void* out, void* out2, hipStream_t s) {
+hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, const void* B1,
+                       const int32_t* offsets, int E, int EW, int K, int N, void* out, void* out2,
+                       hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW><<<grid, 64 * NW, 0, s>>>(
-      static_cast<const bf16*>(A), static_cast<const bf16*>(B0), static_cast<const bf16*>(B1),
-      offsets, E, K, N, EW, out, out2);
+      static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
+      static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
   return hipGetLastError();
 }
 
 template <bool SPLIT>
-hipError_t gateup_bf16(const void* xp, const void* Wgate, const void* Wup, const int32_t* offsets,
-                       int E, int d, int f, void* h, void* h_lo, hipStream_t s) {
+hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate, const void* Wup,
+                       const int32_t* offsets, int E, int d, int f, void* h, void* h_lo,
+                       hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, Wgate, Wup, offsets, E, E, d, f, h,
-                                                         h_lo, s);
-  return launch_bf16<256, 128, true, SPLIT, 4>(xp, Wgate, Wup, offsets, E, E, d, f, h, h_lo, s);
+    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, gather, Wgate, Wup, offsets, E, E, d,
+                                                         f, h, h_lo, s);
+  return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d, f, h, h_lo,
+                                               s);
 }
 
 hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int EW,
                      int f, int d, float* o, hipStream_t s) {
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, false, kWaves256>(h, Wdown, nullptr, offsets, E, EW, f, d,
-                                                          o, nullptr, s);
+    return launch_bf16<256, 256, false, false, kWaves256>(h, nullptr, Wdown, nullptr, offsets, E, EW,
+                                                          f, d, o, nullptr, s);
   if (d % 128 == 0)
-    return launch_bf16<256, 128, false, false, 4>(h, Wdown, nullptr, offsets, E, EW, f, d, o,
-                                                  nullptr, s);
-  return launch_bf16<256, 64, false, false, 4>(h, Wdown, nullptr, offsets, E, EW, f, d, o, nullptr,
-                                               s);
+    return launch_bf16<256, 128, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d,
+                                                  o, nullptr, s);
+  return launch_bf16<256, 64, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d, o,
+                                               nullptr, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_gateup(int bf16in, const void* xp, const void* Wgate, const void* Wup,
-                              const int32_t* offsets, int E, int R_max, int d, int f, void* h,
-                              void* h_lo, hipStream_t s) {
+hipError_t launch_gemm_gateup(int bf16in, const void* xp, const int32_t* gather, const void* Wgate,
+                              const void* Wup, const int32_t* offsets, int E, int R_max, int d,
+                              int f, void* h, void* h_lo, hipStream_t s) {
   if (bf16in) {
-    if (h_lo) return gateup_bf16<true>(xp, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
-    return gateup_bf16<false>(xp, Wgate, Wup, offsets, E, d, f, h, nullptr, s);
+    if (h_lo) return gateup_bf16<true>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
+    return gateup_bf16<false>(xp, gather, Wgate, Wup, offsets, E, d, f, h, nullptr, s);
   }
+  if (gather) return hipErrorInvalidValue;  // the fp32 path reads copied rows
   dim3 grid(f / 64, R_max / 64 + E);
   gemm_f32_kernel<true><<<grid, 256, 0, s>>>(static_cast<const float*>(xp),
                                              static_cast<const float*>(Wgate),

@@ -69,19 +69,22 @@ hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, 
                              const int32_t* offsets, int cap, int renorm, int32_t* pos,
                              int32_t* src, float* w, void* x_perm, hipStream_t s);
 
-// Expert choice: row e*C + c takes token idx[e, c].
+// Expert choice: row e*C + c takes token idx[e, c] (src; the row copy into x_perm only when
+// x_perm is not nullptr).
 hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
                              const int32_t* idx, int32_t* src, void* x_perm, hipStream_t s);
 
 // Grouped GEMMs over expert-contiguous rows (group e = rows [offsets[e], offsets[e+1])).
-//   gate/up: h[r] = silu(x_perm[r] W_gate[e]) * (x_perm[r] W_up[e])  -> h [R, f]
+//   gate/up: h[r] = silu(A[r] W_gate[e]) * (A[r] W_up[e])  -> h [R, f]
+//     A[r] = xp[gather[r]] (bf16 only: the rows are gathered from x inside the GEMM's loads;
+//     every gather[r] * d must stay below 2^31) or xp[r] when gather is nullptr
 //   down:    o[r] = h[r] W_down[e]                                   -> o [R, d] fp32
 // With h_lo non-null (bf16 only) the gate/up epilogue also writes the bf16 rounding
 // residual of h. The down GEMM's group e uses W_down[e % EW] (EW = E normally; the
 // residual rows run as E more groups, EW = E, E' = 2E). R_max bounds the routed rows.
-hipError_t launch_gemm_gateup(int bf16, const void* xp, const void* Wgate, const void* Wup,
-                              const int32_t* offsets, int E, int R_max, int d, int f, void* h,
-                              void* h_lo, hipStream_t s);
+hipError_t launch_gemm_gateup(int bf16, const void* xp, const int32_t* gather, const void* Wgate,
+                              const void* Wup, const int32_t* offsets, int E, int R_max, int d,
+                              int f, void* h, void* h_lo, hipStream_t s);
 hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
                             int E, int EW, int R_max, int f, int d, float* o, hipStream_t s);
 

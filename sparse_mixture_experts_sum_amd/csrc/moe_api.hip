@@ -23,6 +23,7 @@ struct Layout {
          offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
          o_lo = 0, total = 0;
   int ngroups = 0;  // groups of the down projection: E, or 2E with the residual rows
+  bool xperm = false;  // rows copied into x_perm (else the gate/up GEMM gathers them from x)
 };
 
 int64_t ec_capacity(const moe_shape& s) {
@@ -114,7 +115,11 @@ Layout make_layout(const moe_shape& s) {
   L.offsets = take((size_t)(L.ngroups + 1) * 4);
   L.counts = take(E * 4);
   L.src = take(L.R * 4);
-  L.x_perm = take((size_t)L.R * d * eb);
+  // bf16: the gate/up GEMM loads its rows straight from x through src (per-lane addresses of
+  // its direct-to-LDS loads) while every row offset fits in 31 bits; otherwise (and in
+  // fp32) the permute copies the rows into x_perm
+  L.xperm = !(s.dtype == MOE_BF16 && T * d < (int64_t(1) << 31));
+  if (L.xperm) L.x_perm = take((size_t)L.R * d * eb);
   L.h = take((size_t)hrows * f * eb);
   if (resid) L.h_lo = L.h + (size_t)L.R * f * eb;
   L.o = take((size_t)hrows * d * 4);
@@ -309,7 +314,10 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
       *offset = L.pos;
       return MOE_OK;
     case MOE_WS_SRC: *offset = L.src; return MOE_OK;
-    case MOE_WS_XPERM: *offset = L.x_perm; return MOE_OK;
+    case MOE_WS_XPERM:
+      if (!L.xperm) return MOE_ERR_UNSUPPORTED;
+      *offset = L.x_perm;
+      return MOE_OK;
     case MOE_WS_H: *offset = L.h; return MOE_OK;
     case MOE_WS_O: *offset = L.o; return MOE_OK;
     default: return MOE_ERR_BAD_SHAPE;
@@ -380,20 +388,21 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, f, p, loss, z_loss, ws,
                   stream);
   if (st != MOE_OK) return st;
+  void* x_perm = L.xperm ? at<void>(ws, L.x_perm) : nullptr;  // nullptr: no row copies
+  const int32_t* src = at<int32_t>(ws, L.src);
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_PERMUTE,
                launch_permute_tc(x, eb, T, d, E, s.k, idx_b, at<int32_t>(ws, L.lrank),
                                  at<int32_t>(ws, L.base), offsets, tc_cap_limit(s), s.renormalize,
-                                 at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w_b,
-                                 at<void>(ws, L.x_perm), stream));
+                                 at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w_b, x_perm,
+                                 stream));
   } else {
     MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
-                                                    at<int32_t>(ws, L.src),
-                                                    at<void>(ws, L.x_perm), stream));
+                                                    at<int32_t>(ws, L.src), x_perm, stream));
   }
   MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
-             launch_gemm_gateup(bf, at<void>(ws, L.x_perm), W_gate, W_up, offsets, E, R, d, ff,
-                                at<void>(ws, L.h), h_lo, stream));
+             launch_gemm_gateup(bf, x_perm ? x_perm : x, x_perm ? nullptr : src, W_gate, W_up,
+                                offsets, E, R, d, ff, at<void>(ws, L.h), h_lo, stream));
   MOE_LAUNCH(MOE_STAGE_GEMM_DOWN,
              launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, L.ngroups, E,
                               L.h_lo ? 2 * R : R, ff, d, at<float>(ws, L.o), stream));

@@ -113,9 +113,19 @@ def test_workspace_offsets_are_inside(M):
     for mode in ("tc", "ec"):
         s = M.make_shape(1000, 256, 512, 8, 2, mode=mode)
         n = M.workspace_size(s)
-        for which in (M.WS_OFFSETS, M.WS_SRC, M.WS_XPERM, M.WS_H, M.WS_O):
+        for which in (M.WS_OFFSETS, M.WS_SRC, M.WS_H, M.WS_O):
             off = M.workspace_offset(s, which)
             assert 0 <= off < n and off % 256 == 0
+        # bf16 rows are gathered from x inside the GEMM: no copy to inspect; fp32 copies them
+        with pytest.raises(M.MoEError) as ei:
+            M.workspace_offset(s, M.WS_XPERM)
+        assert ei.value.status == 3
+        s32 = M.make_shape(1000, 256, 512, 8, 2, mode=mode, dtype="fp32")
+        off = M.workspace_offset(s32, M.WS_XPERM)
+        assert 0 <= off < M.workspace_size(s32) and off % 256 == 0
+    # the gathered layout needs no copy buffer: the bf16 workspace is smaller by R * d * 2
+    bf = M.workspace_size(M.make_shape(1000, 256, 512, 8, 2))
+    assert bf < M.workspace_size(M.make_shape(1000, 256, 512, 8, 2, dtype="fp32"))
     with pytest.raises(M.MoEError):
         M.workspace_offset(M.make_shape(1000, 256, 512, 8, 2, mode="ec"), M.WS_POS)
 

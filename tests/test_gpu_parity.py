@@ -245,8 +245,9 @@ def test_route_only_matches_forward(moe):
         assert torch.equal(r[key], fw[key]), key
 
 
-def test_dispatch_permutation_is_stable_bijection(moe):
-    w = W.custom("perm", T=900, d=64, f=64, E=5, k=3, seed=(42, 210))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_dispatch_permutation_is_stable_bijection(moe, dtype):
+    w = W.custom(f"perm_{dtype}", dtype=dtype, T=900, d=64, f=64, E=5, k=3, seed=(42, 210))
     inp = W.make_inputs(w)
     dev = PR.device_inputs(inp, w)
     out = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"], k=3)
@@ -269,8 +270,12 @@ def test_dispatch_permutation_is_stable_bijection(moe):
         rows = np.arange(offs[e], offs[e + 1])
         flat = [(t * w.k + j) for t in range(w.T) for j in range(w.k) if idx[t, j] == e]
         assert np.array_equal(pos.ravel()[flat], rows)
-    xperm = grab(moe.WS_XPERM, R * w.d, torch.bfloat16).view(R, w.d)
-    assert torch.equal(xperm, dev["x"].cpu()[torch.from_numpy(src).long()])
+    if dtype == "fp32":  # rows copied by the permute
+        xperm = grab(moe.WS_XPERM, R * w.d, torch.float32).view(R, w.d)
+        assert torch.equal(xperm, dev["x"].cpu()[torch.from_numpy(src).long()])
+    else:  # bf16: the gate/up GEMM gathers x[src] itself; there is no copy
+        with pytest.raises(moe.MoEError):
+            moe.workspace_offset(shape, moe.WS_XPERM)
 
 
 # the full-size case runs last: it is the slowest
