@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(ScanArgs a)
 // (flattened token order) is cap or more is dropped: pos = -1, weight 0, and when the
 // token lost a slot its kept weights are divided by their sum (renorm) — the capacity
 // routing of 机器学习基础系列——混合专家模型 (expert_capacity_routing). x_perm == nullptr:
-// slots and weights only (routing without the layer).
+// slots and weights only (bf16 layers, whose gate/up GEMM gathers the rows through src,
+// and routing without the layer).
 template <int EB>
 __global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict__ x, int T, int d,
                                                          int E, int k, const int32_t* __restrict__ idx,
