@@ -10,7 +10,7 @@ Prints one JSON line (rank 0). The timed steps run with no per-stage events; the
 per-kernel durations come from a second pass of the same steps in which the library
 records HIP events around each launch on the stream it launches on.
 
-Options select the other workloads (--config) and the token-choice variants at a
+Options select the other workloads (--workload NAME) and the token-choice variants at a
 workload's shape (--variant capacity | noisy | zloss).
 """
 from __future__ import annotations
@@ -26,6 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402  (seeded input generators only)
 
 METRIC = "MoE-layer tokens/sec + expert GEMM TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
@@ -116,7 +118,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload id (1-5); default 3")
+    ap.add_argument("--workload", default="mixtral_layer_skewed_top2_bf16",
+                    choices=sorted(W.WORKLOADS), help="workload (default: the Mixtral-size layer)")
     ap.add_argument("--cpu-sample", type=int, default=16384,
                     help="tokens the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--variant", default="plain", choices=("plain", "capacity", "noisy", "zloss"),
@@ -133,10 +136,9 @@ def main():
 
     import torch
     import sparse_mixture_experts_sum_amd as M
-    import workloads as W
 
     M.load_library()
-    w = W.CONFIGS[args.config]
+    w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = W.make_inputs(w)
@@ -254,7 +256,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(gu_tf, 1),
                      "peak": peak_tf, "unit": "TFLOP/s", "frac": round(gu_tf / peak_tf, 4),
                      "traffic": (gemm_traffic_from_profile()
-                                 if args.config == 3 and args.variant == "plain" else None)},
+                                 if w is W.MIXTRAL_LAYER and args.variant == "plain" else None)},
         "stages": st_out,
         "cpu_baseline": cpu,
     }

@@ -182,5 +182,5 @@ def test_route_only_matches_forward(moe):
 
 def test_capacity_mixtral_layer_sampled(moe):
     # the full Mixtral-shaped layer with a skewed router, capacity factor 1
-    w = W.CONFIGS[3]
+    w = W.MIXTRAL_LAYER
     run_capacity_case(moe, w, 1.0, sample=48)

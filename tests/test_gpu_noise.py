@@ -83,7 +83,7 @@ def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0):
 
 
 def test_noisy_mid_bf16(moe):
-    w = W.CONFIGS[2]
+    w = W.MID_BF16
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05))
 
 
@@ -128,7 +128,7 @@ def test_noisy_capacity_fp32_raw_gates(moe):
 
 
 def test_noisy_mixtral_layer_sampled(moe):
-    w = W.CONFIGS[3]
+    w = W.MIXTRAL_LAYER
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02), sample=32)
 
 

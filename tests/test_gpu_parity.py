@@ -98,20 +98,20 @@ def run_ec_case(M, w: W.Workload, inp=None):
 # the five workloads
 # ---------------------------------------------------------------------------------
 
-def test_config1_tiny_fp32(moe):
-    run_tc_case(moe, W.CONFIGS[1])
+def test_tiny_top2_fp32(moe):
+    run_tc_case(moe, W.TINY_FP32)
 
 
-def test_config2_mid_bf16(moe):
-    run_tc_case(moe, W.CONFIGS[2])
+def test_mid_top2_bf16(moe):
+    run_tc_case(moe, W.MID_BF16)
 
 
-def test_config4_fine_grained_e64_top4(moe):
-    run_tc_case(moe, W.CONFIGS[4])
+def test_fine_grained_e64_top4(moe):
+    run_tc_case(moe, W.FINE_GRAINED)
 
 
-def test_config5_expert_choice(moe):
-    run_ec_case(moe, W.CONFIGS[5])
+def test_expert_choice_e16(moe):
+    run_ec_case(moe, W.EXPERT_CHOICE)
 
 
 # ---------------------------------------------------------------------------------
@@ -279,10 +279,10 @@ def test_dispatch_permutation_is_stable_bijection(moe, dtype):
 
 
 # the full-size case runs last: it is the slowest
-def test_config3_mixtral_skewed_sampled(moe):
+def test_mixtral_layer_skewed_sampled(moe):
     """Full-size Mixtral layer with a skewed router bias: routing, counts and
     statistics on every token; outputs on a sample of tokens."""
-    w = W.CONFIGS[3]
+    w = W.MIXTRAL_LAYER
     out, inp = run_tc_case(moe, w, sample=96)
     counts = _np(out["counts"])
     assert counts.sum() == w.T * w.k

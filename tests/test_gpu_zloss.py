@@ -61,20 +61,20 @@ def run_z_case(M, w, route_only=False):
 
 
 def test_zloss_token_choice_mid(moe):
-    run_z_case(moe, W.CONFIGS[2])
+    run_z_case(moe, W.MID_BF16)
 
 
 def test_zloss_mixtral_skewed_full_size(moe):
     # all 16384 tokens of the Mixtral-shaped layer, router bias N(0, 1)
-    run_z_case(moe, W.CONFIGS[3], route_only=True)
+    run_z_case(moe, W.MIXTRAL_LAYER, route_only=True)
 
 
 def test_zloss_fine_grained_e64(moe):
-    run_z_case(moe, W.CONFIGS[4], route_only=True)
+    run_z_case(moe, W.FINE_GRAINED, route_only=True)
 
 
 def test_zloss_expert_choice(moe):
-    run_z_case(moe, W.CONFIGS[5])
+    run_z_case(moe, W.EXPERT_CHOICE)
 
 
 def test_zloss_with_capacity(moe):

@@ -26,16 +26,17 @@ def test_deterministic_and_distinct_seeds():
     assert not np.array_equal(a["x"], c["x"])
 
 
-def test_config_shapes_and_bf16_exact():
-    for cid in (1, 2, 4, 5):
-        w = W.CONFIGS[cid]
+def test_workload_shapes_and_bf16_exact():
+    for w in (W.TINY_FP32, W.MID_BF16, W.FINE_GRAINED, W.EXPERT_CHOICE):
         inp = W.make_inputs(W.Workload(**{**w.__dict__, "T": 64}), experts=False)
         assert inp["x"].shape == (64, w.d)
         assert inp["Wg"].shape == (w.d, w.E)
         if w.dtype == "bf16":
             assert np.array_equal(W.round_bf16(inp["x"]), inp["x"])
-    assert W.CONFIGS[5].capacity == 512
-    assert W.CONFIGS[3].rows == 32768
+    assert W.EXPERT_CHOICE.capacity == 512
+    assert W.MIXTRAL_LAYER.rows == 32768
+    assert sorted(W.WORKLOADS) == sorted(w.name for w in (W.TINY_FP32, W.MID_BF16, W.MIXTRAL_LAYER,
+                                                          W.FINE_GRAINED, W.EXPERT_CHOICE))
 
 
 def test_stds_roughly_right():

@@ -5,8 +5,8 @@ benchmark. It only draws random numbers and rounds them to the storage type;
 it holds none of the layer's arithmetic.
 
 Recipe (the same for every workload):
-  * one ``numpy.random.SeedSequence([42, config_id])`` per workload (42 is the
-    seed both NumPy pages use), spawned into six child streams in the order
+  * one ``numpy.random.SeedSequence(seed)`` per workload, ``seed = (42, i)`` with
+    ``i`` its place (1-5) in the list below (42 is the seed both NumPy pages use), spawned into six child streams in the order
     x, W_g, b, W_gate, W_up, W_down;
   * each tensor is ``standard_normal(dtype=float32)`` times its standard
     deviation; expert stacks are drawn expert by expert, one ``[rows, cols]``
@@ -16,12 +16,13 @@ Recipe (the same for every workload):
     that ``float32 -> bfloat16`` on the device and ``float32 -> float64`` in the
     oracle are both exact. The router bias stays float32.
 
-The five fixed workloads in ``CONFIGS`` take their layer shapes from the
-pages: the NumPy demo of "Mixture of Experts（MoE）の理論と実装" (1), the
-``MoEConfig`` of "Sparse Mixture of Experts(MoE) 아키텍처 심층 분석" (2), the
-Mixtral 8x7B dictionary of "机器学习基础系列——混合专家模型" (3), the 64
-fine-grained sub-experts with top-4 of "細粒度専門家分割がもたらす訓練コスト削減"
-(4), and the ``ExpertChoiceGating`` of the Korean page (5).
+The five fixed workloads (``WORKLOADS``, by name) take their layer shapes from
+the pages: the NumPy demo of "Mixture of Experts（MoE）の理論と実装"
+(``TINY_FP32``), the ``MoEConfig`` of "Sparse Mixture of Experts(MoE) 아키텍처
+심층 분석" (``MID_BF16``), the Mixtral 8x7B dictionary of "机器学习基础系列——混合
+专家模型" (``MIXTRAL_LAYER``), the 64 fine-grained sub-experts with top-4 of
+"細粒度専門家分割がもたらす訓練コスト削減" (``FINE_GRAINED``), and the
+``ExpertChoiceGating`` of the Korean page (``EXPERT_CHOICE``).
 """
 from __future__ import annotations
 
@@ -65,18 +66,19 @@ class Workload:
         return self.E * self.capacity if self.mode == "ec" else self.T * self.k
 
 
-CONFIGS = {
-    1: Workload("tiny_top2_fp32", "fp32", T=256, d=64, f=128, E=8, k=2,
-                x_std=0.5, wg_std=0.1, w_std=0.02, seed=(42, 1)),
-    2: Workload("mid_top2_bf16", "bf16", T=4096, d=1024, f=4096, E=8, k=2,
-                x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 2)),
-    3: Workload("mixtral_layer_skewed_top2_bf16", "bf16", T=16384, d=4096, f=14336, E=8, k=2,
-                x_std=1.0, wg_std=0.02, bias_std=1.0, w_std=0.01, seed=(42, 3)),
-    4: Workload("fine_grained_e64_top4_bf16", "bf16", T=8192, d=2048, f=1408, E=64, k=4,
-                x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 4)),
-    5: Workload("expert_choice_e16_cf1_bf16", "bf16", T=8192, d=1024, f=4096, E=16, k=1,
-                mode="ec", cf=1.0, x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 5)),
-}
+TINY_FP32 = Workload("tiny_top2_fp32", "fp32", T=256, d=64, f=128, E=8, k=2,
+                     x_std=0.5, wg_std=0.1, w_std=0.02, seed=(42, 1))
+MID_BF16 = Workload("mid_top2_bf16", "bf16", T=4096, d=1024, f=4096, E=8, k=2,
+                    x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 2))
+MIXTRAL_LAYER = Workload("mixtral_layer_skewed_top2_bf16", "bf16", T=16384, d=4096, f=14336,
+                         E=8, k=2, x_std=1.0, wg_std=0.02, bias_std=1.0, w_std=0.01,
+                         seed=(42, 3))
+FINE_GRAINED = Workload("fine_grained_e64_top4_bf16", "bf16", T=8192, d=2048, f=1408, E=64, k=4,
+                        x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 4))
+EXPERT_CHOICE = Workload("expert_choice_e16_cf1_bf16", "bf16", T=8192, d=1024, f=4096, E=16, k=1,
+                         mode="ec", cf=1.0, x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 5))
+
+WORKLOADS = {w.name: w for w in (TINY_FP32, MID_BF16, MIXTRAL_LAYER, FINE_GRAINED, EXPERT_CHOICE)}
 
 
 def custom(name: str = "custom", **kw) -> Workload:
