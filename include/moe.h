@@ -46,8 +46,10 @@
  *     workspaces differ.
  *
  * Limits: 1 <= E <= 64; token choice 1 <= k <= min(E, 8); d_model and d_ff multiples
- * of 64; 0 <= T and T * max(k, 1) < 2^31; expert choice needs 1 <= C <= T. x, weights,
- * y and the workspace must be 16-byte aligned.
+ * of 64 and at most 2^20; 0 <= T and T * max(k, 1) < 2^31; expert choice needs
+ * 1 <= C <= T and E * C < 2^31. fp32 layers take at most 64 * (65535 - E) routed rows
+ * (T * k, or E * C; more is MOE_ERR_UNSUPPORTED). x, weights, y and the workspace must be
+ * 16-byte aligned.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -74,6 +74,12 @@ moe_status check_shape(const moe_shape* s) {
     if (C < 1 || C > s->T) return MOE_ERR_BAD_SHAPE;
     if (C * (int64_t)s->E >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
   }
+  // the fp32 GEMMs launch one grid row per 64 routed rows (plus one per group): the grid's
+  // y extent bounds the rows they take
+  if (s->dtype == MOE_FP32) {
+    const int64_t rows = is_tc(s->mode) ? s->T * (int64_t)s->k : ec_capacity(*s) * s->E;
+    if (rows / 64 + s->E > 65535) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 

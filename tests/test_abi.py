@@ -73,6 +73,22 @@ def test_shape_validation(M):
     with pytest.raises(M.MoEError) as ei:
         M.workspace_size(s)
     assert ei.value.status == 3  # k > 8 unsupported
+    # d_model, d_ff at most 2^20
+    with pytest.raises(M.MoEError) as ei:
+        M.workspace_size(M.make_shape(64, 1 << 21, 256, 8, 2))
+    assert ei.value.status == 2
+    # fp32 layers: at most 64 * (65535 - E) routed rows; bf16 has no such limit
+    E, k = 8, 2
+    T_max = 64 * (65535 - E) // k
+    assert M.workspace_size(M.make_shape(T_max, 64, 64, E, k, dtype="fp32")) > 0
+    with pytest.raises(M.MoEError) as ei:
+        M.workspace_size(M.make_shape(T_max + 32, 64, 64, E, k, dtype="fp32"))
+    assert ei.value.status == 3
+    assert M.workspace_size(M.make_shape(T_max + 32, 64, 64, E, k, dtype="bf16")) > 0
+    s = M.make_shape(64 * 65535, 64, 64, 16, mode="ec", dtype="fp32", capacity_factor=1.0)
+    with pytest.raises(M.MoEError) as ei:
+        M.workspace_size(s)
+    assert ei.value.status == 3
 
 
 def test_capacity(M):
