@@ -105,11 +105,23 @@ __device__ inline void aux_stats_block(const int* cnt, const float* __restrict__
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = wave; i <= E; i += 16) {
     double v = 0.0;
-    if (i < E) {
-      if (blk_psum)
-        for (int b = lane; b < nblk; b += 64) v += (double)blk_psum[(size_t)b * E + i];
-    } else if (blk_zsum) {
-      for (int b = lane; b < nblk; b += 64) v += (double)blk_zsum[b];
+    const float* src = i < E ? blk_psum : blk_zsum;
+    const size_t stride = i < E ? (size_t)E : 1;
+    if (src) {
+      if (i < E) src += i;
+      // eight loads in flight per lane, then added in block order (the partials were
+      // just written by other CUs, so each load waits for memory)
+      for (int b0 = lane; b0 < nblk; b0 += 64 * 8) {
+        float x8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int b = b0 + 64 * u;
+          x8[u] = b < nblk ? src[(size_t)b * stride] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (b0 + 64 * u < nblk) v += (double)x8[u];
+      }
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
