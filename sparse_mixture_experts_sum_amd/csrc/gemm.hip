@@ -21,9 +21,8 @@
 //   * 256 x 256 tiles: four waves (one per SIMD), each a 128 x 128 block with its 256
 //     accumulators in AGPRs, software-pipelined (PipeStep): the MFMAs of one stage run
 //     while the fragments of the next are read and the ring is refilled, one barrier
-//     per stage, and the stages stream across tiles (pipe_stream). Alternatives kept
-//     behind kWaves256 = 8: two waves per SIMD in a ping-pong schedule (pp_step).
-//     Smaller tiles (256 x 128, 256 x 64) use the plain ring (ring_step);
+//     per stage, and the stages stream across tiles (pipe_stream). Smaller tiles
+//     (256 x 128, 256 x 64) use the plain ring (ring_step);
 //   * gate and up tiles share the A tile; the SwiGLU epilogue silu(g) * u runs in
 //     registers and writes h in bf16 (plus its bf16 residual when asked: SPLIT). The
 //     down projection writes o in fp32; group e takes weight matrix e % EW, so that the
@@ -35,7 +34,6 @@
 
 namespace {
 
-constexpr int kWaves256 = 4;  // waves per 256 x 256 tile: 4 = pipelined (1 per SIMD), 8 = ping-pong
 constexpr int kBK = 32;       // K per LDS stage
 constexpr int kStages = 4;    // LDS ring stages; kStages - 1 are in flight
 
@@ -231,80 +229,6 @@ __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ri
   }
 }
 
-// Ping-pong K stage for two waves per SIMD. The two waves of a SIMD run the same stage
-// half a stage apart: while one issues its MFMAs (with its refill loads of the ring
-// spread between them), the other reads its fragments of the stage from LDS, and at
-// the next barrier they swap. Every wave passes two barriers per stage; the "second"
-// wave of each SIMD passes one extra barrier at the start of a tile and the first one
-// extra at the end, which sets the offset. Correctness (for any split of the waves into
-// the two roles):
-//  - before any wave reads stage kt, every wave has waited for its own loads of stage
-//    kt: first waves just before their read barrier, second waves before the barrier
-//    that ends their reads of stage kt-1 (which is the first waves' read barrier of kt);
-//  - a wave refills the buffer of stage kt-1 (with stage kt+3) only in its MFMA phase
-//    of stage kt, which follows the barrier that ends every wave's reads of stage kt-1
-//    (reads are complete at lgkmcnt(0) before that barrier); MFMAs read registers only.
-template <class G, bool SWIGLU, bool SPLIT, bool SECOND, int J, bool FULL>
-__device__ __forceinline__ void pp_step(int kt, int nk_total,
-                                        char* const (&ring)[G::STAGES],
-                                        const StageLoader<G, SWIGLU, SPLIT>& ld,
-                                        const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
-                                        f32x16 (&acc)[G::NBW][G::MB]) {
-  constexpr int AHEAD = G::STAGES - 1;
-  static_assert(AHEAD >= 2 && AHEAD <= 3, "ring depth");
-  __builtin_amdgcn_sched_barrier(0);  // the wait stays after the previous MFMA phase
-  if constexpr (!SECOND) {  // own loads of stage kt (kt .. kt + AHEAD - 1 may be in flight)
-    if constexpr (FULL) wait_vmcnt<(AHEAD - 1) * G::LPS>();
-    else wait_stages<G::LPS>(min(AHEAD - 1, nk_total - 1 - kt));
-  }
-  sync_point();
-  const char* st = ring[J];
-  bf16x8 af[G::SUB][G::MB], bfr[G::SUB][G::NBW];
-#pragma unroll
-  for (int s = 0; s < G::SUB; ++s) {
-#pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
-      af[s][mb] = *reinterpret_cast<const bf16x8*>(st + (a_frag[mb] ^ (32 * s)));
-#pragma unroll
-    for (int nb = 0; nb < G::NBW; ++nb) {
-      const char* bp = st + b_frag[nb] + 16 * s * G::B_ROW;
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bp);
-      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bp + 4 * G::B_ROW));
-      const s16x8 v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      bfr[s][nb] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  wait_lgkmcnt0();
-  if constexpr (SECOND) {  // own loads of stage kt + 1 (kt + 1 .. kt + AHEAD - 1 may be in
-                           // flight; stage kt + AHEAD is issued below)
-    if constexpr (FULL) wait_vmcnt<(AHEAD - 2) * G::LPS>();
-    else wait_stages<G::LPS>(max(0, min(AHEAD - 2, nk_total - 2 - kt)));
-  }
-  sync_point();
-  // MFMAs with the refill of stage kt + AHEAD spread between them: one load after every
-  // PER MFMAs keeps each wave's loads from queueing behind each other in a burst
-  constexpr int NM = G::SUB * G::NBW * G::MB;
-  constexpr int PER = NM / G::LPS;
-  static_assert(PER >= 1 && PER * G::LPS == NM, "loads per MFMA group");
-  const bool refill = FULL || kt + AHEAD < nk_total;
-  char* const dst = ring[(J + AHEAD) % G::STAGES];
-#define MOE_MFMA(I)                                                                          \
-  {                                                                                          \
-    constexpr int s = (I) / (G::NBW * G::MB), nb = (I) / G::MB % G::NBW, mb = (I) % G::MB;   \
-    acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][nb], af[s][mb], acc[nb][mb], \
-                                                          0, 0, 0);                          \
-    if constexpr ((I) % PER == PER - 1) {                                                    \
-      if (refill) ld.issue_one((I) / PER, kt + AHEAD, dst);                                  \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-    }                                                                                        \
-  }
-  static_assert(NM == 16, "MFMA phase is written out for 16 MFMAs");
-  MOE_MFMA(0) MOE_MFMA(1) MOE_MFMA(2) MOE_MFMA(3) MOE_MFMA(4) MOE_MFMA(5) MOE_MFMA(6)
-  MOE_MFMA(7) MOE_MFMA(8) MOE_MFMA(9) MOE_MFMA(10) MOE_MFMA(11) MOE_MFMA(12) MOE_MFMA(13)
-  MOE_MFMA(14) MOE_MFMA(15)
-#undef MOE_MFMA
-}
-
 // Fragments of one K stage for one wave: A as SUB x MB 8-element rows, B as the two
 // transposed 4-element halves of SUB x NBW fragments.
 template <class G>
@@ -391,32 +315,22 @@ static __device__ __forceinline__ void run(int n_after, bool more_, bool refill_
 }
 };
 
-// The K loop of one tile. ROLE 0: every wave runs ring_step; ROLE 1 / 2: the first /
-// second wave of a SIMD in the ping-pong schedule (compiled separately, so that each
-// role's waits are fixed at compile time).
-template <class G, bool SWIGLU, bool SPLIT, int ROLE>
+// The K loop of one tile through the plain ring (ring_step).
+template <class G, bool SWIGLU, bool SPLIT>
 __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAGES],
                                        const StageLoader<G, SWIGLU, SPLIT>& ld,
                                        const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
                                        f32x16 (&acc)[G::NBW][G::MB]) {
   constexpr int S = G::STAGES;
   int kt = 0;
-#define MOE_STEP(J, FULL, KT)                                                                 \
-  if constexpr (ROLE == 0)                                                                    \
-    ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc);        \
-  else                                                                                        \
-    pp_step<G, SWIGLU, SPLIT, ROLE == 2, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
-  // Prologue: stages 0 .. S-2 in flight; the second ping-pong waves then wait for their
-  // stage 0 and pass their extra barrier. The main loop (every step refills) sits in the
+#define MOE_STEP(J, FULL, KT) \
+  ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
+  // Prologue: stages 0 .. S-2 in flight. The main loop (every step refills) sits in the
   // same branch as an unconditional prologue, so that the compiler sees the same loads
   // in flight on every path into it. At most 2 * S - 2 stages remain after it.
   if (nk_total >= 2 * S - 1) {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) ld.issue(i, ring[i]);
-    if constexpr (ROLE == 2) {
-      wait_vmcnt<(S - 2) * G::LPS>();
-      sync_point();
-    }
     for (; kt + 2 * S - 1 <= nk_total; kt += S) {
       MOE_STEP(0, true, kt);
       MOE_STEP(1, true, kt + 1);
@@ -427,10 +341,6 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
       if (i < nk_total) ld.issue(i, ring[i]);
-    if constexpr (ROLE == 2) {
-      wait_stages<G::LPS>(min(S - 2, nk_total - 1));
-      sync_point();
-    }
   }
   if (kt < nk_total) { MOE_STEP(0, false, kt); }
   if (kt + 1 < nk_total) { MOE_STEP(1 % S, false, kt + 1); }
@@ -443,10 +353,6 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
     if (kt + 5 < nk_total) { MOE_STEP(5 % S, false, kt + 5); }
   }
 #undef MOE_STEP
-  // Every load of the tile has landed by now (each role's last wait was for its last
-  // stage); saying so keeps the compiler's load tracking exact into the next tile.
-  if constexpr (ROLE != 0) wait_vmcnt<0>();
-  if constexpr (ROLE == 1) sync_point();  // the first waves' extra barrier
 }
 
 // Kernel arguments shared by the tile helpers.
@@ -777,23 +683,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
   for (int i = 0; i < G::STAGES; ++i) ring[i] = ring4[i];
   // the wave index is uniform: keep it scalar so LDS destinations stay plain offsets
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
-  // ping-pong roles for two waves per SIMD: the second wave (by index) on each SIMD
-  constexpr bool PP = NW == 8;
   // one wave per SIMD on 256 x 256 tiles: the software-pipelined loop
   constexpr bool PIPE = NW == 4 && BM == 256 && BNL == 256;
-  bool second = false;
-  if constexpr (PP) {
-    __shared__ int simd_of[NW];
-    // HW_ID bits 5:4 hold the SIMD the wave runs on
-    if (lane == 0) simd_of[wave] = (int)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
-    __syncthreads();
-    int rank = 0;
-    for (int w = 0; w < wave; ++w) rank += simd_of[w] == simd_of[wave];
-    second = __builtin_amdgcn_readfirstlane(rank & 1) != 0;
-  }
 
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
@@ -827,19 +720,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     zero_acc<G>(acc);
 
     // (the pipelined layout falls back to the plain ring when its stream does not apply)
-    if constexpr (!PP) k_loop<G, SWIGLU, SPLIT, 0>(nk_total, ring, ld, a_frag, b_frag, acc);
-    else if (second) k_loop<G, SWIGLU, SPLIT, 2>(nk_total, ring, ld, a_frag, b_frag, acc);
-    else k_loop<G, SWIGLU, SPLIT, 1>(nk_total, ring, ld, a_frag, b_frag, acc);
+    k_loop<G, SWIGLU, SPLIT>(nk_total, ring, ld, a_frag, b_frag, acc);
 
     store_tile<G, SWIGLU, SPLIT>(args, t, ln, wm, wn, acc);
-    if constexpr (!PP) {
-      // stores retired and every wave past its last stage read before the next
-      // tile's loads refill the ring
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-    }
-    // (ping-pong: every wave's reads of this tile ended before the first waves' extra
-    // barrier, which precedes both roles' next refills)
+    // stores retired and every wave past its last stage read before the next tile's
+    // loads refill the ring
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
   }
 }
 
@@ -932,7 +819,7 @@ hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate,
                        const int32_t* offsets, int E, int d, int f, void* h, void* h_lo,
                        hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT, kWaves256>(xp, gather, Wgate, Wup, offsets, E, E, d,
+    return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d,
                                                          f, h, h_lo, s);
   return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d, f, h, h_lo,
                                                s);
@@ -941,7 +828,7 @@ hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate,
 hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int EW,
                      int f, int d, float* o, hipStream_t s) {
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, false, kWaves256>(h, nullptr, Wdown, nullptr, offsets, E, EW,
+    return launch_bf16<256, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW,
                                                           f, d, o, nullptr, s);
   if (d % 128 == 0)
     return launch_bf16<256, 128, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d,
