@@ -254,7 +254,14 @@ def route_ec(x, Wg, b, cf):
     tokens of largest column-softmax score, lower token first among equals;
     idx [E,C] lists each expert's tokens in ascending token order and score
     [E,C] their scores. Returns (idx, score, S [T,E], logits [T,E])."""
-    s = router_logits(x, Wg, b)
+    return route_ec_logits(router_logits(x, Wg, b), cf)
+
+
+def route_ec_logits(s, cf):
+    """The part of ``route_ec`` after the router projection, from the logits s [T,E]
+    (so that a caller holding the logits of repeated rows need not hold the rows).
+    Returns (idx, score, S [T,E], logits [T,E])."""
+    s = _f64(s)
     S = softmax_cols(s)
     T, E = S.shape
     C = capacity(T, E, cf)

@@ -1,5 +1,5 @@
-"""GPU parity at element offsets past 2^31: a bf16 token-choice layer whose input x holds
-more than 2^31 elements (T * d_model >= 2^31).
+"""GPU parity at element offsets past 2^31: bf16 layers (token choice and expert
+choice) whose input x holds more than 2^31 elements (T * d_model >= 2^31).
 
 There the rows are no longer gathered from x inside the gate/up GEMM (its per-lane row
 offsets are 32-bit): the permute copies them into the workspace's x_perm and the GEMM
@@ -11,7 +11,10 @@ shift maps a row onto an equal one). Token t's routing and output are those of b
 row t mod P, which the oracle evaluates once for the block: routing, weights and
 probabilities are checked on every token, counts and statistics over all tokens, the
 output on a sample (including tokens past the 2^31-element boundary and the last
-token), and on the device every output row against its block row's.
+token), and on the device every output row against its block row's. In expert choice
+the repeated rows tie at each expert's capacity boundary, which the lower token index
+breaks; outputs are compared among tokens with the same row and the same choosing
+experts.
 """
 from __future__ import annotations
 
@@ -97,3 +100,67 @@ def test_bf16_input_past_2_31_elements(moe):
     assert worst <= 1e-4 * rms, f"rows differ from their block rows by {worst / rms:.3e} rms"
     _say(f"  ok: y err {err:.3e}, periodic deviation {worst / rms:.3e} rms, "
          f"exempt tokens {int(exempt.sum())}")
+
+
+def test_bf16_expert_choice_input_past_2_31_elements(moe):
+    # expert choice at the same size: the permute copies the chosen rows into x_perm and
+    # the gate/up GEMM reads them contiguously while writing h and its bf16 residual
+    w = W.custom("large_x_ec_bf16", dtype="bf16", T=(1 << 18) + 1000, d=8192, f=128, E=8, k=1,
+                 mode="ec", cf=1.0, x_std=1.0, wg_std=0.02, w_std=0.02, seed=(42, 402))
+    C = w.capacity
+    _say(w, "C", C, "x repeats", P, "seeded rows")
+    blk = W.make_inputs(replace(w, T=P))
+    dev = PR.device_inputs(blk, w)
+    x = dev["x"].repeat(-(-w.T // P), 1)[: w.T].contiguous()
+    torch.cuda.synchronize()
+    out = moe.moe_forward(x, dev["Wg"], None, dev["Wgate"], dev["Wup"], dev["Wdown"], mode="ec",
+                          capacity_factor=w.cf, want_stats=False)
+    torch.cuda.synchronize()
+    _say("  forward done")
+    assert moe.workspace_offset(out["shape"], moe.WS_XPERM) > 0
+
+    src = np.arange(w.T) % P
+    idx_r, score_r, S, s = O.route_ec_logits(O.router_logits(blk["x"], blk["Wg"], None)[src], w.cf)
+    ref = {"idx": idx_r, "w": score_r, "probs": S, "logits": s}
+    idx = out["idx"].cpu().numpy().astype(np.int64)
+    PR.check_ec_routing(idx, out["w"].cpu().numpy(), ref, C)
+    assert np.all(out["counts"].cpu().numpy() == C)
+    np.testing.assert_allclose(out["probs"].cpu().numpy(), S, rtol=1e-4, atol=1e-9)
+
+    # outputs on a sample, with the device's choice of tokens
+    chose = np.zeros((w.T, w.E), dtype=bool)
+    for e in range(w.E):
+        chose[idx[e], e] = True
+    edge = (1 << 31) // w.d
+    rng = np.random.default_rng(12)
+    toks = np.unique(np.concatenate([rng.choice(w.T, size=40, replace=False),
+                                     np.arange(edge - 4, edge + 4), [0, w.T - 1],
+                                     idx[:, -1]]))
+    y_ref = np.zeros((len(toks), w.d))
+    for i, t in enumerate(toks):
+        for e in np.flatnonzero(chose[t]):
+            y_ref[i] += S[t, e] * O.expert_ffn(blk["x"][src[t]][None], blk["Wgate"][e],
+                                               blk["Wup"][e], blk["Wdown"][e])[0]
+    y = out["y"]
+    err = PR.check_y(y[torch.from_numpy(toks).to(y.device)].cpu().numpy(), y_ref, w.dtype)
+
+    # every token: the same block row chosen by the same experts gives the same output,
+    # and a token no expert chose gives 0
+    bits = torch.from_numpy((chose * (1 << np.arange(w.E))).sum(1)).to(y.device)
+    key = torch.from_numpy(src).to(y.device) * (1 << w.E) + bits
+    uniq, inv = torch.unique(key, return_inverse=True)
+    first = torch.full((len(uniq),), w.T, dtype=torch.int64, device=y.device)
+    first.scatter_reduce_(0, inv, torch.arange(w.T, device=y.device), reduce="amin")
+    rep = first[inv]
+    rms = y[torch.from_numpy(toks).to(y.device)].pow(2).mean().sqrt().item()
+    worst, nz = 0.0, 0.0
+    for c0 in range(0, w.T, 8192):
+        c1 = min(w.T, c0 + 8192)
+        worst = max(worst, (y[c0:c1] - y[rep[c0:c1]]).abs().max().item())
+        none = bits[c0:c1] == 0
+        if bool(none.any()):
+            nz = max(nz, y[c0:c1][none].abs().max().item())
+    assert nz == 0.0, "a token no expert chose has a nonzero output"
+    assert worst <= 1e-4 * rms, f"equal rows and choices differ by {worst / rms:.3e} rms"
+    _say(f"  ok: y err {err:.3e}, deviation within groups {worst / rms:.3e} rms, "
+         f"tokens no expert chose {int((bits == 0).sum())}")
