@@ -9,7 +9,9 @@
 //   * persistent workgroups (one per CU); all XCDs walk the experts in the same order,
 //     XCD x taking the x-th eighth of each expert's tiles listed N-tile-major, so that
 //     an XCD's CUs share weight columns in its L2 and the XCDs share the expert's rows
-//     in the memory-side cache (locate_tile);
+//     in the memory-side cache; when every expert has few tiles, each XCD takes a
+//     contiguous run of experts instead, so that its CUs share operands in its L2
+//     (TileMap);
 //   * v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand, so that
 //     each lane's 16 accumulators are 4 runs of 4 consecutive output columns of one row
 //     (8- and 16-byte stores);
@@ -373,22 +375,85 @@ struct TileCoord {
   int e, row0, rows, n0;
 };
 
-// Tile i of XCD xcd's share. Experts are processed one after another by all XCDs
-// together: XCD x takes the x-th eighth of each expert's tiles listed N-tile-major, i.e.
-// mostly its own slice of the expert's weight columns, for all of the expert's rows.
+// How the tiles are dealt to the eight XCDs (each XCD runs 32 at a time, one per CU;
+// every group's tiles are listed N-tile-major).
+//  - Split (groups with many tiles): the groups are processed one after another by all
+//    XCDs together, XCD x taking the x-th eighth of each group's list, i.e. mostly its
+//    own slice of the group's weight columns, for all of the group's rows.
+//  - Contiguous (every group small: split would give each XCD under 2 tiles of a group,
+//    or under 6 when the rows are gathered from x): the groups' lists are concatenated,
+//    groups that share a weight matrix next to each other, and XCD x takes the x-th
+//    eighth of the whole list. The tiles an XCD runs together then come from one or a few
+//    groups and share their weight columns and rows in the XCD's L2; split, they would
+//    come from a different group each. (Measured: contiguous gains where split leaves
+//    an XCD one tile per group, and on gathered rows up to about 6 per group; with plain
+//    rows at 2-3 tiles per group, and beyond 6 with gathered rows, split was faster.)
+// Both keep the XCDs' tile counts within one of each other.
+constexpr int kXcds = 8;
+constexpr int kContigTiles = 16;        // max tiles per group for contiguous, plain rows
+constexpr int kContigGatherTiles = 48;  // the same, rows gathered from x
+struct TileMap {
+  int NT, xcd, E, EW;
+  bool contiguous;
+  int base;      // contiguous: this XCD's first tile in the whole list
+  int my_total;  // tiles of this XCD
+};
+
 template <int BM>
-__device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, int NT,
-                                                 int bn_out, int xcd) {
-  int e = 0, acc_i = 0, p = 0, mte = 1;
-  for (;; ++e) {
-    mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-    const long long pe = (long long)mte * NT;
-    const int plo = (int)((pe * xcd) >> 3), phi = (int)((pe * (xcd + 1)) >> 3);
-    if (i < acc_i + (phi - plo)) {
-      p = plo + (i - acc_i);
-      break;
+__device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int EW, int NT,
+                                                 int xcd, bool gathered) {
+  TileMap m;
+  m.NT = NT;
+  m.xcd = xcd;
+  m.E = E;
+  m.EW = EW;
+  long long total = 0, maxpe = 0;
+  int split_total = 0;
+  for (int e = 0; e < E; ++e) {
+    const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
+    total += pe;
+    maxpe = pe > maxpe ? pe : maxpe;
+    split_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
+  }
+  // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
+  m.contiguous = maxpe < (gathered ? kContigGatherTiles : kContigTiles) && E % EW == 0;
+  m.base = m.contiguous ? (int)((total * xcd) >> 3) : 0;
+  m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base : split_total;
+  return m;
+}
+
+// Tile i of this XCD's share (see TileMap).
+template <int BM>
+__device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, const TileMap& m,
+                                                 int bn_out) {
+  int e = 0, p = 0, mte = 1;
+  if (!m.contiguous) {
+    int acc_i = 0;
+    for (;; ++e) {
+      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      const long long pe = (long long)mte * m.NT;
+      const int plo = (int)((pe * m.xcd) >> 3), phi = (int)((pe * (m.xcd + 1)) >> 3);
+      if (i < acc_i + (phi - plo)) {
+        p = plo + (i - acc_i);
+        break;
+      }
+      acc_i += phi - plo;
     }
-    acc_i += phi - plo;
+  } else {
+    // list position j holds group (j mod G) * EW + j / G: the G groups of weight matrix w
+    // (w, w + EW, ...) sit next to each other
+    const int G = m.E / m.EW, gi = m.base + i;
+    int acc_i = 0;
+    for (int j = 0;; ++j) {
+      e = (j % G) * m.EW + j / G;
+      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+      const int pe = mte * m.NT;
+      if (gi < acc_i + pe) {
+        p = gi - acc_i;
+        break;
+      }
+      acc_i += pe;
+    }
   }
   const int nt = p / mte, mtl = p - nt * mte;
   TileCoord t;
@@ -597,15 +662,16 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
 // that stage s of every tile sits in ring buffer s % S. (The next tile's fragments are
 // read after the epilogue: holding them through it would leave too few registers.)
 template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL>
-__device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my_total, int nslot,
-                                            int NT, int xcd, int wave, int wm, int wn,
+__device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const TileMap& tm,
+                                            int nslot, int wave, int wm, int wn,
                                             int nk, int nk_total, char* const (&ring)[G::STAGES]) {
   constexpr int S = G::STAGES;
   static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
   int ln = fresh_lane();
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-  TileCoord t = locate_tile<BM>(first, a.offsets, NT, G::BN_OUT, xcd);
+  const int my_total = tm.my_total;
+  TileCoord t = locate_tile<BM>(first, a.offsets, tm, G::BN_OUT);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
   StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk, gv);
@@ -631,7 +697,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, int my
     // bounds)
     const int inext = i + nslot;
     const bool has_next = inext < my_total;
-    const TileCoord tn = has_next ? locate_tile<BM>(inext, a.offsets, NT, G::BN_OUT, xcd) : t;
+    const TileCoord tn = has_next ? locate_tile<BM>(inext, a.offsets, tm, G::BN_OUT) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
@@ -689,13 +755,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr bool PIPE = NW == 4 && BM == 256 && BNL == 256;
 
   const int NT = N / G::BN_OUT;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
-  // this XCD's number of tiles (the order is described at locate_tile)
-  int my_total = 0;
-  for (int e = 0; e < E; ++e) {
-    const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
-    my_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
-  }
+  const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
+  // this XCD's tiles (the order is described at TileMap)
+  const TileMap tm = make_tile_map<BM>(offsets, E, EW, NT, xcd, gather != nullptr);
+  const int my_total = tm.my_total;
   const int nk = K / G::BK;
   const int nk_total = nk;
 
@@ -703,8 +766,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
       if (slot < my_total)
-        pipe_stream<G, SWIGLU, SPLIT, BM, BNL>(args, slot, my_total, nslot, NT, xcd, wave, wm, wn,
-                                               nk, nk_total, ring);
+        pipe_stream<G, SWIGLU, SPLIT, BM, BNL>(args, slot, tm, nslot, wave, wm, wn, nk, nk_total,
+                                               ring);
       return;
     }
   }
@@ -712,7 +775,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int ln = fresh_lane();
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-    const TileCoord t = locate_tile<BM>(i, offsets, NT, G::BN_OUT, xcd);
+    const TileCoord t = locate_tile<BM>(i, offsets, tm, G::BN_OUT);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
     const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, gv);
