@@ -192,7 +192,8 @@ __device__ __forceinline__ void wait_stages(int n) {
 // ahead, then SUB x (fragment reads + MB x NBW MFMAs). J = kt % STAGES is a template
 // argument so that every LDS access names one of the stage arrays; FULL steps always
 // refill, so that the compiler sees the same number of loads in flight on every path.
-template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL>
+// (TAG: see k_loop)
+template <class G, bool SWIGLU, bool SPLIT, int J, bool FULL, int TAG>
 __device__ __forceinline__ void ring_step(int kt, int nk_total, char* const (&ring)[G::STAGES],
                                           const StageLoader<G, SWIGLU, SPLIT>& ld,
                                           const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
@@ -318,7 +319,10 @@ static __device__ __forceinline__ void run(int n_after, bool more_, bool refill_
 };
 
 // The K loop of one tile through the plain ring (ring_step).
-template <class G, bool SWIGLU, bool SPLIT>
+// (TAG separates the instantiations of different kernels: hipcc's host pass rejects a
+// second call of a function template with these array-reference parameters from
+// another kernel with the same arguments)
+template <class G, bool SWIGLU, bool SPLIT, int TAG>
 __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAGES],
                                        const StageLoader<G, SWIGLU, SPLIT>& ld,
                                        const int (&a_frag)[G::MB], const int (&b_frag)[G::NBW],
@@ -326,7 +330,7 @@ __device__ __forceinline__ void k_loop(int nk_total, char* const (&ring)[G::STAG
   constexpr int S = G::STAGES;
   int kt = 0;
 #define MOE_STEP(J, FULL, KT) \
-  ring_step<G, SWIGLU, SPLIT, J, FULL>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
+  ring_step<G, SWIGLU, SPLIT, J, FULL, TAG>(KT, nk_total, ring, ld, a_frag, b_frag, acc)
   // Prologue: stages 0 .. S-2 in flight. The main loop (every step refills) sits in the
   // same branch as an unconditional prologue, so that the compiler sees the same loads
   // in flight on every path into it. At most 2 * S - 2 stages remain after it.
@@ -399,7 +403,9 @@ struct TileMap {
   int my_total;  // tiles of this XCD
 };
 
-template <int BM>
+// CONTIG_OK: the shape allows the contiguous order (a group of one M-tile has NT tiles,
+// so NT at or above the threshold rules it out; the launch picks the instantiation).
+template <int BM, bool CONTIG_OK>
 __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int EW, int NT,
                                                  int xcd, bool gathered) {
   TileMap m;
@@ -411,23 +417,27 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
   int split_total = 0;
   for (int e = 0; e < E; ++e) {
     const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
-    total += pe;
-    maxpe = pe > maxpe ? pe : maxpe;
+    if constexpr (CONTIG_OK) {
+      total += pe;
+      maxpe = pe > maxpe ? pe : maxpe;
+    }
     split_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
   }
   // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
-  m.contiguous = maxpe < (gathered ? kContigGatherTiles : kContigTiles) && E % EW == 0;
+  m.contiguous =
+      CONTIG_OK && maxpe < (gathered ? kContigGatherTiles : kContigTiles) && E % EW == 0;
   m.base = m.contiguous ? (int)((total * xcd) >> 3) : 0;
   m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base : split_total;
   return m;
 }
 
-// Tile i of this XCD's share (see TileMap).
-template <int BM>
+// Tile i of this XCD's share (see TileMap); CONTIG = m.contiguous, fixed at compile time
+// so that the split order's stream carries no code of the other.
+template <int BM, bool CONTIG>
 __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, const TileMap& m,
                                                  int bn_out) {
   int e = 0, p = 0, mte = 1;
-  if (!m.contiguous) {
+  if constexpr (!CONTIG) {
     int acc_i = 0;
     for (;; ++e) {
       mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
@@ -661,7 +671,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
 // and the next tile only waits for its stage 0 to be read. Needs nk_total % S == 0, so
 // that stage s of every tile sits in ring buffer s % S. (The next tile's fragments are
 // read after the epilogue: holding them through it would leave too few registers.)
-template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL>
+// (TAG: see k_loop)
+template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL, bool CONTIG, int TAG>
 __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const TileMap& tm,
                                             int nslot, int wave, int wm, int wn,
                                             int nk, int nk_total, char* const (&ring)[G::STAGES]) {
@@ -671,7 +682,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const 
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
   const int my_total = tm.my_total;
-  TileCoord t = locate_tile<BM>(first, a.offsets, tm, G::BN_OUT);
+  TileCoord t = locate_tile<BM, CONTIG>(first, a.offsets, tm, G::BN_OUT);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
   StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk, gv);
@@ -697,7 +708,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const 
     // bounds)
     const int inext = i + nslot;
     const bool has_next = inext < my_total;
-    const TileCoord tn = has_next ? locate_tile<BM>(inext, a.offsets, tm, G::BN_OUT) : t;
+    const TileCoord tn = has_next ? locate_tile<BM, CONTIG>(inext, a.offsets, tm, G::BN_OUT) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
@@ -732,7 +743,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const 
   wait_vmcnt<0>();
 }
 
-template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
+template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
   // this XCD's tiles (the order is described at TileMap)
-  const TileMap tm = make_tile_map<BM>(offsets, E, EW, NT, xcd, gather != nullptr);
+  const TileMap tm = make_tile_map<BM, CONTIG_OK>(offsets, E, EW, NT, xcd, gather != nullptr);
   const int my_total = tm.my_total;
   const int nk = K / G::BK;
   const int nk_total = nk;
@@ -765,9 +776,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, EW, out, out2};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
-      if (slot < my_total)
-        pipe_stream<G, SWIGLU, SPLIT, BM, BNL>(args, slot, tm, nslot, wave, wm, wn, nk, nk_total,
-                                               ring);
+      if (slot < my_total) {
+        if (CONTIG_OK && tm.contiguous)
+          pipe_stream<G, SWIGLU, SPLIT, BM, BNL, CONTIG_OK, CONTIG_OK>(args, slot, tm, nslot, wave,
+                                                                       wm, wn, nk, nk_total, ring);
+        else
+          pipe_stream<G, SWIGLU, SPLIT, BM, BNL, false, CONTIG_OK>(args, slot, tm, nslot, wave, wm,
+                                                                   wn, nk, nk_total, ring);
+      }
       return;
     }
   }
@@ -775,7 +791,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int ln = fresh_lane();
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-    const TileCoord t = locate_tile<BM>(i, offsets, tm, G::BN_OUT);
+    const TileCoord t = CONTIG_OK && tm.contiguous
+                            ? locate_tile<BM, CONTIG_OK>(i, offsets, tm, G::BN_OUT)
+                            : locate_tile<BM, false>(i, offsets, tm, G::BN_OUT);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
     const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, gv);
@@ -783,7 +801,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     zero_acc<G>(acc);
 
     // (the pipelined layout falls back to the plain ring when its stream does not apply)
-    k_loop<G, SWIGLU, SPLIT>(nk_total, ring, ld, a_frag, b_frag, acc);
+    k_loop<G, SWIGLU, SPLIT, CONTIG_OK>(nk_total, ring, ld, a_frag, b_frag, acc);
 
     store_tile<G, SWIGLU, SPLIT>(args, t, ln, wm, wn, acc);
     // stores retired and every wave past its last stage read before the next tile's
@@ -871,9 +889,17 @@ hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, con
                        const int32_t* offsets, int E, int EW, int K, int N, void* out, void* out2,
                        hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
-  gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW><<<grid, 64 * NW, 0, s>>>(
-      static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-      static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
+  // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
+  // only below the threshold
+  const int NT = N / (SWIGLU ? BNL / 2 : BNL);
+  if (NT < (gather ? kContigGatherTiles : kContigTiles))
+    gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, true><<<grid, 64 * NW, 0, s>>>(
+        static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
+  else
+    gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, false><<<grid, 64 * NW, 0, s>>>(
+        static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
   return hipGetLastError();
 }
 
