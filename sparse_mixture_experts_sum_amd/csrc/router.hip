@@ -121,13 +121,56 @@ __device__ __forceinline__ void stage_wg_transposed(const TI* __restrict__ src, 
   }
 }
 
+// bf16 with E a multiple of 8: W_g[kc : kc + kn, 0 : E) copied as it lies in HBM (kn rows
+// of E elements, 2E bytes each) into LDS at dst by direct global->LDS loads, 1 KB per wave
+// instruction, lane l's 16 bytes into slot l (kn * E * 2 is a whole number of KB: kn is a
+// multiple of 64). No registers in between: the B fragments come out of LDS with
+// transposing reads (wg_fragment).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void stage_wg_direct(const bf16* __restrict__ src, int kn, int E,
+                                                char* dst, int wave, int lane) {
+  const int nchunk = kn * E / 8;  // 16-byte chunks
+  const int ninst = (nchunk + 63) / 64;
+  for (int j = wave; j < ninst; j += 4) {
+    const int c = min(64 * j + lane, nchunk - 1);
+    __builtin_amdgcn_global_load_lds(src + (size_t)c * 8, (lds_void*)(dst + j * 1024), 16, 0, 0);
+  }
+}
+
+// B fragment of a 16x16x32 MFMA from the natural layout of stage_wg_direct: 8 consecutive
+// k (rows kr .. kr + 7) of column col0 + lane % 16, from two transposing reads. Source lane
+// i of each 16-lane group addresses row kr + i / 4 (+ 4 for the second read), columns
+// col0 + 4 (i % 4) .. + 3; result lane j gets column col0 + j of the four rows. Columns at
+// or past E read the next row's values (the logits of padding experts are never used).
+__device__ __forceinline__ u32x4 wg_fragment(const char* w, int rowbytes, int kr, int col0,
+                                             int lane) {
+  const int i = lane & 15;
+  const char* p = w + (size_t)(kr + (i >> 2)) * rowbytes + (col0 + 4 * (i & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * rowbytes));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(u32x4, v);
+}
+
 // softplus(z) = log(1 + e^z), as max(z, 0) + log(1 + e^-|z|) so that e^z never overflows
 __device__ __forceinline__ float softplus_f(float z) {
   return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
 }
 
-// NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added
-template <typename TI, int EP, int NOISE>
+// NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added.
+// DIRECT (bf16, E a multiple of 8): W_g (and W_noise) staged by stage_wg_direct and read
+// with wg_fragment; otherwise transposed through registers by stage_wg_transposed.
+template <typename TI, int EP, int NOISE, bool DIRECT>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   using M = RouterMma<TI>;
   constexpr int VEC = M::VEC;
@@ -139,6 +182,10 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   constexpr int LSP = EP + 1;
   constexpr int PF = kRouterPF;
   static_assert(KC % ITK == 0, "stage must hold whole iterations");
+  static_assert(!DIRECT || sizeof(TI) == 2, "direct staging is the bf16 layout");
+  // DIRECT: W_noise sits after W_g's KC rows of EP elements (the same split as the
+  // transposed layout's)
+  constexpr int WN_BYTES = KC * EP * 2;
 
   // rows [0, EP): W_g transposed; rows [EP, 2 EP): W_noise transposed (NOISE == 2)
   __shared__ __attribute__((aligned(16))) TI Wl[NB * 16 * LDW];
@@ -190,14 +237,34 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
     const TI* xs = xrow + kc;
     const int nit = (kn + ITK - 1) / ITK;
     u32x4 av[PF][4];
+    if constexpr (DIRECT) {
+      // the slice's direct loads go out first, then the first x loads: waiting for the
+      // former (loads complete in order) does not wait for the latter
+      if (kc > 0) lds_barrier();  // the previous slice's fragment reads are done
+      // (a uniform wave index keeps the loads' LDS destinations scalar)
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      stage_wg_direct(reinterpret_cast<const bf16*>(Wg) + (size_t)kc * E, kn, E,
+                      reinterpret_cast<char*>(Wl), wave_u, lane);
+      if constexpr (NOISE == 2)
+        stage_wg_direct(static_cast<const bf16*>(a.Wn) + (size_t)kc * E, kn, E,
+                        reinterpret_cast<char*>(Wl) + WN_BYTES, wave_u, lane);
 #pragma unroll
-    for (int p = 0; p < PF - 1; ++p) router_load_x<VEC>(xs, p, kn, g, av[p]);
-    lds_barrier();  // the previous slice's fragment reads are done
-    stage_wg_transposed<TI>(Wg + (size_t)kc * E, kn, E, LDW, Wl, tid);
-    if constexpr (NOISE == 2)
-      stage_wg_transposed<TI>(static_cast<const TI*>(a.Wn) + (size_t)kc * E, kn, E, LDW,
-                              Wl + EP * LDW, tid);
-    lds_barrier();  // the slice is in LDS
+      for (int p = 0; p < PF - 1; ++p) router_load_x<VEC>(xs, p, kn, g, av[p]);
+      // this wave's share of the slice has landed (the x loads behind it may still be in
+      // flight); then every wave's has. A plain barrier: a fence would wait for the x
+      // loads too.
+      wait_vmcnt<(PF - 1) * 4>();
+      __builtin_amdgcn_s_barrier();
+    } else {
+#pragma unroll
+      for (int p = 0; p < PF - 1; ++p) router_load_x<VEC>(xs, p, kn, g, av[p]);
+      lds_barrier();  // the previous slice's fragment reads are done
+      stage_wg_transposed<TI>(Wg + (size_t)kc * E, kn, E, LDW, Wl, tid);
+      if constexpr (NOISE == 2)
+        stage_wg_transposed<TI>(static_cast<const TI*>(a.Wn) + (size_t)kc * E, kn, E, LDW,
+                                Wl + EP * LDW, tid);
+      lds_barrier();  // the slice is in LDS
+    }
     for (int it0 = 0; it0 < nit; it0 += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
@@ -208,9 +275,16 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
           const int kx = it * ITK + (4 * u + g) * VEC;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            // W_noise blocks (nb >= NG) sit EP rows further down
-            const int row = (nb >= NG ? EP : 0) + min((nb % NG) * 16 + (lane & 15), E - 1);
-            const u32x4 bw = ld16(&Wl[row * LDW + min(kx, kn - VEC)]);
+            u32x4 bw;
+            if constexpr (DIRECT) {
+              // W_noise blocks (nb >= NG) sit WN_BYTES further on
+              bw = wg_fragment(reinterpret_cast<const char*>(Wl) + (nb >= NG ? WN_BYTES : 0),
+                               2 * E, min(kx, kn - VEC), (nb % NG) * 16, lane);
+            } else {
+              // W_noise blocks (nb >= NG) sit EP rows further down
+              const int row = (nb >= NG ? EP : 0) + min((nb % NG) * 16 + (lane & 15), E - 1);
+              bw = ld16(&Wl[row * LDW + min(kx, kn - VEC)]);
+            }
             const u32x4 bv = kx < kn ? bw : u32x4{0u, 0u, 0u, 0u};  // k past the stage: 0
             M::step(acc[nb], av[j][u], bv);
           }
@@ -535,21 +609,27 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
   const int noise = a.eps ? (a.Wn ? 2 : 1) : 0;
   if (noise && ec) return hipErrorInvalidValue;  // noise is a token-choice feature
   dim3 grid(nblk), block(256);
-#define MOE_ROUTER(TI, EP, NOISE) router_kernel<TI, EP, NOISE><<<grid, block, 0, s>>>(a, ec)
-#define MOE_ROUTER_EP(TI, NOISE)                        \
-  do {                                                  \
-    if (ep == 16) MOE_ROUTER(TI, 16, NOISE);            \
-    else if (ep == 32) MOE_ROUTER(TI, 32, NOISE);       \
-    else MOE_ROUTER(TI, 64, NOISE);                     \
+  const bool direct = bf16in && a.E % 8 == 0;
+#define MOE_ROUTER(TI, EP, NOISE, DIRECT) \
+  router_kernel<TI, EP, NOISE, DIRECT><<<grid, block, 0, s>>>(a, ec)
+#define MOE_ROUTER_EP(TI, NOISE, DIRECT)                        \
+  do {                                                          \
+    if (ep == 16) MOE_ROUTER(TI, 16, NOISE, DIRECT);            \
+    else if (ep == 32) MOE_ROUTER(TI, 32, NOISE, DIRECT);       \
+    else MOE_ROUTER(TI, 64, NOISE, DIRECT);                     \
   } while (0)
-  if (bf16in) {
-    if (noise == 0) MOE_ROUTER_EP(bf16, 0);
-    else if (noise == 1) MOE_ROUTER_EP(bf16, 1);
-    else MOE_ROUTER_EP(bf16, 2);
+  if (bf16in && direct) {
+    if (noise == 0) MOE_ROUTER_EP(bf16, 0, true);
+    else if (noise == 1) MOE_ROUTER_EP(bf16, 1, true);
+    else MOE_ROUTER_EP(bf16, 2, true);
+  } else if (bf16in) {
+    if (noise == 0) MOE_ROUTER_EP(bf16, 0, false);
+    else if (noise == 1) MOE_ROUTER_EP(bf16, 1, false);
+    else MOE_ROUTER_EP(bf16, 2, false);
   } else {
-    if (noise == 0) MOE_ROUTER_EP(float, 0);
-    else if (noise == 1) MOE_ROUTER_EP(float, 1);
-    else MOE_ROUTER_EP(float, 2);
+    if (noise == 0) MOE_ROUTER_EP(float, 0, false);
+    else if (noise == 1) MOE_ROUTER_EP(float, 1, false);
+    else MOE_ROUTER_EP(float, 2, false);
   }
 #undef MOE_ROUTER_EP
 #undef MOE_ROUTER
