@@ -4,7 +4,8 @@
 // "Mixture of Experts（MoE）の理論と実装", MoELayer.route; the Korean page's
 // TopKGating): one workgroup takes 64 tokens. The skinny GEMM x W_g runs on
 // 16x16 MFMA tiles (x rows streamed from HBM straight into registers as the A
-// operand, W_g staged transposed in LDS as the B operand), then four threads per
+// operand, W_g staged in LDS as the B operand: bf16 copied as it lies and read with
+// transposing LDS reads, otherwise transposed through registers), then four threads per
 // token do the max-shifted softmax, top-k by (logit desc, index asc) and the
 // weights. The same workgroup counts its slots per expert, ranks each slot among
 // the block's slots of the same expert (flattened token-major order) and sums the
@@ -121,11 +122,6 @@ __device__ __forceinline__ void stage_wg_transposed(const TI* __restrict__ src, 
   }
 }
 
-// bf16 with E a multiple of 8: W_g[kc : kc + kn, 0 : E) copied as it lies in HBM (kn rows
-// of E elements, 2E bytes each) into LDS at dst by direct global->LDS loads, 1 KB per wave
-// instruction, lane l's 16 bytes into slot l (kn * E * 2 is a whole number of KB: kn is a
-// multiple of 64). No registers in between: the B fragments come out of LDS with
-// transposing reads (wg_fragment).
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -137,6 +133,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+
+// bf16 with E a multiple of 8: W_g[kc : kc + kn, 0 : E) copied as it lies in HBM (kn rows
+// of E elements, 2E bytes each) into LDS at dst by direct global->LDS loads, 1 KB per wave
+// instruction, lane l's 16 bytes into slot l (kn * E * 2 is a whole number of KB: kn is a
+// multiple of 64). No registers in between: the B fragments come out of LDS with
+// transposing reads (wg_fragment).
 __device__ __forceinline__ void stage_wg_direct(const bf16* __restrict__ src, int kn, int E,
                                                 char* dst, int wave, int lane) {
   const int nchunk = kn * E / 8;  // 16-byte chunks
@@ -187,7 +189,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
   // transposed layout's)
   constexpr int WN_BYTES = KC * EP * 2;
 
-  // rows [0, EP): W_g transposed; rows [EP, 2 EP): W_noise transposed (NOISE == 2)
+  // rows [0, EP): W_g transposed; rows [EP, 2 EP): W_noise transposed (NOISE == 2).
+  // DIRECT: W_g's [k, E] rows from byte 0, W_noise's from byte WN_BYTES.
   __shared__ __attribute__((aligned(16))) TI Wl[NB * 16 * LDW];
   __shared__ float Ls[kRT * LSP];
   __shared__ float red[256];
