@@ -92,6 +92,12 @@ def test_noisy_fine_grained_e64_top4(moe):
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05))
 
 
+def test_noisy_24_experts_two_slices(moe):
+    # bf16, E = 24: W_g and W_noise staged as they lie, two LDS slices (d = 2048)
+    w = W.custom("noisy_e24", T=333, d=2048, f=128, E=24, k=3, wg_std=0.05, seed=(42, 310))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05))
+
+
 def test_additive_noise_fp32_ragged(moe):
     # the fixed-scale form: logits + noise_std * eps, noise_std = 0.1
     w = W.custom("additive_fp32", dtype="fp32", T=1000, d=128, f=64, E=8, k=2, x_std=0.5,

@@ -153,6 +153,15 @@ def test_max_k_and_E(moe):
     run_tc_case(moe, W.custom("E64k8", T=333, d=128, f=128, E=64, k=8, wg_std=0.2, seed=(42, 205)))
 
 
+@pytest.mark.parametrize("E,k,d", [(24, 3, 512), (40, 5, 2048)])
+def test_router_expert_counts_with_partial_column_blocks(moe, E, k, d):
+    # bf16 router with E a multiple of 8 but not of 16: W_g is staged as it lies and the
+    # last 16-column block of the MFMA holds padding columns (E = 40: d = 2048 needs two
+    # LDS slices of the [k, E] rows)
+    run_tc_case(moe, W.custom(f"E{E}k{k}", T=300, d=d, f=128, E=E, k=k, wg_std=0.05,
+                              seed=(42, 220 + E)))
+
+
 def test_zero_input_uniform_routing(moe):
     w = W.custom("zeros", T=70, d=64, f=64, E=8, k=3, seed=(42, 206))
     inp = W.make_inputs(w)
