@@ -301,8 +301,11 @@ def profile_read() -> dict:
 class SparseMoE:
     """One sparse MoE layer with its weights held as device tensors.
 
-    ``layer(x)`` runs ``moe_forward`` and returns the fp32 output y; the workspace is
-    allocated once per token count and reused."""
+    ``layer(x)`` runs ``moe_forward`` and returns the fp32 output y. x may carry leading
+    dimensions, [..., d_model] (the [batch, seq, d_model] input of the pages' layer
+    modules): the tokens are those dimensions flattened (a view of the contiguous x), and
+    y comes back with x's leading shape. The workspace is kept and reused while it is
+    large enough; ``last`` holds the full result of the latest call (routing, f, p, loss)."""
 
     def __init__(self, W_g, W_gate, W_up, W_down, b_g=None, *, k=2, mode="tc",
                  capacity_factor=1.0, renormalize=True):
@@ -312,9 +315,11 @@ class SparseMoE:
         self.last = None
 
     def __call__(self, x, **kw):
-        out = moe_forward(x, self.W_g, self.b_g, self.W_gate, self.W_up, self.W_down, k=self.k,
-                          mode=self.mode, capacity_factor=self.cf, renormalize=self.renormalize,
-                          workspace=self._ws, **kw)
+        _need(x, "x")
+        lead, d = x.shape[:-1], x.shape[-1]
+        out = moe_forward(x.view(-1, d), self.W_g, self.b_g, self.W_gate, self.W_up,
+                          self.W_down, k=self.k, mode=self.mode, capacity_factor=self.cf,
+                          renormalize=self.renormalize, workspace=self._ws, **kw)
         self._ws = out["workspace"]
         self.last = out
-        return out["y"]
+        return out["y"].view(*lead, d)

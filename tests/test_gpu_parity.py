@@ -287,6 +287,25 @@ def test_dispatch_permutation_is_stable_bijection(moe, dtype):
             moe.workspace_offset(shape, moe.WS_XPERM)
 
 
+def test_layer_module_batch_seq_input(moe):
+    # the layer object on [batch, seq, d_model] input: the same bits as moe_forward on the
+    # flattened tokens, for three calls of different token counts sharing its workspace
+    w = W.custom("module", T=4 * 75, d=128, f=128, E=8, k=2, seed=(42, 230))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    layer = moe.SparseMoE(dev["Wg"], dev["Wgate"], dev["Wup"], dev["Wdown"], dev["b"], k=2)
+    for B, S in ((4, 75), (2, 33), (4, 75)):
+        x = dev["x"][: B * S].reshape(B, S, w.d)
+        y = layer(x)
+        ref = moe.moe_forward(dev["x"][: B * S], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"],
+                              dev["Wdown"], k=2)
+        torch.cuda.synchronize()
+        assert y.shape == (B, S, w.d)
+        assert torch.equal(y.reshape(B * S, w.d), ref["y"])
+        assert torch.equal(layer.last["idx"], ref["idx"])
+        assert torch.equal(layer.last["loss"], ref["loss"])
+
+
 # the full-size case runs last: it is the slowest
 def test_mixtral_layer_skewed_sampled(moe):
     """Full-size Mixtral layer with a skewed router bias: routing, counts and
