@@ -197,6 +197,36 @@ def pin_k_equals_E_is_dense(O):
     assert np.allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-14)
 
 
+def pin_dense_mixture(O):
+    """The dense mixture y = sum_e g_e E_e(x) over every expert (the Chinese page's
+    ``MixtureOfExperts``) equals the same sum computed in torch float64 with a bias, and
+    the literal per-token loops of the brute-force expert on a second case; its gates are
+    the full softmax (not a top-k), so a token's output changes when any expert's
+    weights change."""
+    c = _case(21, T=9, d=6, f=8, E=5, bias=True)
+    got = O.dense_mixture(c["x"], c["Wg"], c["b"], c["Wgate"], c["Wup"], c["Wdown"])
+    X = torch.from_numpy(c["x"])
+    g = torch.softmax(X @ torch.from_numpy(c["Wg"]) + torch.from_numpy(c["b"]), dim=1)
+    ref = torch.zeros(9, 6, dtype=torch.float64)
+    for e in range(5):
+        h = F.silu(X @ torch.from_numpy(c["Wgate"][e])) * (X @ torch.from_numpy(c["Wup"][e]))
+        ref += g[:, e:e + 1] * (h @ torch.from_numpy(c["Wdown"][e]))
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-14)
+    c = _case(22, T=4, d=3, f=5, E=3, bias=False, wg_std=2.0)
+    got = O.dense_mixture(c["x"], c["Wg"], None, c["Wgate"], c["Wup"], c["Wdown"])
+    for t in range(4):
+        s = [sum(c["x"][t, i] * c["Wg"][i, e] for i in range(3)) for e in range(3)]
+        m = max(s)
+        ex = [math.exp(v - m) for v in s]
+        want = [0.0] * 3
+        for e in range(3):
+            out = B.expert(_lists(c["x"][t]), _lists(c["Wgate"][e]), _lists(c["Wup"][e]),
+                           _lists(c["Wdown"][e]))
+            for j in range(3):
+                want[j] += ex[e] / sum(ex) * out[j]
+        assert np.allclose(got[t], want, rtol=1e-12, atol=1e-14), t
+
+
 def pin_brute_layer(O):
     """Whole token-choice layer equals the literal-loop brute force on T <= 8
     to 1e-12 relative."""

@@ -62,7 +62,13 @@ MUTANTS = {
     "tc_capacity_dropped_keep_gate": ("g = np.where(kept, np.take_along_axis(p, idx, axis=1), 0.0)",
                                       "g = np.take_along_axis(p, idx, axis=1)"),
     "tc_capacity_truncates_factors": ("return int((T / E) * cf * k)", "return int(T / E) * int(cf * k)"),
-    "tc_capacity_renorm_over_all_slots": ("rows = g.sum(axis=1, keepdims=True)",
+    "dense_mixture_drops_gate": ("y += g[:, e:e + 1] * expert_ffn(x, Wgate[e], Wup[e], Wdown[e])",
+                                 "y += expert_ffn(x, Wgate[e], Wup[e], Wdown[e])"),
+    "dense_mixture_drops_bias": ("g = softmax_rows(router_logits(x, Wg, b))",
+                                 "g = softmax_rows(router_logits(x, Wg, None))"),
+    "dense_mixture_skips_last_expert": ("for e in range(g.shape[1]):",
+                                        "for e in range(g.shape[1] - 1):"),
+    "tc_capacity_renorm_over_all_slots":("rows = g.sum(axis=1, keepdims=True)",
                                           "rows = np.take_along_axis(p, idx, axis=1).sum(axis=1, keepdims=True)"),
 }
 
