@@ -67,6 +67,11 @@ def stage_work(w, R=None, noisy=False):
     return work
 
 
+TRAFFIC_SOURCE = ("HBM bytes per gate/up launch from profiles/mixtral_layer_hbm_traffic.md "
+                  "(rocprofv3 FETCH_SIZE and WRITE_SIZE runs scaled by a copy kernel), valid for "
+                  "the gemm.hip source whose SHA-256 it records; not measured in this run")
+
+
 def gemm_traffic_from_profile():
     """HBM bytes per gate/up GEMM launch from the committed FETCH_SIZE/WRITE_SIZE summary,
     scaled by the copy-kernel calibration; None when the GEMM source changed since."""
@@ -89,7 +94,8 @@ def gemm_traffic_from_profile():
 
 
 def cpu_baseline(w, inp, sample_tokens):
-    """The fp64 oracle as it stands, on the first `sample_tokens` tokens."""
+    """The fp64 oracle as it stands, on the first `sample_tokens` tokens. Returns the
+    baseline record and the oracle's outputs (for the parity check after the timing)."""
     from oracle import moe_oracle as O
     try:
         import threadpoolctl
@@ -102,15 +108,52 @@ def cpu_baseline(w, inp, sample_tokens):
     xs = inp["x"][:n]
     t0 = time.perf_counter()
     if w.mode == "tc":
-        O.forward_tc(xs, inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.k,
-                     w.renormalize)
+        ref = O.forward_tc(xs, inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.k,
+                           w.renormalize)
     else:
-        O.forward_ec(xs, inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.cf)
+        ref = O.forward_ec(xs, inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.cf)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {w.T} tokens of the same workload through the fp64 NumPy "
-                      f"oracle (router, top-k, per-expert fp64 GEMMs, combine); {dt:.1f} s",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+    rec = {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"first {n} of {w.T} tokens of the same workload through the fp64 NumPy "
+                     f"oracle (router, top-k, per-expert fp64 GEMMs, combine); {dt:.1f} s",
+           "seconds": dt, "host_cpus": os.cpu_count()}
+    return rec, ref, n
+
+
+def parity_vs_oracle(w, inp, ref, n, y_dev, idx_dev):
+    """The timed run's output against the oracle's on the tokens the CPU leg ran: routing
+    (tokens whose top-k margin exceeds 1e-5 must pick the oracle's experts) and y, by the
+    bf16 rule max|dy| / rms(y) <= 2e-2 (fp32: max|dy| / max|y| <= 1e-4). Near-tie tokens
+    are compared with the oracle evaluated on the device's experts."""
+    from oracle import moe_oracle as O
+    bf = w.dtype == "bf16"
+    y_ref = ref["y"]
+    out = {"tokens": int(n), "tol": 2e-2 if bf else 1e-4,
+           "norm": "max|dy| / rms(y_ref)" if bf else "max|dy| / max|y_ref|"}
+    if w.mode == "tc":
+        idx_ref = ref["idx"]
+        exempt = O.topk_margin(ref["probs"], w.k) <= 1e-5
+        idx_d = idx_dev[:n].astype(np.int64)
+        diff = np.any(np.sort(idx_d, 1) != np.sort(idx_ref, 1), axis=1)
+        out["idx_mismatch_tokens"] = int(np.sum(diff & ~exempt))
+        out["exempt_tokens"] = int(exempt.sum())
+        redo = np.nonzero(diff & exempt)[0]
+        if redo.size:
+            y_ref = y_ref.copy()
+            w_use = O.gate_weights(ref["probs"][redo], idx_d[redo], w.renormalize)
+            y_ref[redo] = O.mix(inp["x"][redo], idx_d[redo], w_use, inp["Wgate"], inp["Wup"],
+                                inp["Wdown"])
+    else:
+        if n != w.T:  # expert choice ranks every token: only the full batch is comparable
+            return None
+        out["idx_mismatch_experts"] = int(np.sum(np.any(idx_dev.astype(np.int64) != ref["idx"],
+                                                        axis=1)))
+    dy = np.max(np.abs(y_dev[:n].astype(np.float64) - y_ref))
+    scale = np.sqrt(np.mean(y_ref ** 2)) if bf else np.max(np.abs(y_ref))
+    out["y_err"] = float(dy / scale)
+    out["ok"] = bool(out["y_err"] <= out["tol"] and out.get("idx_mismatch_tokens", 0) == 0
+                     and out.get("idx_mismatch_experts", 0) == 0)
+    return out
 
 
 def main():
@@ -184,16 +227,20 @@ def main():
     for _ in range(args.warmup):
         M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
     torch.cuda.synchronize()
-    # the timed steps run without per-stage events; a second pass of the same steps
+    # the timed steps: one event pair per step on the stream the library launches on
+    # (torch's current stream), no per-stage events; a second pass of the same steps
     # records HIP events around every kernel launch for the per-stage figures
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
-    stop.record()
+    t_wall = time.perf_counter()
+    for a, z in ev:
+        a.record()
+        last = M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
+        z.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
+    t_wall = time.perf_counter() - t_wall
+    step_ms = np.array([a.elapsed_time(z) for a, z in ev])
     M.profile_enable(True)
     M.profile_read()  # clear
     for _ in range(args.steps):
@@ -201,7 +248,7 @@ def main():
     torch.cuda.synchronize()
     M.profile_enable(False)
     stages = M.profile_read()
-    ms_step = ms_total / args.steps
+    ms_step = float(np.median(step_ms))
     tokens_s = w.T / (ms_step * 1e-3)
 
     work = stage_work(w, R_run, noisy=args.variant == "noisy")
@@ -229,9 +276,15 @@ def main():
     gemm_tf = gemm_flop / ((gu_ms + dn_ms) * 1e-3) / 1e12
     gu_tf = work["gemm_gate_up"][1] / (gu_ms * 1e-3) / 1e12
 
-    cpu = None
+    traffic = (gemm_traffic_from_profile()
+               if w is W.MIXTRAL_LAYER and args.variant == "plain" else None)
+    cpu = parity = None
     if args.cpu_sample > 0 and args.variant == "plain":
-        cpu = cpu_baseline(w, inp, args.cpu_sample)
+        y_dev = y.cpu().numpy()
+        idx_dev = last["idx"].cpu().numpy()
+        cpu, ref, n_ref = cpu_baseline(w, inp, args.cpu_sample)
+        parity = parity_vs_oracle(w, inp, ref, n_ref, y_dev, idx_dev)
+        del ref
 
     line = {
         "metric": METRIC,
@@ -241,6 +294,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_stats": {"median": round(ms_step, 4), "mean": round(float(step_ms.mean()), 4),
+                              "min": round(float(step_ms.min()), 4),
+                              "max": round(float(step_ms.max()), 4),
+                              "timing": "hipEvent pair per step on the launch stream; median"},
+        "timed_wall_s": round(t_wall, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -255,10 +313,11 @@ def main():
         "expert_gemm_frac_of_peak": round(gemm_tf / peak_tf, 4),
         "roofline": {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(gu_tf, 1),
                      "peak": peak_tf, "unit": "TFLOP/s", "frac": round(gu_tf / peak_tf, 4),
-                     "traffic": (gemm_traffic_from_profile()
-                                 if w is W.MIXTRAL_LAYER and args.variant == "plain" else None)},
+                     "traffic": traffic,
+                     "traffic_source": (TRAFFIC_SOURCE if traffic is not None else None)},
         "stages": st_out,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     if args.variant != "plain":
         line["config"]["variant"] = args.variant

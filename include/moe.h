@@ -45,11 +45,13 @@
  *   - Entry points are reentrant; calls on different streams may overlap if their
  *     workspaces differ.
  *
- * Limits: 1 <= E <= 64; token choice 1 <= k <= min(E, 8); d_model and d_ff multiples
- * of 64 and at most 2^20; 0 <= T and T * max(k, 1) < 2^31; expert choice needs
- * 1 <= C <= T and E * C < 2^31. fp32 layers take at most 64 * (65535 - E) routed rows
- * (T * k, or E * C; more is MOE_ERR_UNSUPPORTED). x, weights, y and the workspace must be
- * 16-byte aligned.
+ * Limits: 1 <= E <= 64; token choice 1 <= k <= min(E, 8); d_model and d_ff at most 2^20;
+ * 0 <= T and T * max(k, 1) < 2^31; expert choice needs 1 <= C <= T and E * C < 2^31
+ * (outside these: MOE_ERR_BAD_SHAPE). Limits of this implementation, not of the method,
+ * return MOE_ERR_UNSUPPORTED: E > 64, k > 8, d_model or d_ff not a multiple of 64 (the
+ * kernels run whole 64-column tiles), fp32 layers with more than 64 * (65535 - E)
+ * routed rows (T * k, or E * C), and bf16 expert choice with 2 * E * C >= 2^31 (the
+ * residual rows of h, below). x, weights, y and the workspace must be 16-byte aligned.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -95,9 +97,10 @@ typedef struct moe_shape {
   int32_t renormalize;   /* token choice: 1 = selected weights divided by their sum
                             (Mixture of Experts（MoE）の理論と実装, MoELayer.route);
                             0 = raw probabilities (the qiita router equations) */
-  float capacity_factor; /* expert choice: C = floor(T * capacity_factor / E);
-                            token choice with capacity: C = int((T / E) * capacity_factor
-                            * k), > 0 and finite; ignored in plain token choice */
+  double capacity_factor; /* expert choice: C = floor(T * capacity_factor / E);
+                             token choice with capacity: C = int((T / E) * capacity_factor
+                             * k); both in double, > 0 and finite; ignored in plain token
+                             choice */
 } moe_shape;
 
 /* Training noise of noisy top-k gating, token choice only (both token-choice modes).
@@ -187,9 +190,12 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
                      int32_t* counts, float* z_loss, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
-/* Whole layer forward: router, dispatch (histogram, prefix sum, stable permutation of
- * token rows into expert-contiguous order), grouped SwiGLU gate/up GEMM, grouped down
- * GEMM, weighted combine, and (token choice) the load-balancing statistics.
+/* Whole layer forward ("Mixture of Experts（MoE）の理論と実装", MoELayer.forward: route,
+ * run each expert on its tokens, add the weighted expert outputs; the Korean page's
+ * MoELayerWithAuxLoss, which also returns the load-balancing loss): router, dispatch
+ * (histogram, prefix sum, stable permutation of token rows into expert-contiguous order),
+ * grouped SwiGLU gate/up GEMM, grouped down GEMM, weighted combine, and (token choice) the
+ * load-balancing statistics.
  *   x, W_g, b_g, noise   as in moe_route
  *   W_gate, W_up  [E, d_model, d_ff] dtype, expert e's matrix at offset e*d_model*d_ff
  *   W_down        [E, d_ff, d_model] dtype

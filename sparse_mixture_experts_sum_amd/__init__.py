@@ -54,7 +54,7 @@ class MoeShape(ctypes.Structure):
         ("mode", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("renormalize", ctypes.c_int32),
-        ("capacity_factor", ctypes.c_float),
+        ("capacity_factor", ctypes.c_double),
     ]
 
 
@@ -148,6 +148,18 @@ def _dtype_name(t: torch.Tensor) -> str:
     raise TypeError(f"unsupported dtype {t.dtype}: x and weights must be bfloat16 or float32")
 
 
+def _shape_is(t, name, shape):
+    """Full shape check, before anything reaches the library: the C ABI sees only raw
+    pointers, so an undersized tensor would be read or written out of bounds on the
+    device."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _need(t, name, dtype=None, dev=None):
     if t is None:
         return
@@ -161,12 +173,28 @@ def _need(t, name, dtype=None, dev=None):
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
 
-def _noise(x, W_noise, eps, dev):
-    """moe_noise for training noise: eps [T,E] fp32 (required for any noise) and
-    optionally W_noise [d,E] of x's dtype; None when eps is None."""
+def _x_shape(x):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a tensor")
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, d_model], got shape {tuple(x.shape)}")
+    return x.shape
+
+
+def _noise_shapes(T, d, E, W_noise, eps):
     if eps is None:
         if W_noise is not None:
             raise ValueError("W_noise needs eps, the normal draw")
+        return
+    _shape_is(eps, "eps", (T, E))
+    _shape_is(W_noise, "W_noise", (d, E))
+
+
+def _noise(x, W_noise, eps, dev):
+    """moe_noise for training noise: eps [T,E] fp32 (required for any noise) and
+    optionally W_noise [d,E] of x's dtype; None when eps is None. Shapes are checked by
+    _noise_shapes first."""
+    if eps is None:
         return None
     _need(eps, "eps", torch.float32, dev)
     _need(W_noise, "W_noise", x.dtype, dev)
@@ -176,8 +204,10 @@ def _noise(x, W_noise, eps, dev):
 
 def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     n = workspace_size(shape)
-    if workspace is not None and workspace.numel() * workspace.element_size() >= n:
-        return workspace
+    if workspace is not None:
+        _need(workspace, "workspace", dev=dev)
+        if workspace.numel() * workspace.element_size() >= n:
+            return workspace
     return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
 
 
@@ -187,13 +217,18 @@ def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormal
     """Router only. Token choice (with or without capacity) returns idx/w [T,k];
     expert choice idx/w [E,C]. want_z_loss adds the router z-loss (fp32 [1]); eps
     (and W_noise) add the training noise of noisy top-k gating."""
+    T, d = _x_shape(x)
+    if not isinstance(W_g, torch.Tensor) or W_g.dim() != 2:
+        raise ValueError("W_g must be [d_model, E]")
+    E = W_g.shape[1]
+    _shape_is(W_g, "W_g", (d, E))
+    _shape_is(b_g, "b_g", (E,))
+    _noise_shapes(T, d, E, W_noise, eps)
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
     _need(W_g, "W_g", dt, dev)
     _need(b_g, "b_g", torch.float32, dev)
-    T, d = x.shape
-    E = W_g.shape[1]
     shape = make_shape(T, d, 64, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
     ws = _workspace(shape, dev, workspace)
     if mode != "ec":
@@ -219,22 +254,28 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
     """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
     counts, (token choice) f, p, loss, and the router z-loss. eps (and W_noise) add
     the training noise of noisy top-k gating."""
+    T, d = _x_shape(x)
+    if not isinstance(W_gate, torch.Tensor) or W_gate.dim() != 3:
+        raise ValueError("W_gate must be [E, d_model, d_ff]")
+    E, _, f = W_gate.shape
+    _shape_is(W_gate, "W_gate", (E, d, f))
+    _shape_is(W_up, "W_up", (E, d, f))
+    _shape_is(W_down, "W_down", (E, f, d))
+    _shape_is(W_g, "W_g", (d, E))
+    _shape_is(b_g, "b_g", (E,))
+    _shape_is(y, "y", (T, d))
+    _noise_shapes(T, d, E, W_noise, eps)
     dev = x.device
     dt = x.dtype
     _need(x, "x", dev=dev)
     for t, nm in ((W_g, "W_g"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down, "W_down")):
         _need(t, nm, dt, dev)
     _need(b_g, "b_g", torch.float32, dev)
-    T, d = x.shape
-    E, _, f = W_gate.shape
-    if W_g.shape != (d, E) or W_up.shape != (E, d, f) or W_down.shape != (E, f, d):
-        raise ValueError("inconsistent weight shapes")
+    _need(y, "y", torch.float32, dev)
     shape = make_shape(T, d, f, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
     ws = _workspace(shape, dev, workspace)
     if y is None:
         y = torch.empty(T, d, dtype=torch.float32, device=dev)
-    else:
-        _need(y, "y", torch.float32, dev)
     idx = w = probs = counts = fo = po = lo = None
     if want_routing:
         if mode != "ec":
@@ -264,11 +305,16 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
 
 def moe_aux_loss(probs, idx, *, workspace=None) -> dict:
     """f, p, loss and counts from router outputs probs [T,E] and idx [T,k] (token choice)."""
+    if not isinstance(probs, torch.Tensor) or probs.dim() != 2:
+        raise ValueError("probs must be [T, E]")
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 2:
+        raise ValueError("idx must be [T, k]")
+    T, E = probs.shape
+    k = idx.shape[1]
+    _shape_is(idx, "idx", (T, k))
     dev = probs.device
     _need(probs, "probs", torch.float32, dev)
     _need(idx, "idx", torch.int32, dev)
-    T, E = probs.shape
-    k = idx.shape[1]
     shape = make_shape(T, 64, 64, E, k, "tc", "fp32")
     ws = _workspace(shape, dev, workspace)
     f = torch.empty(E, dtype=torch.float32, device=dev)

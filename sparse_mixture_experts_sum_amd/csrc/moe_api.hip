@@ -27,7 +27,7 @@ struct Layout {
 };
 
 int64_t ec_capacity(const moe_shape& s) {
-  const double c = floor((double)s.T * (double)s.capacity_factor / (double)s.E);
+  const double c = floor((double)s.T * s.capacity_factor / (double)s.E);
   if (!(c >= 0.0) || c > 9.0e18) return -1;
   return (int64_t)c;
 }
@@ -35,7 +35,7 @@ int64_t ec_capacity(const moe_shape& s) {
 // Token choice with an expert capacity: int((T / E) * cf * k), the product taken in that
 // order in double (机器学习基础系列——混合专家模型, expert_capacity_routing).
 int64_t tc_capacity(const moe_shape& s) {
-  const double c = floor((double)s.T / (double)s.E * (double)s.capacity_factor * (double)s.k);
+  const double c = floor((double)s.T / (double)s.E * s.capacity_factor * (double)s.k);
   if (!(c >= 0.0) || c > 9.0e18) return -1;
   return (int64_t)c;
 }
@@ -56,8 +56,12 @@ moe_status check_shape(const moe_shape* s) {
       s->mode != MOE_TOKEN_CHOICE_CAPACITY)
     return MOE_ERR_BAD_SHAPE;
   if (s->T < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->E < 1) return MOE_ERR_BAD_SHAPE;
-  if (s->d_model % 64 || s->d_ff % 64) return MOE_ERR_BAD_SHAPE;
+  // every row index is an int32 (and T * k below must not overflow)
+  if (s->T >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
   if (s->d_model > (1 << 20) || s->d_ff > (1 << 20)) return MOE_ERR_BAD_SHAPE;
+  // a limit of the kernels' tiles (whole 64-column tiles, whole 32-deep K stages), not of
+  // the method
+  if (s->d_model % 64 || s->d_ff % 64) return MOE_ERR_UNSUPPORTED;
   if (s->E > 64) return MOE_ERR_UNSUPPORTED;
   if (is_tc(s->mode)) {
     if (s->k < 1 || s->k > s->E) return MOE_ERR_BAD_SHAPE;
@@ -65,14 +69,18 @@ moe_status check_shape(const moe_shape* s) {
     if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_BAD_SHAPE;
     if (s->T * (int64_t)s->k >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
     if (s->mode == MOE_TOKEN_CHOICE_CAPACITY) {
-      if (!(s->capacity_factor > 0.0f) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
+      if (!(s->capacity_factor > 0.0) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
       if (tc_capacity(*s) < 0) return MOE_ERR_BAD_SHAPE;
     }
   } else {
-    if (!(s->capacity_factor > 0.0f) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
+    if (!(s->capacity_factor > 0.0) || !isfinite(s->capacity_factor)) return MOE_ERR_BAD_SHAPE;
     const int64_t C = ec_capacity(*s);
     if (C < 1 || C > s->T) return MOE_ERR_BAD_SHAPE;
     if (C * (int64_t)s->E >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
+    // bf16 carries h's rounding residual as E * C more rows of the down projection, whose
+    // group offsets are int32 too
+    if (s->dtype == MOE_BF16 && 2 * C * (int64_t)s->E >= (int64_t(1) << 31))
+      return MOE_ERR_UNSUPPORTED;
   }
   // the fp32 GEMMs launch one grid row per 64 routed rows (plus one per group): the grid's
   // y extent bounds the rows they take
@@ -175,7 +183,7 @@ struct StageTimer {
     if (!g_prof_on) return;
     a = prof_event();
     b = prof_event();
-    if (a && b && hipEventRecord(a, s) != hipSuccess) drop();
+    if (!a || !b || hipEventRecord(a, s) != hipSuccess) drop();
   }
   void drop() {
     if (a) g_event_pool.push_back(a);
@@ -411,7 +419,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
                                 offsets, E, R, d, ff, at<void>(ws, L.h), h_lo, stream));
   MOE_LAUNCH(MOE_STAGE_GEMM_DOWN,
              launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, L.ngroups, E,
-                              L.h_lo ? 2 * R : R, ff, d, at<float>(ws, L.o), stream));
+                              (int)(L.h_lo ? 2 * L.R : L.R), ff, d, at<float>(ws, L.o), stream));
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));

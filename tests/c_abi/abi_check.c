@@ -16,7 +16,7 @@ static void check(int cond, const char* what) {
 }
 
 static moe_shape shape(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t mode,
-                       float cf) {
+                       double cf) {
   moe_shape s;
   memset(&s, 0, sizeof s);
   s.T = T;
@@ -40,11 +40,17 @@ int main(void) {
 
   /* capacities */
   int64_t cap = -1;
-  moe_shape ec = shape(8192, 1024, 4096, 16, 1, MOE_EXPERT_CHOICE, 1.0f);
+  moe_shape ec = shape(8192, 1024, 4096, 16, 1, MOE_EXPERT_CHOICE, 1.0);
   check(moe_capacity(&ec, &cap) == MOE_OK && cap == 512, "expert-choice capacity 8192*1/16");
-  moe_shape tcc = shape(100, 64, 64, 8, 2, MOE_TOKEN_CHOICE_CAPACITY, 1.25f);
+  moe_shape tcc = shape(100, 64, 64, 8, 2, MOE_TOKEN_CHOICE_CAPACITY, 1.25);
   check(moe_capacity(&tcc, &cap) == MOE_OK && cap == 31, "token-choice capacity of T=100 E=8 k=2 cf=1.25");
-  moe_shape tc = shape(4096, 1024, 4096, 8, 2, MOE_TOKEN_CHOICE, 1.0f);
+  /* the factor is a double: 0.7 (not exact in binary) gives int(1000 * 0.7 / 10) = 70 as
+     the pages' double arithmetic does; its float rounding would give 69 */
+  moe_shape ec7 = shape(1000, 64, 64, 10, 1, MOE_EXPERT_CHOICE, 0.7);
+  check(moe_capacity(&ec7, &cap) == MOE_OK && cap == 70, "expert-choice capacity 1000*0.7/10");
+  moe_shape tc9 = shape(1000, 64, 64, 10, 2, MOE_TOKEN_CHOICE_CAPACITY, 0.9);
+  check(moe_capacity(&tc9, &cap) == MOE_OK && cap == 180, "token-choice capacity 1000/10*0.9*2");
+  moe_shape tc = shape(4096, 1024, 4096, 8, 2, MOE_TOKEN_CHOICE, 1.0);
   check(moe_capacity(&tc, &cap) == MOE_ERR_BAD_SHAPE, "plain token choice has no capacity");
   check(moe_capacity(NULL, &cap) == MOE_ERR_NULL_ARG, "capacity of NULL shape");
 
@@ -55,17 +61,17 @@ int main(void) {
         "position table inside the workspace");
   check(moe_workspace_offset(&ec, MOE_WS_POS, &off) == MOE_ERR_UNSUPPORTED,
         "no position table in expert choice");
-  moe_shape bad = shape(64, 100, 64, 8, 2, MOE_TOKEN_CHOICE, 1.0f); /* d_model % 64 != 0 */
-  check(moe_workspace_size(&bad, &ws) == MOE_ERR_BAD_SHAPE, "d_model not a multiple of 64");
-  bad = shape(64, 64, 64, 65, 2, MOE_TOKEN_CHOICE, 1.0f);
+  moe_shape bad = shape(64, 100, 64, 8, 2, MOE_TOKEN_CHOICE, 1.0); /* d_model % 64 != 0 */
+  check(moe_workspace_size(&bad, &ws) == MOE_ERR_UNSUPPORTED, "d_model not a multiple of 64");
+  bad = shape(64, 64, 64, 65, 2, MOE_TOKEN_CHOICE, 1.0);
   check(moe_workspace_size(&bad, &ws) != MOE_OK, "more than 64 experts");
-  bad = shape(64, 64, 64, 16, 9, MOE_TOKEN_CHOICE, 1.0f);
+  bad = shape(64, 64, 64, 16, 9, MOE_TOKEN_CHOICE, 1.0);
   check(moe_workspace_size(&bad, &ws) == MOE_ERR_UNSUPPORTED, "k = 9");
-  bad = shape(64, 64, 64, 8, 2, MOE_TOKEN_CHOICE_CAPACITY, 0.0f);
+  bad = shape(64, 64, 64, 8, 2, MOE_TOKEN_CHOICE_CAPACITY, 0.0);
   check(moe_workspace_size(&bad, &ws) == MOE_ERR_BAD_SHAPE, "capacity factor 0");
 
   /* argument errors of the compute entry points (returned before any HIP call) */
-  moe_shape s = shape(64, 128, 256, 8, 2, MOE_TOKEN_CHOICE, 1.0f);
+  moe_shape s = shape(64, 128, 256, 8, 2, MOE_TOKEN_CHOICE, 1.0);
   size_t need = 0;
   moe_workspace_size(&s, &need);
   void* p = (void*)(uintptr_t)4096; /* never dereferenced */
@@ -82,7 +88,7 @@ int main(void) {
   moe_noise nz = {NULL, NULL};
   check(moe_route(&s, p, p, NULL, &nz, p, p, NULL, NULL, NULL, p, need, NULL) == MOE_ERR_NULL_ARG,
         "noise without its draw");
-  moe_shape ecs = shape(64, 128, 256, 8, 1, MOE_EXPERT_CHOICE, 1.0f);
+  moe_shape ecs = shape(64, 128, 256, 8, 1, MOE_EXPERT_CHOICE, 1.0);
   nz.eps = (const float*)p;
   check(moe_route(&ecs, p, p, NULL, &nz, p, p, NULL, NULL, NULL, p, need, NULL) ==
             MOE_ERR_UNSUPPORTED,

@@ -65,6 +65,13 @@ def test_shape_validation(M):
         with pytest.raises(M.MoEError) as ei:
             M.workspace_size(s)
         assert ei.value.status in (2, 3)
+    # tile limits of the kernels, not of the method: unsupported rather than a bad shape
+    for kw in (dict(d_model=100), dict(d_ff=96), dict(d_model=72, d_ff=136)):
+        a = dict(T=64, d_model=128, d_ff=256, E=8, k=2)
+        a.update(kw)
+        with pytest.raises(M.MoEError) as ei:
+            M.workspace_size(M.make_shape(**a))
+        assert ei.value.status == 3, kw
     s = M.make_shape(64, 128, 256, 65, 2)
     with pytest.raises(M.MoEError) as ei:
         M.workspace_size(s)
@@ -94,6 +101,13 @@ def test_shape_validation(M):
 def test_capacity(M):
     assert M.capacity(M.make_shape(8192, 1024, 4096, 16, mode="ec", capacity_factor=1.0)) == 512
     assert M.capacity(M.make_shape(100, 64, 64, 8, mode="ec", capacity_factor=1.25)) == 15
+    # the factor travels as a double: factors that binary floating point cannot hold give
+    # the pages' int(T * cf / E) in double (0.7 as a float would give 69 here)
+    from oracle import moe_oracle as O
+    for T, E, cf in ((1000, 10, 0.7), (1000, 10, 0.3), (777, 7, 1.1), (4096, 64, 0.9)):
+        s = M.make_shape(T, 64, 64, E, mode="ec", capacity_factor=cf)
+        assert M.capacity(s) == O.capacity(T, E, cf) == int(T * cf / E), (T, E, cf)
+    assert M.capacity(M.make_shape(1000, 64, 64, 10, mode="ec", capacity_factor=0.7)) == 70
     with pytest.raises(M.MoEError):
         M.capacity(M.make_shape(4, 64, 64, 8, mode="ec", capacity_factor=1.0))  # C = 0
     with pytest.raises(M.MoEError):
@@ -103,15 +117,17 @@ def test_capacity(M):
 def test_token_choice_capacity_host_checks(M):
     # the page's example call of the capacity routing: T=100, E=8, k=2, cf=1.25 -> 31
     import json
+    from oracle import moe_oracle as O
     with open(os.path.join(ROOT, "tests", "golden", "page_values.json")) as fh:
         g = json.load(fh)["p5_capacity_of_page_call"]
     s = M.make_shape(g["T"], 64, 64, g["E"], g["k"], mode="tc_capacity",
                      capacity_factor=g["capacity_factor"])
     assert M.capacity(s) == g["value"]
     # int((T / E) * cf * k) in double, the product in that order
-    for T, E, k, cf in ((8192, 8, 2, 1.0), (4096, 64, 4, 0.5), (7, 8, 1, 1.0), (1000, 3, 2, 1.1)):
+    for T, E, k, cf in ((8192, 8, 2, 1.0), (4096, 64, 4, 0.5), (7, 8, 1, 1.0), (1000, 3, 2, 1.1),
+                        (1000, 10, 2, 0.9), (1000, 10, 1, 0.7), (333, 6, 3, 0.35)):
         s = M.make_shape(T, 64, 64, E, k, mode="tc_capacity", capacity_factor=cf)
-        assert M.capacity(s) == int((T / E) * float(ctypes.c_float(cf).value) * k)
+        assert M.capacity(s) == int((T / E) * cf * k) == O.tc_capacity(T, E, k, cf)
     assert M.capacity(M.make_shape(7, 64, 64, 8, 1, mode="tc_capacity")) == 0  # valid: drops all
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         with pytest.raises(M.MoEError) as ei:

@@ -133,9 +133,10 @@ def test_noisy_capacity_fp32_raw_gates(moe):
     run_noisy_case(moe, w, W.make_noise(w, wn_std=0.2), mode="tc_capacity", cf=0.6)
 
 
-def test_noisy_mixtral_layer_sampled(moe):
+def test_noisy_mixtral_layer_full(moe):
+    # every output of the full Mixtral-shaped layer with training noise
     w = W.MIXTRAL_LAYER
-    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02), sample=32)
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02))
 
 
 def test_zero_draw_is_bitwise_plain_routing(moe):
