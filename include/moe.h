@@ -221,6 +221,25 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
                        float* loss, float* z_loss, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_forward with the same arguments
+ * and results, minus the workspace. The workspace is a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (128 MiB) inside the library, one per GPU, held until the
+ * process ends; its address is looked up (hipGetSymbolAddress) on the first call on each
+ * device. The call allocates nothing (no hipMalloc, no library allocation).
+ *   - Shapes whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES return
+ *     MOE_ERR_WORKSPACE_TOO_SMALL before any HIP call (every other check is moe_forward's).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     intermediates: calls that overlap on one GPU (different streams, or threads) race and
+ *     must be ordered by the caller. Nothing in the array needs to start at zero.
+ *   - MOE_ERR_HIP also reports a failed lookup of the array's address. */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void* W_g,
+                               const float* b_g, const moe_noise* noise, const void* W_gate,
+                               const void* W_up, const void* W_down, float* y, int32_t* idx,
+                               float* w, float* probs, int32_t* counts, float* f, float* p,
+                               float* loss, float* z_loss, hipStream_t stream);
+
 /* Load-balancing statistics from router outputs (Mixture of Experts（MoE）の理論と実装,
  * load_balancing_loss; the Korean page's compute_load_balancing_loss), token choice:
  *   probs [T, E] fp32, idx [T, k] int32 (values in [0, E)) ->

@@ -16,7 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "moe_route", "moe_forward", "moe_aux_loss", "make_shape", "workspace_size", "capacity",
+    "moe_route", "moe_forward", "moe_forward_noalloc", "moe_aux_loss", "make_shape", "workspace_size", "capacity",
     "workspace_offset", "profile_enable", "profile_read", "stage_names", "SparseMoE",
     "MoEError", "load_library", "LIB_PATH",
 ]
@@ -34,7 +34,7 @@ WS_OFFSETS, WS_POS, WS_SRC, WS_XPERM, WS_H, WS_O = range(6)
 EXPORTS = (
     "moe_status_string", "moe_capacity", "moe_workspace_size", "moe_workspace_offset",
     "moe_route", "moe_forward", "moe_aux_loss", "moe_profile_enable", "moe_profile_read",
-    "moe_stage_name",
+    "moe_stage_name", "moe_forward_noalloc",
 )
 
 
@@ -87,10 +87,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.argtypes = [S, P, P, P, N, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                 ctypes.c_size_t, P]
     lib.moe_aux_loss.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_forward_noalloc.argtypes = [S, P, P, P, N, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.moe_profile_enable.argtypes = [I32]
     lib.moe_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]
     for name in ("moe_capacity", "moe_workspace_size", "moe_workspace_offset", "moe_route",
-                 "moe_forward", "moe_aux_loss", "moe_profile_enable", "moe_profile_read"):
+                 "moe_forward", "moe_forward_noalloc", "moe_aux_loss", "moe_profile_enable",
+                 "moe_profile_read"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -254,6 +256,30 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
     """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
     counts, (token choice) f, p, loss, and the router z-loss. eps (and W_noise) add
     the training noise of noisy top-k gating."""
+    return _forward(x, W_g, b_g, W_gate, W_up, W_down, k, mode, capacity_factor, renormalize,
+                    want_routing, want_probs, want_stats, want_z_loss, W_noise, eps, workspace, y,
+                    noalloc=False)
+
+
+def moe_forward_noalloc(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc",
+                        capacity_factor=1.0, renormalize=True, want_routing=True, want_probs=True,
+                        want_stats=True, want_z_loss=False, W_noise=None, eps=None,
+                        y=None) -> dict:
+    """moe_forward through the library's allocation-free entry point: its workspace is the
+    library's own fixed device array (NOALLOC_SCRATCH_BYTES per GPU), which every such
+    call on a GPU shares (overlapping calls race). The outputs requested here are still
+    allocated by torch unless passed in (y); the library call itself allocates nothing."""
+    return _forward(x, W_g, b_g, W_gate, W_up, W_down, k, mode, capacity_factor, renormalize,
+                    want_routing, want_probs, want_stats, want_z_loss, W_noise, eps, None, y,
+                    noalloc=True)
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def _forward(x, W_g, b_g, W_gate, W_up, W_down, k, mode, capacity_factor, renormalize,
+             want_routing, want_probs, want_stats, want_z_loss, W_noise, eps, workspace, y,
+             noalloc):
     T, d = _x_shape(x)
     if not isinstance(W_gate, torch.Tensor) or W_gate.dim() != 3:
         raise ValueError("W_gate must be [E, d_model, d_ff]")
@@ -273,7 +299,7 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
     _need(b_g, "b_g", torch.float32, dev)
     _need(y, "y", torch.float32, dev)
     shape = make_shape(T, d, f, E, k, mode, _dtype_name(x), renormalize, capacity_factor)
-    ws = _workspace(shape, dev, workspace)
+    ws = None if noalloc else _workspace(shape, dev, workspace)
     if y is None:
         y = torch.empty(T, d, dtype=torch.float32, device=dev)
     idx = w = probs = counts = fo = po = lo = None
@@ -294,11 +320,18 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
         lo = torch.empty(1, dtype=torch.float32, device=dev)
     z = torch.empty(1, dtype=torch.float32, device=dev) if want_z_loss else None
     noise = _noise(x, W_noise, eps, dev)
-    _check("moe_forward", load_library().moe_forward(
-        ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), noise, _ptr(W_gate), _ptr(W_up),
-        _ptr(W_down),
-        _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo), _ptr(po), _ptr(lo),
-        _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
+    lib = load_library()
+    if noalloc:
+        _check("moe_forward_noalloc", lib.moe_forward_noalloc(
+            ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), noise, _ptr(W_gate), _ptr(W_up),
+            _ptr(W_down), _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo),
+            _ptr(po), _ptr(lo), _ptr(z), _stream(dev)))
+    else:
+        _check("moe_forward", lib.moe_forward(
+            ctypes.byref(shape), _ptr(x), _ptr(W_g), _ptr(b_g), noise, _ptr(W_gate), _ptr(W_up),
+            _ptr(W_down),
+            _ptr(y), _ptr(idx), _ptr(w), _ptr(probs), _ptr(counts), _ptr(fo), _ptr(po), _ptr(lo),
+            _ptr(z), _ptr(ws), ws.numel(), _stream(dev)))
     return {"y": y, "idx": idx, "w": w, "probs": probs, "counts": counts, "f": fo, "p": po,
             "loss": lo, "z_loss": z, "workspace": ws, "shape": shape}
 

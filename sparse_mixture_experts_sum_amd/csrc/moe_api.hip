@@ -8,6 +8,7 @@
 #include <mutex>
 #include <vector>
 
+#include "api_internal.h"
 #include "kernels.h"
 #include "moe.h"
 
@@ -370,24 +371,45 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
-                       const moe_noise* noise, const void* W_gate, const void* W_up,
-                       const void* W_down, float* y,
-                       int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
-                       float* loss, float* z_loss, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+}  // extern "C"
+
+// Every host check of moe_forward except those of the workspace; *ws_need gets the
+// workspace size the shape needs. Shared with the allocation-free entry point.
+moe_status forward_host_checks(const moe_shape* shape, const void* x, const void* W_g,
+                               const moe_noise* noise, const void* W_gate, const void* W_up,
+                               const void* W_down, const float* y, const float* f,
+                               const float* p, const float* loss, size_t* ws_need) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   const moe_shape& s = *shape;
   if (s.mode == MOE_EXPERT_CHOICE && (f || p || loss)) return MOE_ERR_UNSUPPORTED;
   st = check_noise(s, noise);
   if (st != MOE_OK) return st;
-  if (s.T > 0 && (!x || !W_g || !W_gate || !W_up || !W_down || !y || !ws)) return MOE_ERR_NULL_ARG;
+  if (s.T > 0 && (!x || !W_g || !W_gate || !W_up || !W_down || !y)) return MOE_ERR_NULL_ARG;
   if (!aligned16(x) || !aligned16(W_g) || !aligned16(W_gate) || !aligned16(W_up) ||
-      !aligned16(W_down) || !aligned16(y) || !aligned16(ws))
+      !aligned16(W_down) || !aligned16(y))
     return MOE_ERR_MISALIGNED;
+  *ws_need = make_layout(s).total;
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
+                       const moe_noise* noise, const void* W_gate, const void* W_up,
+                       const void* W_down, float* y,
+                       int32_t* idx, float* w, float* probs, int32_t* counts, float* f, float* p,
+                       float* loss, float* z_loss, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  size_t need = 0;
+  moe_status st = forward_host_checks(shape, x, W_g, noise, W_gate, W_up, W_down, y, f, p, loss,
+                                      &need);
+  if (st != MOE_OK) return st;
+  const moe_shape& s = *shape;
+  if (s.T > 0 && !ws) return MOE_ERR_NULL_ARG;
+  if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   const Layout L = make_layout(s);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (s.T == 0) return zero_stats(s.E, f, p, loss, counts, z_loss, stream);
 
   const int bf = s.dtype == MOE_BF16;

@@ -101,6 +101,17 @@ int main(void) {
             MOE_ERR_NULL_ARG,
         "aux loss without f");
 
+  /* the allocation-free entry point refuses a layer larger than its scratch */
+  moe_shape big = shape(16384, 4096, 14336, 8, 2, MOE_TOKEN_CHOICE, 1.0);
+  check(moe_workspace_size(&big, &need) == MOE_OK && need > MOE_NOALLOC_SCRATCH_BYTES,
+        "Mixtral-size workspace exceeds the fixed scratch");
+  check(moe_forward_noalloc(&big, p, p, NULL, NULL, p, p, p, p, NULL, NULL, NULL, NULL, NULL,
+                            NULL, NULL, NULL, NULL) == MOE_ERR_WORKSPACE_TOO_SMALL,
+        "allocation-free forward refuses a layer larger than its scratch");
+  check(moe_forward_noalloc(&s, NULL, p, NULL, NULL, p, p, p, p, NULL, NULL, NULL, NULL, NULL,
+                            NULL, NULL, NULL, NULL) == MOE_ERR_NULL_ARG,
+        "allocation-free forward without x");
+
   /* profiling with nothing recorded */
   double ms[MOE_NUM_STAGES];
   int64_t n[MOE_NUM_STAGES];

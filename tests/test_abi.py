@@ -206,3 +206,30 @@ def test_profile_read_without_records(M):
     M.profile_enable(False)
     d = M.profile_read()
     assert set(d) == set(M.stage_names()) and all(v == (0.0, 0) for v in d.values())
+
+
+def test_noalloc_refusals_before_any_hip_call(M):
+    # the allocation-free entry point: moe_forward's argument checks, then the size of its
+    # fixed scratch (a shape needing more returns MOE_ERR_WORKSPACE_TOO_SMALL); none of
+    # these calls reaches a HIP call, so they run without a GPU
+    lib = M.load_library()
+    P = ctypes.c_void_p
+    good = P(4096)
+
+    def call(shape, **over):
+        a = dict(x=good, Wg=good, Wgate=good, Wup=good, Wdown=good, y=good, f=None)
+        a.update(over)
+        return lib.moe_forward_noalloc(ctypes.byref(shape), a["x"], a["Wg"], None, None,
+                                       a["Wgate"], a["Wup"], a["Wdown"], a["y"], None, None, None,
+                                       None, a["f"], None, None, None, None)
+
+    big = M.make_shape(16384, 4096, 14336, 8, 2)
+    assert M.workspace_size(big) > M.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 4
+    fits = M.make_shape(4096, 1024, 4096, 8, 2)
+    assert M.workspace_size(fits) <= M.NOALLOC_SCRATCH_BYTES
+    assert call(fits, x=None) == 1
+    assert call(fits, y=P(4100)) == 5
+    assert call(M.make_shape(64, 100, 64, 8, 2)) == 3
+    assert call(M.make_shape(64, 128, 256, 8, mode="ec"), f=P(8192)) == 3
+    assert lib.moe_forward_noalloc(None, *([None] * 16), None) == 1
