@@ -156,6 +156,55 @@ def parity_vs_oracle(w, inp, ref, n, y_dev, idx_dev):
     return out
 
 
+def reference_gemm(torch, w, group_rows, steps, warmup, gu_ms, dn_ms):
+    """torch's bf16 matmul (hipBLASLt) on the grouped GEMMs' problems, one matmul per expert:
+    gate and up as one [d, 2 d_ff] weight (the same FLOP as the fused gate/up GEMM, without its
+    SwiGLU epilogue) and the down projection; random bf16 operands of the same sizes. Timed
+    with one event pair around all experts' matmuls per step; median over the steps."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows = [int(n) for n in group_rows]
+    nmax = max(rows)
+    xa = torch.randn(nmax, w.d, device=dev, generator=g).to(torch.bfloat16)
+    ha = torch.randn(nmax, w.f, device=dev, generator=g).to(torch.bfloat16)
+    Wgu = torch.randn(w.E, w.d, 2 * w.f, device=dev, generator=g).to(torch.bfloat16)
+    Wd = torch.randn(w.E, w.f, w.d, device=dev, generator=g).to(torch.bfloat16)
+    out_gu = torch.empty(nmax, 2 * w.f, device=dev, dtype=torch.bfloat16)
+    out_d = torch.empty(nmax, w.d, device=dev, dtype=torch.bfloat16)
+
+    def run(which):
+        for e, n in enumerate(rows):
+            if n == 0:
+                continue
+            if which == "gu":
+                torch.matmul(xa[:n], Wgu[e], out=out_gu[:n])
+            else:
+                torch.matmul(ha[:n], Wd[e], out=out_d[:n])
+
+    res = {}
+    R = sum(rows)
+    for which, flop, ours in (("gate_up", 4.0 * w.d * w.f * R, gu_ms),
+                              ("down", 2.0 * w.f * w.d * R, dn_ms)):
+        key = "gu" if which == "gate_up" else "down"
+        for _ in range(warmup):
+            run(key)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, z in ev:
+            a.record()
+            run(key)
+            z.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(z) for a, z in ev]))
+        res[which] = {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                      "frac_of_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "ours_ms": round(ours, 4), "ours_over_reference": round(ms / ours, 4)}
+    res["what"] = ("torch.matmul bf16 per expert (hipBLASLt), bf16 output, same group sizes; "
+                   "gate/up as one [d, 2 d_ff] weight without the SwiGLU epilogue")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +218,10 @@ def main():
                     help="token-choice variant: an expert capacity (--cf), training noise "
                          "softplus(x W_noise) * eps, or the router z-loss as an extra output")
     ap.add_argument("--cf", type=float, default=1.0, help="capacity factor of --variant capacity")
+    ap.add_argument("--reference-gemm", action="store_true",
+                    help="after the layer, also time torch's bf16 matmul (hipBLASLt) on the same "
+                         "per-expert problems as the grouped GEMMs: x_e [n_e, d] @ [d, 2 d_ff] "
+                         "and h_e [n_e, d_ff] @ [d_ff, d], n_e the layer's group sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
@@ -319,6 +372,10 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if args.reference_gemm and w.dtype == "bf16":
+        line["reference_gemm"] = reference_gemm(torch, w, counts if w.mode != "ec" else
+                                                np.full(w.E, w.capacity), args.steps, args.warmup,
+                                                gu_ms, dn_ms)
     if args.variant != "plain":
         line["config"]["variant"] = args.variant
         if args.variant == "capacity":
