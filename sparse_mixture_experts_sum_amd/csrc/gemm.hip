@@ -7,11 +7,11 @@
 //
 // bf16 path (the hot path):
 //   * persistent workgroups (one per CU); all XCDs walk the experts in the same order,
-//     XCD x taking the x-th eighth of each expert's tiles listed N-tile-major, so that
-//     an XCD's CUs share weight columns in its L2 and the XCDs share the expert's rows
-//     in the memory-side cache; when every expert has few tiles, each XCD takes a
-//     contiguous run of experts instead, so that its CUs share operands in its L2
-//     (TileMap);
+//     XCD x owning the x-th eighth of each expert's output columns and walking them in
+//     blocks of a few columns, so that an XCD's concurrent tiles share both their rows
+//     and their weight columns in its L2 and the XCDs share the expert's rows in the
+//     memory-side cache; when every expert has few tiles, each XCD takes a contiguous
+//     run of experts instead (TileMap);
 //   * v_mfma_f32_32x32x16_bf16 with the weight fragment as the first operand, so that
 //     each lane's 16 accumulators are 4 runs of 4 consecutive output columns of one row
 //     (8- and 16-byte stores);
@@ -379,11 +379,17 @@ struct TileCoord {
   int e, row0, rows, n0;
 };
 
-// How the tiles are dealt to the eight XCDs (each XCD runs 32 at a time, one per CU;
-// every group's tiles are listed N-tile-major).
-//  - Split (groups with many tiles): the groups are processed one after another by all
-//    XCDs together, XCD x taking the x-th eighth of each group's list, i.e. mostly its
-//    own slice of the group's weight columns, for all of the group's rows.
+// How the tiles are dealt to the eight XCDs (each XCD runs 32 at a time, one per CU).
+//  - Columns (groups with many tiles, N-tiles a multiple of 8): the groups are processed one
+//    after another by all XCDs together; XCD x owns the x-th eighth of each group's output
+//    columns (NX = NT / 8 N-tiles) for all of the group's rows, and walks that rectangle in
+//    column blocks of GN N-tiles, rows outer and the block's columns inner. The 32 tiles an
+//    XCD runs together then cover about 32 / GN row tiles x GN column tiles, so they share
+//    both their rows and their weight columns in the XCD's L2 (about 32 / GN + GN tile
+//    operands fetched per 32 tiles, against 33 for one column of 32 row tiles).
+//  - Split (groups with many tiles, N-tiles not a multiple of 8; tiles listed
+//    N-tile-major): XCD x takes the x-th eighth of each group's list, i.e. mostly its own
+//    slice of the group's weight columns, for all of the group's rows.
 //  - Contiguous (every group small: split would give each XCD under 2 tiles of a group,
 //    or under 6 when the rows are gathered from x): the groups' lists are concatenated,
 //    groups that share a weight matrix next to each other, and XCD x takes the x-th
@@ -401,33 +407,40 @@ struct TileMap {
   bool contiguous;
   int base;      // contiguous: this XCD's first tile in the whole list
   int my_total;  // tiles of this XCD
+  int nx, gn;    // columns order: N-tiles per XCD and per column block (gn = 0: split order)
 };
 
 // CONTIG_OK: the shape allows the contiguous order (a group of one M-tile has NT tiles,
 // so NT at or above the threshold rules it out; the launch picks the instantiation).
 template <int BM, bool CONTIG_OK>
 __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int EW, int NT,
-                                                 int xcd, bool gathered) {
+                                                 int xcd, bool gathered, int gn) {
   TileMap m;
   m.NT = NT;
   m.xcd = xcd;
   m.E = E;
   m.EW = EW;
+  m.nx = NT / kXcds;
+  m.gn = gn;
   long long total = 0, maxpe = 0;
-  int split_total = 0;
+  int split_total = 0, col_total = 0;
   for (int e = 0; e < E; ++e) {
-    const long long pe = (long long)((offsets[e + 1] - offsets[e] + BM - 1) / BM) * NT;
+    const int mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+    const long long pe = (long long)mte * NT;
     if constexpr (CONTIG_OK) {
       total += pe;
       maxpe = pe > maxpe ? pe : maxpe;
     }
     split_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
+    col_total += mte * m.nx;
   }
   // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
   m.contiguous =
       CONTIG_OK && maxpe < (gathered ? kContigGatherTiles : kContigTiles) && E % EW == 0;
+  if (m.contiguous) m.gn = 0;
   m.base = m.contiguous ? (int)((total * xcd) >> 3) : 0;
-  m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base : split_total;
+  m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base
+                            : (m.gn > 0 ? col_total : split_total);
   return m;
 }
 
@@ -438,6 +451,28 @@ __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, 
                                                  int bn_out) {
   int e = 0, p = 0, mte = 1;
   if constexpr (!CONTIG) {
+    if (m.gn > 0) {
+      // columns order: this XCD's rectangle of group e is mte row tiles x nx column tiles,
+      // walked block by block (gn columns; only the last block may be narrower)
+      int acc_i = 0;
+      for (;; ++e) {
+        mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+        const int pe = mte * m.nx;
+        if (i < acc_i + pe) break;
+        acc_i += pe;
+      }
+      const int q = i - acc_i;
+      const int g = min(q / (mte * m.gn), (m.nx - 1) / m.gn);
+      const int r = q - g * mte * m.gn;
+      const int wg = min(m.gn, m.nx - g * m.gn);
+      const int mtl = r / wg;
+      TileCoord t;
+      t.e = e;
+      t.row0 = offsets[e] + mtl * BM;
+      t.rows = min(BM, offsets[e + 1] - t.row0);
+      t.n0 = (m.xcd * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
+      return t;
+    }
     int acc_i = 0;
     for (;; ++e) {
       mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
@@ -747,7 +782,7 @@ template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
-    void* __restrict__ out, void* __restrict__ out2) {
+    void* __restrict__ out, void* __restrict__ out2, int gn) {
   using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
   // one array per ring stage, so that the compiler can tell a stage's LDS reads from
   // the direct loads still in flight into the other stages
@@ -768,7 +803,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
   // this XCD's tiles (the order is described at TileMap)
-  const TileMap tm = make_tile_map<BM, CONTIG_OK>(offsets, E, EW, NT, xcd, gather != nullptr);
+  const TileMap tm = make_tile_map<BM, CONTIG_OK>(offsets, E, EW, NT, xcd, gather != nullptr, gn);
   const int my_total = tm.my_total;
   const int nk = K / G::BK;
   const int nk_total = nk;
@@ -884,6 +919,19 @@ int device_cu_count() {
   return cached[dev];
 }
 
+// Column-block width of the columns tile order (0: split order). An XCD's 32 concurrent tiles
+// span about 32 / GN row tiles and GN column tiles, so about 32 / GN + GN tile operands are
+// fetched per 32 tiles. Measured on the Mixtral-size layer (NX = 14 gate/up columns per XCD,
+// A/B in one process): widths 3 to 7 within 1% of each other, 4 the best, all 4-5% faster
+// than the split order; NX = 2 (its down projection): width 2 is 2% faster than 1 or split.
+// NX columns are cut into round(NX / 4) blocks.
+int column_block(int NT) {
+  if (NT % kXcds != 0) return 0;
+  const int nx = NT / kXcds;
+  const int nblocks = nx < 6 ? 1 : (nx + 2) / 4;
+  return (nx + nblocks - 1) / nblocks;
+}
+
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, const void* B1,
                        const int32_t* offsets, int E, int EW, int K, int N, void* out, void* out2,
@@ -892,14 +940,15 @@ hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, con
   // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
   // only below the threshold
   const int NT = N / (SWIGLU ? BNL / 2 : BNL);
+  const int gn = column_block(NT);
   if (NT < (gather ? kContigGatherTiles : kContigTiles))
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, true><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn);
   else
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, false><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2);
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn);
   return hipGetLastError();
 }
 
