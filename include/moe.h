@@ -224,7 +224,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): moe_forward with the same arguments
  * and results, minus the workspace. The workspace is a file-scope device array of
- * MOE_NOALLOC_SCRATCH_BYTES (128 MiB) inside the library, one per GPU, held until the
+ * MOE_NOALLOC_SCRATCH_BYTES (256 MiB) inside the library, one per GPU, held until the
  * process ends; its address is looked up (hipGetSymbolAddress) on the first call on each
  * device. The call allocates nothing (no hipMalloc, no library allocation).
  *   - Shapes whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES return
@@ -233,7 +233,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
  *     intermediates: calls that overlap on one GPU (different streams, or threads) race and
  *     must be ordered by the caller. Nothing in the array needs to start at zero.
  *   - MOE_ERR_HIP also reports a failed lookup of the array's address. */
-#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES (256u << 20)
 moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const void* W_g,
                                const float* b_g, const moe_noise* noise, const void* W_gate,
                                const void* W_up, const void* W_down, float* y, int32_t* idx,

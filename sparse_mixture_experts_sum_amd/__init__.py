@@ -274,7 +274,7 @@ def moe_forward_noalloc(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc",
                     noalloc=True)
 
 
-NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+NOALLOC_SCRATCH_BYTES = 256 << 20  # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
 
 
 def _forward(x, W_g, b_g, W_gate, W_up, W_down, k, mode, capacity_factor, renormalize,

@@ -122,9 +122,12 @@ __global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict_
                                                          const int32_t* __restrict__ offsets,
                                                          int cap, int renorm, int32_t* pos,
                                                          int32_t* src, float* w,
-                                                         char* __restrict__ x_perm) {
+                                                         char* __restrict__ x_perm,
+                                                         int32_t* sk_flags) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sk_flags && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < kStreamKSlots; i += blockDim.x) sk_flags[i] = 0;
   if (t >= T) return;
   const int R = T * k;
   int p = -1;
@@ -176,9 +179,12 @@ __global__ __launch_bounds__(256) void permute_tc_kernel(const char* __restrict_
 // One wave per routed row of expert choice: row e*C + c takes token idx[e, c].
 __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict__ x, size_t row_bytes,
                                                          int R, const int32_t* __restrict__ idx,
-                                                         int32_t* src, char* __restrict__ x_perm) {
+                                                         int32_t* src, char* __restrict__ x_perm,
+                                                         int32_t* sk_flags) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (sk_flags && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < kStreamKSlots; i += blockDim.x) sk_flags[i] = 0;
   if (r >= R) return;
   const int t = idx[r];
   if (lane == 0) src[r] = t;
@@ -200,24 +206,26 @@ hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
                              const int32_t* offsets, int cap, int renorm, int32_t* pos,
-                             int32_t* src, float* w, void* x_perm, hipStream_t s) {
+                             int32_t* src, float* w, void* x_perm, int32_t* sk_flags,
+                             hipStream_t s) {
   dim3 grid((T + 3) / 4), block(256);
   if (elt_bytes == 2)
     permute_tc_kernel<2><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
                                                 base, offsets, cap, renorm, pos, src, w,
-                                                static_cast<char*>(x_perm));
+                                                static_cast<char*>(x_perm), sk_flags);
   else
     permute_tc_kernel<4><<<grid, block, 0, s>>>(static_cast<const char*>(x), T, d, E, k, idx, lrank,
                                                 base, offsets, cap, renorm, pos, src, w,
-                                                static_cast<char*>(x_perm));
+                                                static_cast<char*>(x_perm), sk_flags);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
-                             const int32_t* idx, int32_t* src, void* x_perm, hipStream_t s) {
+                             const int32_t* idx, int32_t* src, void* x_perm, int32_t* sk_flags,
+                             hipStream_t s) {
   const int R = E * C;
   dim3 grid((R + 3) / 4), block(256);
   permute_ec_kernel<<<grid, block, 0, s>>>(static_cast<const char*>(x), (size_t)d * elt_bytes, R, idx,
-                                           src, static_cast<char*>(x_perm));
+                                           src, static_cast<char*>(x_perm), sk_flags);
   return hipGetLastError();
 }

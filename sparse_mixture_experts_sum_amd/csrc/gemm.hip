@@ -372,6 +372,8 @@ struct GemmArgs {
   int EW;                // weight matrices: group e uses matrix e % EW
   void* out;             // h (bf16) or o (fp32)
   void* out2;            // h_lo (bf16, SPLIT): the bf16 rounding residual of h
+  float* partial;        // stream-K partial sums, one slot per workgroup (nullptr: no stream-K)
+  int32_t* flags;        // stream-K: flags[slot] = 1 once that slot's partial is written
 };
 
 // One output tile: expert e, rows [row0, row0 + rows), output columns from n0.
@@ -563,21 +565,23 @@ __device__ __forceinline__ void gather_rows(int fetched, int ln, int (&gv)[G::A_
 
 // Direct-load sources of tile t for this lane (element offsets, without the K step). With
 // gathered rows, gv holds gather_rows(t).
+// ks0: the first K stage the loader's stage 0 stands for (a stream-K piece starts inside K).
 template <class G, bool SWIGLU, bool SPLIT, int BNL>
 __device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmArgs& a,
                                                                     const TileCoord& t, int ln,
-                                                                    int wave, int nk,
+                                                                    int wave, int nk, int ks0,
                                                                     const int (&gv)[G::A_PW]) {
   StageLoader<G, SWIGLU, SPLIT> ld;
   // gathered rows: offsets from A itself (the caller keeps every A offset below 2^31
   // elements); contiguous rows: offsets from the tile's first row
-  ld.Ab = a.gather ? a.A : a.A + (size_t)t.row0 * a.K;
+  const size_t koff = (size_t)ks0 * G::BK;
+  ld.Ab = (a.gather ? a.A : a.A + (size_t)t.row0 * a.K) + koff;
   ld.nk = nk;
   ld.N = a.N;
   ld.wave = wave;
   const int ew = t.e < a.EW ? t.e : t.e % a.EW;
-  const bf16* W0 = a.B0 + (size_t)ew * a.K * a.N;
-  const bf16* W1 = SWIGLU ? a.B1 + (size_t)ew * a.K * a.N : W0;
+  const bf16* W0 = a.B0 + (size_t)ew * a.K * a.N + koff * a.N;
+  const bf16* W1 = SWIGLU ? a.B1 + (size_t)ew * a.K * a.N + koff * a.N : W0;
 #pragma unroll
   for (int j = 0; j < G::A_PW; ++j) {
     const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
@@ -700,79 +704,293 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
   }
 }
 
-// This workgroup's tiles first, first + nslot, ... < my_total as one stream of K stages
-// through the ring (PipeStep): the last S steps of a tile refill the ring with the next
-// tile's first S stages, so those loads are in flight while this tile's epilogue runs
-// and the next tile only waits for its stage 0 to be read. Needs nk_total % S == 0, so
-// that stage s of every tile sits in ring buffer s % S. (The next tile's fragments are
-// read after the epilogue: holding them through it would leave too few registers.)
+// ---- stream-K ----------------------------------------------------------------------
+// An XCD's tile list (TileMap) is worked through by its nslot workgroups. Whole rounds of
+// tiles are dealt round-robin (data-parallel: tile slot, slot + nslot, ...). The tiles of the
+// last, partial round are not: their K extents, in chunks of 4 stages, are laid end to end
+// and cut into nslot equal runs, one per workgroup, so that every workgroup of the XCD ends
+// at the same time instead of most of them idling through a last round of few tiles. (When
+// that remainder has too few chunks for the workgroups, one whole round joins it.)
+//
+// A run covers whole tiles and pieces of tiles. The piece that starts a tile (its "head",
+// K from 0) belongs to the workgroup that owns the tile's output; the other pieces are
+// computed by the following workgroups of the XCD, whose run starts inside that tile: each
+// writes its fp32 accumulators to its own partial slot and raises its flag. The owner, after
+// its own K loop, waits for those flags and adds the partials in workgroup order, then runs
+// the epilogue. The sums therefore have one fixed order for a given shape and routing (the
+// result is deterministic). A workgroup holds at most one such non-head piece (the first
+// piece of its run), so one slot per workgroup suffices; a head waits only on workgroups
+// after its own, so every wait ends (and a spin limit bounds it in any case). The flags are
+// zero when the kernel starts (the dispatch clears them) and each owner clears the flags it
+// consumed, so they are zero again when it ends.
+constexpr int kSkSlots = 256;            // workgroups that may take stream-K pieces
+constexpr int kSkSpinLimit = 1 << 22;    // bound on a head's wait for one partial
+// Stream-K only for tiles of at least this many K stages: exchanging a piece costs a piece
+// about 9 us and its owner about 35 us (256 KB partials through L2, measured per workgroup
+// on the mid-size layer), which only a long tile's saved round repays. Measured (A/B in one
+// process): Mixtral-size down projection (448 stages) 3197 -> 3049 us; the 128-stage
+// (mid-size) and 44-stage (64-expert) down projections ran 30% and 22% slower with it.
+constexpr int kSkMinStages = 256;
+
+struct SkPlan {
+  int dp_tiles;   // XCD list positions [0, dp_tiles) are dealt round-robin as whole tiles
+  int nkc;        // chunks (4 K stages) per tile
+  int per;        // stream-K chunks per workgroup
+  int c_beg, c_end;  // this workgroup's chunk run inside the stream-K part
+};
+
+__device__ __forceinline__ SkPlan make_sk_plan(int my_total, int slot, int nslot, int nk,
+                                               bool enable) {
+  SkPlan p;
+  p.nkc = nk / 4;
+  p.dp_tiles = my_total;
+  p.per = 0;
+  int sk_chunks = 0;
+  if (enable && nk >= kSkMinStages && my_total % nslot != 0) {
+    int dp = my_total / nslot * nslot;
+    int rem = my_total - dp;
+    if (rem * p.nkc < 2 * nslot && dp >= nslot) {  // too few chunks: add a whole round
+      dp -= nslot;
+      rem += nslot;
+    }
+    p.dp_tiles = dp;
+    sk_chunks = rem * p.nkc;
+    p.per = (sk_chunks + nslot - 1) / nslot;
+  }
+  p.c_beg = min(slot * p.per, sk_chunks);
+  p.c_end = min(p.c_beg + p.per, sk_chunks);
+  return p;
+}
+
+enum { kWhole = 0, kHead = 1, kPiece = 2 };
+struct Item {
+  int tile;      // position in the XCD's tile list
+  int ks0, ks1;  // K stages [ks0, ks1)
+  int role;      // kWhole, kHead (owner of a split tile), kPiece (partial for an owner)
+};
+struct ItemIt {
+  int j;  // next round-robin round
+  int c;  // next stream-K chunk
+};
+
+__device__ __forceinline__ bool next_item(ItemIt& it, const SkPlan& p, int slot, int nslot,
+                                          int nk, Item& out) {
+  const int i = slot + it.j * nslot;
+  if (i < p.dp_tiles) {
+    out.tile = i;
+    out.ks0 = 0;
+    out.ks1 = nk;
+    out.role = kWhole;
+    ++it.j;
+    return true;
+  }
+  if (it.c < p.c_end) {
+    const int u = it.c / p.nkc, kc0 = it.c - u * p.nkc;
+    const int kc1 = min(p.nkc, kc0 + (p.c_end - it.c));
+    out.tile = p.dp_tiles + u;
+    out.ks0 = 4 * kc0;
+    out.ks1 = 4 * kc1;
+    out.role = kc0 > 0 ? kPiece : (kc1 < p.nkc ? kHead : kWhole);
+    it.c += kc1 - kc0;
+    return true;
+  }
+  return false;
+}
+
+// A partial slot holds one piece's fp32 accumulators as a row-major [BM, BNL] array. Only the
+// down projection splits tiles: its output is the accumulator itself, so the owner stores its
+// own piece to o like any tile and then adds the other pieces to o in workgroup order
+// (o = head + p1 + p2 + ...), with the accumulators no longer live. (The gate/up GEMM's SwiGLU
+// epilogue would need the sum before it, and a second epilogue path in those kernels costs
+// registers they do not have.)
+//
+// Where the partials travel: a piece and its owner always run on one XCD (their workgroup
+// ids differ by a multiple of 8, and workgroups are dealt round-robin over a partition's 8,
+// 4, 2 or 1 XCDs), so they share that XCD's L2. The partials therefore go through it: plain
+// stores (the per-CU L1 writes through to L2) and loads that bypass the L1 (sc0), after the
+// piece has waited for its stores to complete (vmcnt 0) and for its other waves (barrier)
+// before raising the flag. The flags themselves are device-scope relaxed atomics, so a wait
+// ends as soon as the flag is raised whatever the placement. (Device-scope accesses for the
+// partials, sc1, write through to memory and ran at about 10 GB/s per CU; a device-scope
+// release or acquire fence writes back or invalidates the whole L2 of the XCD.)
+constexpr int kCpolSc0 = 1;                  // cache-policy bits: miss in the per-CU L1
+constexpr int kBufRsrcWord3 = 0x00020000;    // raw buffer descriptor, dword 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const GemmArgs& a, int slot_id) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.partial + (size_t)slot_id * (kStreamKSlotBytes / 4),
+                                           0, (int)kStreamKSlotBytes, kBufRsrcWord3);
+}
+
+template <class G>
+__device__ __forceinline__ void put_partial(const GemmArgs& a, int bid, int ln, int wm, int wn,
+                                            const f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr int BNL = G::WNL * G::WGN;
+  const __amdgpu_buffer_rsrc_t r = partial_rsrc(a, bid);
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int m = wm * G::WM + mb * 32 + (ln & 31);
+#pragma unroll
+    for (int nb = 0; nb < G::NBW; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (ln >> 5);
+        const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
+                         acc[nb][mb][4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (m * BNL + ncol) * 4, 0, 0);
+      }
+  }
+  wait_vmcnt<0>();   // this thread's partial stores have reached the L2
+  __syncthreads();   // and every other thread's
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.flags + bid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The owner of a split tile, after storing its own piece to o: for each later workgroup w of
+// this XCD whose run covers part of the tile (w = slot + 1 .. w_last) wait for its flag and
+// clear it; then o += p_{slot+1} + p_{slot+2} + ... element by element, in that order, each
+// lane over the elements it stored (store_tile's order, rows of the tile only).
+template <class G>
+__device__ __forceinline__ void add_partials(const GemmArgs& a, const TileCoord& t, int xcd,
+                                             int slot, int w_last, int wm, int wn) {
+  constexpr int BNL = G::WNL * G::WGN;
+  if (threadIdx.x == 0) {
+    for (int w = slot + 1; w <= w_last; ++w) {
+      const int wb = w * kXcds + xcd;
+      int n = 0;
+      while (__hip_atomic_load(a.flags + wb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+             ++n < kSkSpinLimit)
+        __builtin_amdgcn_s_sleep(8);
+      __hip_atomic_store(a.flags + wb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  wait_vmcnt<0>();  // this thread's own o stores have completed
+  __syncthreads();
+  const int ln = fresh_lane();
+  float* o = static_cast<float*>(a.out);
+  // per 32-row block: all 16 of the lane's o chunks, then each partial's 16 chunks, are
+  // loaded before they are added
+  constexpr int NQ = G::NBW * 4;
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int m = wm * G::WM + mb * 32 + (ln & 31);
+    const bool row_ok = m < t.rows;
+    const size_t rowoff = (size_t)(t.row0 + (row_ok ? m : 0)) * a.N + t.n0;
+    f32x4 v[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
+      v[i] = row_ok ? *reinterpret_cast<const f32x4*>(o + rowoff + ncol) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int w = slot + 1; w <= w_last; ++w) {
+      const __amdgpu_buffer_rsrc_t r = partial_rsrc(a, w * kXcds + xcd);
+      f32x4 p[NQ];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
+        p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (m * BNL + ncol) * 4, 0, kCpolSc0);
+      }
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) v[i] += p[i];
+    }
+    if (row_ok) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
+        *reinterpret_cast<f32x4*>(o + rowoff + ncol) = v[i];
+      }
+    }
+  }
+}
+
+// This workgroup's work items (whole tiles, then its stream-K run) as one stream of K stages
+// through the ring (PipeStep): the last S steps of an item refill the ring with the next
+// item's first S stages, so those loads are in flight while this item's epilogue runs and
+// the next item only waits for its stage 0 to be read. Every item's stage count is a
+// multiple of S (whole chunks), so that stage s of every item sits in ring buffer s % S.
+// (The next item's fragments are read after the epilogue: holding them through it would
+// leave too few registers.)
 // (TAG: see k_loop)
 template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL, bool CONTIG, int TAG>
-__device__ __forceinline__ void pipe_stream(const GemmArgs& a, int first, const TileMap& tm,
-                                            int nslot, int wave, int wm, int wn,
-                                            int nk, int nk_total, char* const (&ring)[G::STAGES]) {
+__device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm, int slot,
+                                            int nslot, int wave, int wm, int wn, int nk,
+                                            char* const (&ring)[G::STAGES]) {
   constexpr int S = G::STAGES;
   static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
+  const SkPlan sp = make_sk_plan(tm.my_total, slot, nslot, nk, !SWIGLU && a.partial != nullptr);
+  ItemIt it{0, sp.c_beg};
+  Item cur;
+  if (!next_item(it, sp, slot, nslot, nk, cur)) return;
   int ln = fresh_lane();
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-  const int my_total = tm.my_total;
-  TileCoord t = locate_tile<BM, CONTIG>(first, a.offsets, tm, G::BN_OUT);
+  TileCoord t = locate_tile<BM, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
-  StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk, gv);
+  StageLoader<G, SWIGLU, SPLIT> ld =
+      make_loader<G, SWIGLU, SPLIT, BNL>(a, t, ln, wave, nk, cur.ks0, gv);
 #define MOE_SSTEP(J, RL, RSTAGE)                                                             \
   PipeStep<G, SWIGLU, SPLIT, J, true>::run(0, true, true, RL, RSTAGE, ring, a_frag, b_frag, acc, \
                                        (J) % 2 ? F1 : F0, (J) % 2 ? F0 : F1)
-  // prologue of the first tile: the whole ring in flight
+  // prologue of the first item: the whole ring in flight
 #pragma unroll
   for (int i = 0; i < S; ++i) ld.issue(i, ring[i]);
-  for (int i = first;;) {
-    // accumulators and fragments are per tile (none is carried around this loop)
+  for (;;) {
+    // accumulators and fragments are per item (none is carried around this loop)
     f32x16 acc[G::NBW][G::MB];
     zero_acc<G>(acc);
     Frags<G> F0, F1;
-    // stage 0's fragments (the ring holds stages 0 .. S-1 of this tile, stage 0 is the
-    // oldest load in flight; epilogue stores of the previous tile may be newer)
+    // stage 0's fragments (the ring holds stages 0 .. S-1 of this item, stage 0 is the
+    // oldest load in flight; epilogue stores of the previous item may be newer)
     wait_vmcnt<(S - 1) * G::LPS>();
     sync_point();
 #pragma unroll
     for (int r = 0; r < G::SUB * G::MB + 2 * G::SUB * G::NBW; ++r)
       read_frag<G>(r, ring[0], a_frag, b_frag, F0);
-    // the next tile (this one again after the last: its loads below are unused but in
+    // the next item (this one again after the last: its loads below are unused but in
     // bounds)
-    const int inext = i + nslot;
-    const bool has_next = inext < my_total;
-    const TileCoord tn = has_next ? locate_tile<BM, CONTIG>(inext, a.offsets, tm, G::BN_OUT) : t;
+    Item nx = cur;
+    const bool has_next = next_item(it, sp, slot, nslot, nk, nx);
+    const TileCoord tn = has_next ? locate_tile<BM, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
     const int gnext = (SWIGLU && a.gather) ? gather_fetch<G>(a, tn, fresh_lane(), wave) : 0;
+    const int nkt = cur.ks1 - cur.ks0;
     int kt = 0;
-    for (; kt + 2 * S <= nk_total; kt += S) {  // refills from this tile
+    for (; kt + 2 * S <= nkt; kt += S) {  // refills from this item
       MOE_SSTEP(0, ld, kt + S);
       MOE_SSTEP(1, ld, kt + S + 1);
       MOE_SSTEP(2, ld, kt + S + 2);
       MOE_SSTEP(3, ld, kt + S + 3);
     }
-    // kt == nk_total - S: the last S steps refill the ring with the next tile's first S
-    // stages; after the last tile they load this tile's first stages again, unused but
+    // kt == nkt - S: the last S steps refill the ring with the next item's first S
+    // stages; after the last item they load this item's first stages again, unused but
     // in bounds, so that every path into the loop above has the same loads in flight
     // (the compiler then needs no extra wait there). The last step reads nothing.
     ln = fresh_lane();
     if (SWIGLU && a.gather) gather_rows<G>(gnext, ln, gv);
-    const StageLoader<G, SWIGLU, SPLIT> ldn = make_loader<G, SWIGLU, SPLIT, BNL>(a, tn, ln, wave, nk, gv);
+    const StageLoader<G, SWIGLU, SPLIT> ldn =
+        make_loader<G, SWIGLU, SPLIT, BNL>(a, tn, ln, wave, nk, nx.ks0, gv);
     MOE_SSTEP(0, ldn, 0);
     MOE_SSTEP(1, ldn, 1);
     MOE_SSTEP(2, ldn, 2);
     PipeStep<G, SWIGLU, SPLIT, 3, false>::run(S - 2, false, true, ldn, 3, ring, a_frag, b_frag,
                                               acc, F1, F0);
     ln = fresh_lane();
-    store_tile<G, SWIGLU, SPLIT>(a, t, ln, wm, wn, acc);
+    if (!SWIGLU && cur.role == kPiece) {
+      put_partial<G>(a, (int)blockIdx.x, ln, wm, wn, acc);
+    } else {
+      store_tile<G, SWIGLU, SPLIT>(a, t, ln, wm, wn, acc);
+      if (!SWIGLU && cur.role == kHead) {
+        // the workgroups whose runs cover the rest of this tile
+        const int u = cur.tile - sp.dp_tiles;
+        add_partials<G>(a, t, (int)blockIdx.x & (kXcds - 1), slot,
+                        ((u + 1) * sp.nkc - 1) / sp.per, wm, wn);
+      }
+    }
     if (!has_next) break;
     t = tn;
     ld = ldn;
-    i = inext;
+    cur = nx;
   }
 #undef MOE_SSTEP
   wait_vmcnt<0>();
@@ -782,7 +1000,8 @@ template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
-    void* __restrict__ out, void* __restrict__ out2, int gn) {
+    void* __restrict__ out, void* __restrict__ out2, int gn, float* __restrict__ partial,
+    int32_t* __restrict__ flags) {
   using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
   // one array per ring stage, so that the compiler can tell a stage's LDS reads from
   // the direct loads still in flight into the other stages
@@ -808,17 +1027,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int nk = K / G::BK;
   const int nk_total = nk;
 
-  const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, EW, out, out2};
+  const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, EW, out, out2,
+                      PIPE && gridDim.x <= kSkSlots ? partial : nullptr, flags};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
-      if (slot < my_total) {
-        if (CONTIG_OK && tm.contiguous)
-          pipe_stream<G, SWIGLU, SPLIT, BM, BNL, CONTIG_OK, CONTIG_OK>(args, slot, tm, nslot, wave,
-                                                                       wm, wn, nk, nk_total, ring);
-        else
-          pipe_stream<G, SWIGLU, SPLIT, BM, BNL, false, CONTIG_OK>(args, slot, tm, nslot, wave, wm,
-                                                                   wn, nk, nk_total, ring);
-      }
+      if (CONTIG_OK && tm.contiguous)
+        pipe_stream<G, SWIGLU, SPLIT, BM, BNL, CONTIG_OK, CONTIG_OK>(args, tm, slot, nslot, wave,
+                                                                     wm, wn, nk, ring);
+      else
+        pipe_stream<G, SWIGLU, SPLIT, BM, BNL, false, CONTIG_OK>(args, tm, slot, nslot, wave, wm,
+                                                                 wn, nk, ring);
       return;
     }
   }
@@ -831,7 +1049,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
                             : locate_tile<BM, false>(i, offsets, tm, G::BN_OUT);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
-    const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, gv);
+    const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, 0, gv);
     f32x16 acc[G::NBW][G::MB];
     zero_acc<G>(acc);
 
@@ -935,7 +1153,7 @@ int column_block(int NT) {
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, const void* B1,
                        const int32_t* offsets, int E, int EW, int K, int N, void* out, void* out2,
-                       hipStream_t s) {
+                       const StreamK& sk, hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
   // only below the threshold
@@ -944,45 +1162,45 @@ hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, con
   if (NT < (gather ? kContigGatherTiles : kContigTiles))
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, true><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn);
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn, sk.partial, sk.flags);
   else
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, false><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn);
+        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn, sk.partial, sk.flags);
   return hipGetLastError();
 }
 
 template <bool SPLIT>
 hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate, const void* Wup,
                        const int32_t* offsets, int E, int d, int f, void* h, void* h_lo,
-                       hipStream_t s) {
+                       const StreamK& sk, hipStream_t s) {
   if (f % 128 == 0)
     return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d,
-                                                         f, h, h_lo, s);
+                                                         f, h, h_lo, sk, s);
   return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d, f, h, h_lo,
-                                               s);
+                                               sk, s);
 }
 
 hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int EW,
-                     int f, int d, float* o, hipStream_t s) {
+                     int f, int d, float* o, const StreamK& sk, hipStream_t s) {
   if (d % 256 == 0)
     return launch_bf16<256, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW,
-                                                          f, d, o, nullptr, s);
+                                                          f, d, o, nullptr, sk, s);
   if (d % 128 == 0)
     return launch_bf16<256, 128, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d,
-                                                  o, nullptr, s);
+                                                  o, nullptr, sk, s);
   return launch_bf16<256, 64, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d, o,
-                                               nullptr, s);
+                                               nullptr, sk, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_gateup(int bf16in, const void* xp, const int32_t* gather, const void* Wgate,
                               const void* Wup, const int32_t* offsets, int E, int R_max, int d,
-                              int f, void* h, void* h_lo, hipStream_t s) {
+                              int f, void* h, void* h_lo, const StreamK& sk, hipStream_t s) {
   if (bf16in) {
-    if (h_lo) return gateup_bf16<true>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo, s);
-    return gateup_bf16<false>(xp, gather, Wgate, Wup, offsets, E, d, f, h, nullptr, s);
+    if (h_lo) return gateup_bf16<true>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo, sk, s);
+    return gateup_bf16<false>(xp, gather, Wgate, Wup, offsets, E, d, f, h, nullptr, sk, s);
   }
   if (gather) return hipErrorInvalidValue;  // the fp32 path reads copied rows
   dim3 grid(f / 64, R_max / 64 + E);
@@ -994,8 +1212,9 @@ hipError_t launch_gemm_gateup(int bf16in, const void* xp, const int32_t* gather,
 }
 
 hipError_t launch_gemm_down(int bf16in, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int EW, int R_max, int f, int d, float* o, hipStream_t s) {
-  if (bf16in) return down_bf16(h, Wdown, offsets, E, EW, f, d, o, s);
+                            int E, int EW, int R_max, int f, int d, float* o, const StreamK& sk,
+                            hipStream_t s) {
+  if (bf16in) return down_bf16(h, Wdown, offsets, E, EW, f, d, o, sk, s);
   if (EW != E) return hipErrorInvalidValue;  // the fp32 path runs one matrix per group
   dim3 grid(d / 64, R_max / 64 + E);
   gemm_f32_kernel<false><<<grid, 256, 0, s>>>(static_cast<const float*>(h),

@@ -63,16 +63,30 @@ hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s);
 // Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t]. With a
 // capacity (cap < INT_MAX) slots ranked cap or later in their expert get pos = -1 and
 // weight 0, and the token's kept weights w are renormalised when renorm is set.
-// x_perm == nullptr: slots and weights only.
+// x_perm == nullptr: slots and weights only. sk_flags (or nullptr): the GEMMs' stream-K
+// flags, cleared here.
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
                              const int32_t* offsets, int cap, int renorm, int32_t* pos,
-                             int32_t* src, float* w, void* x_perm, hipStream_t s);
+                             int32_t* src, float* w, void* x_perm, int32_t* sk_flags,
+                             hipStream_t s);
 
 // Expert choice: row e*C + c takes token idx[e, c] (src; the row copy into x_perm only when
-// x_perm is not nullptr).
+// x_perm is not nullptr). sk_flags as for launch_permute_tc.
 hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
-                             const int32_t* idx, int32_t* src, void* x_perm, hipStream_t s);
+                             const int32_t* idx, int32_t* src, void* x_perm, int32_t* sk_flags,
+                             hipStream_t s);
+
+// Stream-K scratch of the bf16 grouped GEMMs (in the caller's workspace): partial sums, one
+// slot of kStreamKSlotBytes per workgroup, and one int32 flag per workgroup, which must be
+// zero when a GEMM starts (the permute kernels clear them; each GEMM leaves them zero).
+// partial == nullptr: no stream-K (every tile whole).
+constexpr int kStreamKSlots = 256;
+constexpr size_t kStreamKSlotBytes = (size_t)256 * 256 * 4;  // a 256 x 256 fp32 tile
+struct StreamK {
+  float* partial;   // [kStreamKSlots * kStreamKSlotBytes / 4]
+  int32_t* flags;   // [kStreamKSlots]
+};
 
 // Grouped GEMMs over expert-contiguous rows (group e = rows [offsets[e], offsets[e+1])).
 //   gate/up: h[r] = silu(A[r] W_gate[e]) * (A[r] W_up[e])  -> h [R, f]
@@ -84,9 +98,10 @@ hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
 // residual rows run as E more groups, EW = E, E' = 2E). R_max bounds the routed rows.
 hipError_t launch_gemm_gateup(int bf16, const void* xp, const int32_t* gather, const void* Wgate,
                               const void* Wup, const int32_t* offsets, int E, int R_max, int d,
-                              int f, void* h, void* h_lo, hipStream_t s);
+                              int f, void* h, void* h_lo, const StreamK& sk, hipStream_t s);
 hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int EW, int R_max, int f, int d, float* o, hipStream_t s);
+                            int E, int EW, int R_max, int f, int d, float* o, const StreamK& sk,
+                            hipStream_t s);
 
 // y[t] = sum_j w[t,j] * o[pos[t,j]]  (j in slot order)
 hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,

@@ -22,7 +22,8 @@ struct Layout {
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
          offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
-         o_lo = 0, total = 0;
+         o_lo = 0, sk_partial = 0, sk_flags = 0, total = 0;
+  bool stream_k = false;  // bf16: the GEMMs' stream-K partial slots and flags exist
   int ngroups = 0;  // groups of the down projection: E, or 2E with the residual rows
   bool xperm = false;  // rows copied into x_perm (else the gate/up GEMM gathers them from x)
 };
@@ -139,6 +140,13 @@ Layout make_layout(const moe_shape& s) {
   if (resid) L.h_lo = L.h + (size_t)L.R * f * eb;
   L.o = take((size_t)hrows * d * 4);
   if (resid) L.o_lo = L.o + (size_t)L.R * d * 4;
+  // bf16 GEMMs split the tiles of their last partial round along K (stream-K): one fp32
+  // partial slot and one flag per workgroup
+  L.stream_k = s.dtype == MOE_BF16;
+  if (L.stream_k) {
+    L.sk_partial = take((size_t)kStreamKSlots * kStreamKSlotBytes);
+    L.sk_flags = take((size_t)kStreamKSlots * 4);
+  }
   L.total = cur;
   return L;
 }
@@ -367,7 +375,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
                                s.k, idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.base),
                                at<int32_t>(ws, L.offsets), tc_cap_limit(s), s.renormalize,
                                at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w, nullptr,
-                               stream));
+                               nullptr, stream));
   return MOE_OK;
 }
 
@@ -426,22 +434,26 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   if (st != MOE_OK) return st;
   void* x_perm = L.xperm ? at<void>(ws, L.x_perm) : nullptr;  // nullptr: no row copies
   const int32_t* src = at<int32_t>(ws, L.src);
+  const StreamK sk{L.stream_k ? at<float>(ws, L.sk_partial) : nullptr,
+                   L.stream_k ? at<int32_t>(ws, L.sk_flags) : nullptr};
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_PERMUTE,
                launch_permute_tc(x, eb, T, d, E, s.k, idx_b, at<int32_t>(ws, L.lrank),
                                  at<int32_t>(ws, L.base), offsets, tc_cap_limit(s), s.renormalize,
                                  at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w_b, x_perm,
-                                 stream));
+                                 sk.flags, stream));
   } else {
     MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
-                                                    at<int32_t>(ws, L.src), x_perm, stream));
+                                                    at<int32_t>(ws, L.src), x_perm, sk.flags,
+                                                    stream));
   }
   MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
              launch_gemm_gateup(bf, x_perm ? x_perm : x, x_perm ? nullptr : src, W_gate, W_up,
-                                offsets, E, R, d, ff, at<void>(ws, L.h), h_lo, stream));
+                                offsets, E, R, d, ff, at<void>(ws, L.h), h_lo, sk, stream));
   MOE_LAUNCH(MOE_STAGE_GEMM_DOWN,
              launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, L.ngroups, E,
-                              (int)(L.h_lo ? 2 * L.R : L.R), ff, d, at<float>(ws, L.o), stream));
+                              (int)(L.h_lo ? 2 * L.R : L.R), ff, d, at<float>(ws, L.o), sk,
+                              stream));
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));

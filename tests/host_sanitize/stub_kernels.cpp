@@ -80,31 +80,35 @@ hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t) {
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
                              const int32_t* offsets, int cap, int renorm, int32_t* pos,
-                             int32_t* src, float* w, void* x_perm, hipStream_t) {
+                             int32_t* src, float* w, void* x_perm, int32_t* sk_flags,
+                             hipStream_t) {
   ++g_launches;
   const size_t R = (size_t)T * k;
   inside(pos, R * 4, "permute pos");
   inside(src, R * 4, "permute src");
   inside(x_perm, R * d * elt_bytes, "permute rows");
+  inside(sk_flags, kStreamKSlots * 4, "stream-K flags");
   (void)x, (void)E, (void)idx, (void)lrank, (void)base, (void)offsets, (void)cap, (void)renorm,
       (void)w;
   return hipSuccess;
 }
 
 hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
-                             const int32_t* idx, int32_t* src, void* x_perm, hipStream_t) {
+                             const int32_t* idx, int32_t* src, void* x_perm, int32_t* sk_flags,
+                             hipStream_t) {
   ++g_launches;
   const size_t R = (size_t)E * C;
   inside(idx, R * 4, "permute idx");
   inside(src, R * 4, "permute src");
   inside(x_perm, R * d * elt_bytes, "permute rows");
+  inside(sk_flags, kStreamKSlots * 4, "stream-K flags");
   (void)x;
   return hipSuccess;
 }
 
 hipError_t launch_gemm_gateup(int bf16, const void* xp, const int32_t* gather, const void* Wgate,
                               const void* Wup, const int32_t* offsets, int E, int R_max, int d,
-                              int f, void* h, void* h_lo, hipStream_t) {
+                              int f, void* h, void* h_lo, const StreamK& sk, hipStream_t) {
   ++g_launches;
   const size_t eb = bf16 ? 2 : 4;
   inside(xp, (size_t)R_max * d * eb, "gate/up rows");
@@ -112,17 +116,22 @@ hipError_t launch_gemm_gateup(int bf16, const void* xp, const int32_t* gather, c
   inside(offsets, (size_t)(E + 1) * 4, "gate/up offsets");
   inside(h, (size_t)R_max * f * eb, "gate/up h");
   inside(h_lo, (size_t)R_max * f * eb, "gate/up h residual");
+  inside(sk.partial, kStreamKSlots * kStreamKSlotBytes, "stream-K partials");
+  inside(sk.flags, kStreamKSlots * 4, "stream-K flags");
   (void)Wgate, (void)Wup;
   return hipSuccess;
 }
 
 hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int EW, int R_max, int f, int d, float* o, hipStream_t) {
+                            int E, int EW, int R_max, int f, int d, float* o, const StreamK& sk,
+                            hipStream_t) {
   ++g_launches;
   const size_t eb = bf16 ? 2 : 4;
   inside(h, (size_t)R_max * f * eb, "down h");
   inside(offsets, (size_t)(E + 1) * 4, "down offsets");
   inside(o, (size_t)R_max * d * 4, "down o");
+  inside(sk.partial, kStreamKSlots * kStreamKSlotBytes, "stream-K partials");
+  inside(sk.flags, kStreamKSlots * 4, "stream-K flags");
   (void)Wdown, (void)EW;
   return hipSuccess;
 }

@@ -155,9 +155,16 @@ def test_workspace_offsets_are_inside(M):
         s32 = M.make_shape(1000, 256, 512, 8, 2, mode=mode, dtype="fp32")
         off = M.workspace_offset(s32, M.WS_XPERM)
         assert 0 <= off < M.workspace_size(s32) and off % 256 == 0
-    # the gathered layout needs no copy buffer: the bf16 workspace is smaller by R * d * 2
-    bf = M.workspace_size(M.make_shape(1000, 256, 512, 8, 2))
-    assert bf < M.workspace_size(M.make_shape(1000, 256, 512, 8, 2, dtype="fp32"))
+    # the gathered layout needs no copy buffer: past the shared regions the bf16 workspace
+    # holds no x_perm (its h follows src directly), and bf16 adds the down projection's
+    # stream-K partial slots (256 x 256 KB) and flags
+    s16 = M.make_shape(1000, 256, 512, 8, 2)
+    s32 = M.make_shape(1000, 256, 512, 8, 2, dtype="fp32")
+    R, d = 2000, 256
+    assert M.workspace_offset(s32, M.WS_H) - M.workspace_offset(s32, M.WS_SRC) >= R * d * 4
+    assert M.workspace_offset(s16, M.WS_H) - M.workspace_offset(s16, M.WS_SRC) < 256 * 64
+    sk = 256 * 256 * 256 * 4 + 256 * 4
+    assert M.workspace_size(s16) >= M.workspace_offset(s16, M.WS_O) + R * d * 4 + sk
     with pytest.raises(M.MoEError):
         M.workspace_offset(M.make_shape(1000, 256, 512, 8, 2, mode="ec"), M.WS_POS)
 

@@ -219,6 +219,22 @@ def test_dispatch_scan_many_blocks(moe):
                               seed=(42, 341)))
 
 
+@pytest.mark.parametrize("T,d,f,E,k", [(300, 256, 8192, 2, 2), (1500, 512, 8192, 4, 2),
+                                       (700, 256, 16384, 3, 1), (5000, 256, 8192, 8, 2)])
+def test_stream_k_down_projection(moe, T, d, f, E, k):
+    # down projections over d_ff >= 8192 (256 K stages or more): the last round's tiles are
+    # split along K over every workgroup of an XCD (T=300: a tile in up to 32 pieces; T=5000:
+    # several whole rounds first), and the owner adds the pieces' partial sums to its own in
+    # a fixed order; outputs against the oracle, and a second call bitwise equal to the first
+    w = W.custom(f"sk_T{T}_d{d}_f{f}", T=T, d=d, f=f, E=E, k=k, bias_std=0.3, seed=(42, 700 + T))
+    out, inp = run_tc_case(moe, w)
+    dev = PR.device_inputs(inp, w)
+    again = moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                            k=k)
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], again["y"])
+
+
 def test_determinism_bitwise(moe):
     w = W.custom("det", T=777, d=256, f=256, E=8, k=2, seed=(42, 207))
     inp = W.make_inputs(w)
