@@ -172,7 +172,7 @@ __global__ __launch_bounds__(1024) void aux_final_kernel(const int32_t* __restri
   }
   __syncthreads();
   if (counts && threadIdx.x < E) counts[threadIdx.x] = cnt[threadIdx.x];
-  aux_stats_block(cnt, blk_psum, blk_zsum, nblk, T, E, k, f, p, loss, z_loss);
+  aux_stats_block<1>(cnt, blk_psum, blk_zsum, nblk, T, E, k, f, p, loss, z_loss);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {

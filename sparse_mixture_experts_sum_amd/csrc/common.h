@@ -93,39 +93,57 @@ __device__ __forceinline__ void block_expert_sums(float (&v)[NMAX], int nper, in
 //   f[e] = cnt[e] / T, p[e] = (sum over blocks of blk_psum[b, e]) / T,
 //   loss = E * sum_e (f[e] / k) * p[e], z_loss = (sum over blocks of blk_zsum[b]) / T.
 // One fixed order whichever kernel calls it: item i (expert i < E, the z-loss for i = E)
-// belongs to wave i % 16, whose lane l adds blocks l, l + 64, ... in double, then an xor
-// tree over the lanes; thread 0 adds the loss terms in expert order. cnt: the E
-// assignment totals, in LDS, visible to all threads. 1024 threads; every thread must call
-// it. Null outputs are skipped.
-__device__ inline void aux_stats_block(const int* cnt, const float* __restrict__ blk_psum,
-                                       const float* __restrict__ blk_zsum, int nblk, int T, int E,
-                                       int k, float* f, float* p, float* loss, float* z_loss) {
+// belongs to wave i % (waves of the block), whose lane l adds blocks l, l + 64, ... in
+// double, then an xor tree over the lanes; thread 0 adds the loss terms in expert order.
+// The bits of every item depend only on the lane it is summed in, so blocks of any number
+// of waves give the same results. A wave takes IPR of its items at a time: eight loads per
+// lane and item in flight (the partials were just written by other CUs, so each load waits
+// for memory), then each item's values added in block order; IPR changes no bit, only the
+// registers it takes (4 for the 256-thread dispatch, 1 where 1024 threads leave 128
+// registers each). cnt: the E assignment totals, in LDS, visible to all threads. A multiple
+// of 64 threads, at least 128; every thread must call it. Null outputs are skipped.
+template <int IPR>
+__device__ __forceinline__ void aux_stats_block(const int* cnt, const float* __restrict__ blk_psum,
+                                                const float* __restrict__ blk_zsum, int nblk,
+                                                int T, int E, int k, float* f, float* p,
+                                                float* loss, float* z_loss) {
   __shared__ double item[65];
   __shared__ double term[64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = wave; i <= E; i += 16) {
-    double v = 0.0;
-    const float* src = i < E ? blk_psum : blk_zsum;
-    const size_t stride = i < E ? (size_t)E : 1;
-    if (src) {
-      if (i < E) src += i;
-      // eight loads in flight per lane, then added in block order (the partials were
-      // just written by other CUs, so each load waits for memory)
-      for (int b0 = lane; b0 < nblk; b0 += 64 * 8) {
-        float x8[8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  for (int i0 = wave; i0 <= E; i0 += nwaves * IPR) {
+    double v[IPR];
+    const float* src[IPR];
+    size_t stride[IPR];
+#pragma unroll
+    for (int r = 0; r < IPR; ++r) {
+      const int i = i0 + r * nwaves;
+      v[r] = 0.0;
+      src[r] = i > E ? nullptr : (i < E ? (blk_psum ? blk_psum + i : nullptr) : blk_zsum);
+      stride[r] = i < E ? (size_t)E : 1;
+    }
+    for (int b0 = lane; b0 < nblk; b0 += 64 * 8) {
+      float x8[IPR][8];
+#pragma unroll
+      for (int r = 0; r < IPR; ++r)
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int b = b0 + 64 * u;
-          x8[u] = b < nblk ? src[(size_t)b * stride] : 0.f;
+          x8[r][u] = (src[r] && b < nblk) ? src[r][(size_t)b * stride[r]] : 0.f;
         }
 #pragma unroll
+      for (int r = 0; r < IPR; ++r)
+#pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (b0 + 64 * u < nblk) v += (double)x8[u];
-      }
+          if (src[r] && b0 + 64 * u < nblk) v[r] += (double)x8[r][u];
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    if (lane == 0) item[i] = v;
+    for (int r = 0; r < IPR; ++r) {
+      const int i = i0 + r * nwaves;
+      if (i > E) continue;  // (uniform over the wave)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v[r] += __shfl_xor(v[r], o);
+      if (lane == 0) item[i] = v[r];
+    }
   }
   __syncthreads();
   if (threadIdx.x == 64 && z_loss && blk_zsum) *z_loss = (float)(item[E] / (double)T);

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(ScanArgs a)
     if (a.user_counts) a.user_counts[tid] = cnt_sh[tid];
   }
   if (a.f || a.p || a.loss || a.z_loss)
-    aux_stats_block(cnt_sh, a.blk_psum, a.blk_zsum, nblk, a.T, E, a.k, a.f, a.p, a.loss, a.z_loss);
+    aux_stats_block<1>(cnt_sh, a.blk_psum, a.blk_zsum, nblk, a.T, E, a.k, a.f, a.p, a.loss, a.z_loss);
 }
 
 // One wave per token: slots first (pos, src), then the row copy to every slot's row.
@@ -195,7 +195,148 @@ __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict_
   for (int c = lane; c < nch; c += 64) st16(dst + 16 * (size_t)c, ld16(xr + 16 * (size_t)c));
 }
 
+// ---------------------------------------------------------------------------------
+// Token choice in one kernel, for up to kFusedMaxBlocks router blocks: the prefix sums of
+// the dispatch scan and the permutation above, with no launch between them. Block b takes
+// router block b's tokens: it sums every expert's per-block counts itself (the totals, and
+// the part from blocks before b), derives the clamped group starts, and writes its slots'
+// rows (and, where rows are copied, the rows). Block nblk, when statistics are requested,
+// reduces f, p, loss and z_loss from the totals and the router's per-block partials in the
+// fixed order of aux_stats_block (the same bits as the standalone statistics). The counts
+// are re-read by every block (E * nblk ints each), which is why larger batches take the
+// two-kernel path.
+// ---------------------------------------------------------------------------------
+template <int EB>
+__global__ __launch_bounds__(256) void dispatch_tc_kernel(DispatchArgs a) {
+  __shared__ int pre_sh[64];   // this block's slots of expert e come after pre_sh[e] others
+  __shared__ int tot_sh[64];   // assignments per expert (before any capacity)
+  __shared__ int gs_sh[64];    // group start of expert e (clamped sizes)
+  __shared__ int pos_sh[kRouterTokens * 8];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = a.nblk, E = a.E, k = a.k, T = a.T;
+  // wave w sums experts w, w + 4, ...: four experts' rows at a time, every load of the four
+  // issued before any is added (up to 32 in flight per lane), then a wave reduction each
+  constexpr int EPC = 4, LPR = kFusedMaxBlocks / 64;  // experts per round, loads per row
+  for (int e0 = wave; e0 < E; e0 += 4 * EPC) {
+    int c[EPC][LPR];
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+      const int e = e0 + 4 * i;
+      const int32_t* row = a.blk_counts + (size_t)min(e, E - 1) * nblk;
+#pragma unroll
+      for (int j = 0; j < LPR; ++j) {
+        const int jb = lane + 64 * j;
+        c[i][j] = (e < E && jb < nblk) ? row[jb] : 0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPC; ++i) {
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int j = 0; j < LPR; ++j) {
+        tot += c[i][j];
+        pre += lane + 64 * j < b ? c[i][j] : 0;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        pre += __shfl_xor(pre, o);
+        tot += __shfl_xor(tot, o);
+      }
+      const int e = e0 + 4 * i;
+      if (lane == 0 && e < E) {
+        pre_sh[e] = pre;
+        tot_sh[e] = tot;
+      }
+    }
+  }
+  __syncthreads();
+  if (b == nblk) {  // the statistics block
+    aux_stats_block<4>(tot_sh, a.blk_psum, a.blk_zsum, nblk, T, E, k, a.f, a.p, a.loss, a.z_loss);
+    return;
+  }
+  if (wave == 0) {  // clamped sizes and their exclusive prefix (E <= 64)
+    const int c = lane < E ? tot_sh[lane] : 0;
+    const int cc = min(c, a.cap);
+    int incl = cc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane < E) gs_sh[lane] = incl - cc;
+    if (b == 0) {
+      if (lane < E) {
+        a.offsets[lane] = incl - cc;
+        a.counts[lane] = c;
+        if (a.user_counts) a.user_counts[lane] = c;
+      }
+      if (lane == E - 1) a.offsets[E] = incl;
+    }
+  }
+  if (b == 0 && a.sk_flags)
+    for (int i = tid; i < kStreamKSlots; i += blockDim.x) a.sk_flags[i] = 0;
+  __syncthreads();
+  // slots: row = group start + earlier blocks' slots of the expert + rank in this block
+  const int t0 = b * kRouterTokens, ntok = min(kRouterTokens, T - t0);
+  const int R = T * k;
+  for (int q = tid; q < ntok * k; q += blockDim.x) {
+    const size_t sidx = (size_t)t0 * k + q;
+    const int e = a.idx[sidx];
+    const int rank = pre_sh[e] + a.lrank[sidx];  // among the expert's slots, token order
+    int p = rank >= a.cap ? -1 : gs_sh[e] + rank;  // dropped by the capacity
+    if (p >= R) p = -1;  // unreachable for consistent tables; never write outside
+    a.pos[sidx] = p;
+    pos_sh[q] = p;
+    if (p >= 0) a.src[p] = t0 + q / k;
+  }
+  if (a.cap != INT_MAX || a.x_perm) __syncthreads();
+  if (a.cap != INT_MAX && tid < ntok) {
+    // a token that lost a slot: its kept weights divided by their sum, added in slot order
+    const size_t s0 = (size_t)(t0 + tid) * k;
+    bool lost = false;
+    float sk = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const bool kept = pos_sh[tid * k + j] >= 0;
+      lost |= !kept;
+      if (kept) sk += a.w[s0 + j];
+    }
+    if (lost) {
+      for (int j = 0; j < k; ++j) {
+        const float wj = a.w[s0 + j];
+        const float wk = a.renorm ? (sk > 0.f ? wj / sk : 0.f) : wj;
+        a.w[s0 + j] = pos_sh[tid * k + j] >= 0 ? wk : 0.f;
+      }
+    }
+  }
+  if (!a.x_perm) return;
+  // row copies: one wave per token, 16-byte pieces, to each kept slot's row
+  const size_t row_bytes = (size_t)a.d * EB;
+  const int nch = (int)(row_bytes / 16);
+  for (int tt = wave; tt < ntok; tt += 4) {
+    const char* xr = a.x + (size_t)(t0 + tt) * row_bytes;
+    for (int c = lane; c < nch; c += 64) {
+      const u32x4 v = ld16(xr + 16 * (size_t)c);
+      for (int j = 0; j < k; ++j) {
+        const int pj = pos_sh[tt * k + j];
+        if (pj >= 0) st16(a.x_perm + (size_t)pj * row_bytes + 16 * (size_t)c, v);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dispatch_tc(const DispatchArgs& a, hipStream_t s) {
+  if (a.E < 1 || a.E > 64 || a.k < 1 || a.k > 8 || a.nblk > kFusedMaxBlocks)
+    return hipErrorInvalidValue;
+  const bool stats = a.f || a.p || a.loss || a.z_loss;
+  dim3 grid(a.nblk + (stats ? 1 : 0)), block(256);
+  if (a.elt_bytes == 2)
+    dispatch_tc_kernel<2><<<grid, block, 0, s>>>(a);
+  else
+    dispatch_tc_kernel<4><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s) {
   if (a.E < 1 || a.E > 64) return hipErrorInvalidValue;

@@ -60,6 +60,32 @@ struct ScanArgs {
 };
 hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t s);
 
+// Token choice, the scan and the permutation in one launch (up to kFusedMaxBlocks router
+// blocks): offsets, counts, pos, src, capacity drops and renormalised weights, row copies
+// when x_perm is set, and (with any of f, p, loss, z_loss) the statistics, all as from
+// launch_dispatch_scan followed by launch_permute_tc.
+constexpr int kFusedMaxBlocks = 512;
+struct DispatchArgs {
+  const char* x;              // [T, d] rows (read only when x_perm is set)
+  int elt_bytes;
+  int T, d, E, k, nblk, cap, renorm;
+  const int32_t* idx;         // [T, k]
+  const int32_t* lrank;       // [T, k]
+  const int32_t* blk_counts;  // [E, nblk]
+  int32_t* pos;               // [T, k]
+  int32_t* src;               // [T * k]
+  float* w;                   // [T, k], rewritten under a capacity
+  char* x_perm;               // [T * k, d] or nullptr
+  int32_t* offsets;           // [E + 1]
+  int32_t* counts;            // [E]
+  int32_t* user_counts;       // [E] or nullptr
+  const float* blk_psum;      // [nblk, E]
+  const float* blk_zsum;      // [nblk] or nullptr
+  float *f, *p, *loss, *z_loss;
+  int32_t* sk_flags;          // stream-K flags to clear, or nullptr
+};
+hipError_t launch_dispatch_tc(const DispatchArgs& a, hipStream_t s);
+
 // Token choice: pos[t,j] = base + rank, src[pos] = t, x_perm[pos] = x[t]. With a
 // capacity (cap < INT_MAX) slots ranked cap or later in their expert get pos = -1 and
 // weight 0, and the token's kept weights w are renormalised when renorm is set.

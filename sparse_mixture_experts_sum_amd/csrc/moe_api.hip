@@ -232,14 +232,84 @@ moe_status zero_stats(int E, float* f, float* p, float* loss, int32_t* counts, f
   return MOE_OK;
 }
 
+// Token-choice dispatch after the router: group offsets, counts, the requested statistics
+// (f, p, loss, z_loss), the slots' rows (pos, src), capacity drops and renormalised weights,
+// row copies into x_perm (when not nullptr) and the stream-K flags cleared (when not
+// nullptr). Up to kFusedMaxBlocks router blocks in one kernel; beyond, the dispatch scan and
+// then (when `permute` is set) the permute kernel.
+moe_status run_dispatch_tc(const moe_shape& s, const Layout& L, const void* x, int32_t* idx,
+                           float* w, int32_t* user_counts, float* f, float* p, float* loss,
+                           float* z_loss, void* x_perm, int32_t* sk_flags, bool permute, void* ws,
+                           hipStream_t stream) {
+  const bool want_z = z_loss != nullptr;
+  const int eb = s.dtype == MOE_BF16 ? 2 : 4;
+  if (L.nblk <= kFusedMaxBlocks) {
+    DispatchArgs da{};
+    da.x = static_cast<const char*>(x);
+    da.elt_bytes = eb;
+    da.T = (int)s.T;
+    da.d = (int)s.d_model;
+    da.E = s.E;
+    da.k = s.k;
+    da.nblk = L.nblk;
+    da.cap = tc_cap_limit(s);
+    da.renorm = s.renormalize;
+    da.idx = idx;
+    da.lrank = at<int32_t>(ws, L.lrank);
+    da.blk_counts = at<int32_t>(ws, L.blk_counts);
+    da.pos = at<int32_t>(ws, L.pos);
+    da.src = at<int32_t>(ws, L.src);
+    da.w = w;
+    da.x_perm = static_cast<char*>(x_perm);
+    da.offsets = at<int32_t>(ws, L.offsets);
+    da.counts = at<int32_t>(ws, L.counts);
+    da.user_counts = user_counts;
+    da.blk_psum = at<float>(ws, L.blk_psum);
+    da.blk_zsum = want_z ? at<float>(ws, L.blk_zsum) : nullptr;
+    da.f = f;
+    da.p = p;
+    da.loss = loss;
+    da.z_loss = z_loss;
+    da.sk_flags = sk_flags;
+    MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_dispatch_tc(da, stream));
+    return MOE_OK;
+  }
+  ScanArgs sa{};
+  sa.blk_counts = at<int32_t>(ws, L.blk_counts);
+  sa.nblk = L.nblk;
+  sa.E = s.E;
+  sa.cap = tc_cap_limit(s);
+  sa.counts = at<int32_t>(ws, L.counts);
+  sa.offsets = at<int32_t>(ws, L.offsets);
+  sa.base = at<int32_t>(ws, L.base);
+  sa.user_counts = user_counts;
+  sa.blk_psum = at<float>(ws, L.blk_psum);
+  sa.blk_zsum = want_z ? at<float>(ws, L.blk_zsum) : nullptr;
+  sa.T = (int)s.T;
+  sa.k = s.k;
+  sa.f = f;
+  sa.p = p;
+  sa.loss = loss;
+  sa.z_loss = z_loss;
+  MOE_LAUNCH(MOE_STAGE_SCAN, launch_dispatch_scan(sa, stream));
+  if (!permute) return MOE_OK;
+  MOE_LAUNCH(MOE_STAGE_PERMUTE,
+             launch_permute_tc(x, eb, (int)s.T, (int)s.d_model, s.E, s.k, idx,
+                               at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.base),
+                               at<int32_t>(ws, L.offsets), tc_cap_limit(s), s.renormalize,
+                               at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w, x_perm, sk_flags,
+                               stream));
+  return MOE_OK;
+}
+
 // Router stage shared by moe_route and moe_forward. Token choice writes idx/w and the
-// dispatch tables (and, in token choice, the requested statistics f, p, loss, z_loss in the
-// dispatch scan); expert choice writes idx/score and the group offsets, and with z_loss
-// leaves the per-block z-loss partials in the workspace for launch_aux_final.
+// per-block dispatch tables (the dispatch itself follows: run_dispatch_tc); expert choice
+// writes idx/score and the group offsets, and with z_loss leaves the per-block z-loss
+// partials in the workspace for launch_aux_final.
 moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
                       const float* b_g, const moe_noise* noise, int32_t* idx, float* w,
-                      float* probs, int32_t* user_counts, float* f, float* p, float* loss,
-                      float* z_loss, void* ws, hipStream_t stream) {
+                      float* probs, int32_t* user_counts, float* z_loss, void* ws,
+                      hipStream_t stream) {
   const bool want_z = z_loss != nullptr;
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
@@ -262,24 +332,6 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     a.blk_counts = at<int32_t>(ws, L.blk_counts);
     a.blk_psum = at<float>(ws, L.blk_psum);
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 0, stream));
-    ScanArgs sa{};
-    sa.blk_counts = at<int32_t>(ws, L.blk_counts);
-    sa.nblk = L.nblk;
-    sa.E = s.E;
-    sa.cap = tc_cap_limit(s);
-    sa.counts = at<int32_t>(ws, L.counts);
-    sa.offsets = at<int32_t>(ws, L.offsets);
-    sa.base = at<int32_t>(ws, L.base);
-    sa.user_counts = user_counts;
-    sa.blk_psum = at<float>(ws, L.blk_psum);
-    sa.blk_zsum = want_z ? at<float>(ws, L.blk_zsum) : nullptr;
-    sa.T = (int)s.T;
-    sa.k = s.k;
-    sa.f = f;
-    sa.p = p;
-    sa.loss = loss;
-    sa.z_loss = z_loss;
-    MOE_LAUNCH(MOE_STAGE_SCAN, launch_dispatch_scan(sa, stream));
   } else {
     a.logitsT = at<float>(ws, L.logitsT);
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
@@ -361,22 +413,19 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
   const Layout L = make_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (s.T == 0) return zero_stats(s.E, nullptr, nullptr, nullptr, counts, z_loss, stream);
-  st = run_router(s, L, x, W_g, b_g, noise, idx, w, probs, counts, nullptr, nullptr, nullptr,
-                  z_loss, ws, stream);
+  st = run_router(s, L, x, W_g, b_g, noise, idx, w, probs, counts, z_loss, ws, stream);
   if (st != MOE_OK) return st;
-  if (z_loss && !is_tc(s.mode))
-    MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, (int)s.T, 0, s.k, nullptr,
-                                               nullptr, nullptr, nullptr,
-                                               at<float>(ws, L.blk_zsum), z_loss, stream));
-  if (s.mode != MOE_TOKEN_CHOICE_CAPACITY) return MOE_OK;
-  // capacity: the dispatch decides which slots stay; weights only, no row copies
-  MOE_LAUNCH(MOE_STAGE_PERMUTE,
-             launch_permute_tc(nullptr, s.dtype == MOE_BF16 ? 2 : 4, (int)s.T, (int)s.d_model, s.E,
-                               s.k, idx, at<int32_t>(ws, L.lrank), at<int32_t>(ws, L.base),
-                               at<int32_t>(ws, L.offsets), tc_cap_limit(s), s.renormalize,
-                               at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w, nullptr,
-                               nullptr, stream));
-  return MOE_OK;
+  if (!is_tc(s.mode)) {
+    if (z_loss)
+      MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, (int)s.T, 0, s.k,
+                                                 nullptr, nullptr, nullptr, nullptr,
+                                                 at<float>(ws, L.blk_zsum), z_loss, stream));
+    return MOE_OK;
+  }
+  // counts and z_loss; with a capacity the dispatch also decides which slots stay (weights
+  // only, no row copies)
+  return run_dispatch_tc(s, L, x, idx, w, counts, nullptr, nullptr, nullptr, z_loss, nullptr,
+                         nullptr, s.mode == MOE_TOKEN_CHOICE_CAPACITY, ws, stream);
 }
 
 }  // extern "C"
@@ -429,19 +478,16 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
   void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
-  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, f, p, loss, z_loss, ws,
-                  stream);
+  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss, ws, stream);
   if (st != MOE_OK) return st;
   void* x_perm = L.xperm ? at<void>(ws, L.x_perm) : nullptr;  // nullptr: no row copies
   const int32_t* src = at<int32_t>(ws, L.src);
   const StreamK sk{L.stream_k ? at<float>(ws, L.sk_partial) : nullptr,
                    L.stream_k ? at<int32_t>(ws, L.sk_flags) : nullptr};
   if (is_tc(s.mode)) {
-    MOE_LAUNCH(MOE_STAGE_PERMUTE,
-               launch_permute_tc(x, eb, T, d, E, s.k, idx_b, at<int32_t>(ws, L.lrank),
-                                 at<int32_t>(ws, L.base), offsets, tc_cap_limit(s), s.renormalize,
-                                 at<int32_t>(ws, L.pos), at<int32_t>(ws, L.src), w_b, x_perm,
-                                 sk.flags, stream));
+    st = run_dispatch_tc(s, L, x, idx_b, w_b, counts, f, p, loss, z_loss, x_perm, sk.flags, true,
+                         ws, stream);
+    if (st != MOE_OK) return st;
   } else {
     MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
                                                     at<int32_t>(ws, L.src), x_perm, sk.flags,

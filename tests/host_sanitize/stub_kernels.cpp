@@ -77,6 +77,26 @@ hipError_t launch_dispatch_scan(const ScanArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_dispatch_tc(const DispatchArgs& a, hipStream_t) {
+  ++g_launches;
+  const size_t R = (size_t)a.T * a.k;
+  inside(a.lrank, R * 4, "dispatch slot ranks");
+  inside(a.blk_counts, (size_t)a.nblk * a.E * 4, "dispatch block counts");
+  inside(a.pos, R * 4, "dispatch pos");
+  inside(a.src, R * 4, "dispatch src");
+  inside(a.x_perm, R * a.d * a.elt_bytes, "dispatch rows");
+  inside(a.offsets, (size_t)(a.E + 1) * 4, "dispatch offsets");
+  inside(a.counts, (size_t)a.E * 4, "dispatch counts");
+  inside(a.blk_psum, (size_t)a.nblk * a.E * 4, "dispatch block sums");
+  inside(a.blk_zsum, (size_t)a.nblk * 4, "dispatch z partials");
+  inside(a.sk_flags, kStreamKSlots * 4, "stream-K flags");
+  if (a.nblk > kFusedMaxBlocks) {
+    fprintf(stderr, "fused dispatch launched with %d blocks\n", a.nblk);
+    abort();
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_permute_tc(const void* x, int elt_bytes, int T, int d, int E, int k,
                              const int32_t* idx, const int32_t* lrank, const int32_t* base,
                              const int32_t* offsets, int cap, int renorm, int32_t* pos,

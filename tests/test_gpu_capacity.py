@@ -140,6 +140,16 @@ def test_capacity_factor_not_exact_in_binary(moe):
     run_capacity_case(moe, w, 0.9)
 
 
+def test_capacity_two_kernel_dispatch(moe):
+    # 625 router blocks: the capacity is applied by the dispatch scan and the permute kernel
+    # (the path past the fused dispatch's 512 blocks). 50025 of 80000 slots dropped, 15951
+    # tokens lose both; h rounded to bf16 alone puts this case at 0.0162 of the output RMS
+    # (the zeros of fully dropped tokens lower the RMS: with cf 0.8, d = d_ff = 64 that
+    # rounding alone exceeds the 2e-2 bar)
+    w = W.custom("cap_T40000", T=40000, d=128, f=256, E=16, k=2, bias_std=0.5, seed=(42, 611))
+    run_capacity_case(moe, w, 1.0)
+
+
 def test_capacity_fine_grained_top4(moe):
     w = W.custom("cap_e64_top4", T=1024, d=256, f=192, E=64, k=4, bias_std=0.3, seed=(42, 103))
     run_capacity_case(moe, w, 1.0)

@@ -213,10 +213,19 @@ def test_expert_choice_long_column(moe):
 
 
 def test_dispatch_scan_many_blocks(moe):
-    # 313 router blocks x 64 experts = 20032 count entries: more than 16 per scan thread,
-    # so the scan re-reads its entries instead of keeping them in registers
+    # 313 router blocks x 64 experts = 20032 count entries, summed by every block of the
+    # fused dispatch kernel
     run_tc_case(moe, W.custom("scan_T20000_E64", T=20000, d=64, f=64, E=64, k=2, wg_std=0.3,
                               seed=(42, 341)))
+
+
+def test_dispatch_two_kernel_path(moe):
+    # 625 router blocks (more than the fused dispatch takes): the dispatch scan, with more
+    # than 16 count entries per scan thread (it re-reads them), then the permute kernel
+    # (d_model 256, d_ff 512: h rounded to bf16 alone puts this case at 0.011 of the output
+    # RMS; at d = d_ff = 64 that rounding alone reaches the 2e-2 bar over 2.56 M outputs)
+    run_tc_case(moe, W.custom("scan_T40000_E16", T=40000, d=256, f=512, E=16, k=3, wg_std=0.3,
+                              bias_std=0.5, seed=(42, 342)))
 
 
 @pytest.mark.parametrize("T,d,f,E,k", [(300, 256, 8192, 2, 2), (1500, 512, 8192, 4, 2),
