@@ -156,6 +156,41 @@ def parity_vs_oracle(w, inp, ref, n, y_dev, idx_dev):
     return out
 
 
+def router_bound(torch, M, x, weights, y, ws, kw, steps, w, router_bytes):
+    """A plain streaming read of x in the router's place: each step runs one layer call, then
+    torch.sum(x) (every element read once, an fp32 result: the bytes of x and a few partials),
+    timed alone with HIP events; and the same read with x warm (right after another read).
+    Returns the median read rates against the router's own (its event pass in this run)."""
+    Wg, b, Wgate, Wup, Wdown = weights
+    xb = x.numel() * x.element_size()
+    ev = []
+    for _ in range(steps):
+        M.moe_forward(x, Wg, b, Wgate, Wup, Wdown, y=y, workspace=ws, **kw)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = torch.sum(x, dtype=torch.float32)
+        z.record()
+        ev.append((a, z))
+    torch.cuda.synchronize()
+    after_layer = float(np.median([a.elapsed_time(z) for a, z in ev]))
+    ev = []
+    for _ in range(steps):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r = torch.sum(x, dtype=torch.float32)
+        z.record()
+        ev.append((a, z))
+    torch.cuda.synchronize()
+    warm = float(np.median([a.elapsed_time(z) for a, z in ev]))
+    del r
+    return {"what": "torch.sum(x, dtype=float32) timed alone: after a layer call (the router's "
+                    "place) and back to back (x warm)",
+            "x_bytes": xb, "after_layer_us": round(after_layer * 1e3, 2),
+            "after_layer_gbs": round(xb / (after_layer * 1e-3) / 1e9, 1),
+            "warm_us": round(warm * 1e3, 2), "warm_gbs": round(xb / (warm * 1e-3) / 1e9, 1),
+            "router_bytes": router_bytes}
+
+
 def reference_gemm(torch, w, group_rows, steps, warmup, gu_ms, dn_ms):
     """torch's bf16 matmul (hipBLASLt) on the grouped GEMMs' problems, one matmul per expert:
     gate and up as one [d, 2 d_ff] weight (the same FLOP as the fused gate/up GEMM, without its
@@ -222,6 +257,10 @@ def main():
                     help="after the layer, also time torch's bf16 matmul (hipBLASLt) on the same "
                          "per-expert problems as the grouped GEMMs: x_e [n_e, d] @ [d, 2 d_ff] "
                          "and h_e [n_e, d_ff] @ [d_ff, d], n_e the layer's group sizes")
+    ap.add_argument("--router-bound", action="store_true",
+                    help="after the layer, time a plain streaming read of x (torch.sum over its "
+                         "bf16 values, fp32 result) placed where the router runs: right after a "
+                         "layer call, repeated; the read rate x allows in that cache state")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
@@ -372,6 +411,9 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
+    if args.router_bound:
+        line["router_bound"] = router_bound(torch, M, x, (Wg, b, Wgate, Wup, Wdown), y, ws, kw,
+                                            args.steps, w, work["router"][1])
     if args.reference_gemm and w.dtype == "bf16":
         line["reference_gemm"] = reference_gemm(torch, w, counts if w.mode != "ec" else
                                                 np.full(w.E, w.capacity), args.steps, args.warmup,
