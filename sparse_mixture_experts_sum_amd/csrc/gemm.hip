@@ -446,65 +446,92 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
   return m;
 }
 
-// Tile i of this XCD's share (see TileMap); CONTIG = m.contiguous, fixed at compile time
-// so that the split order's stream carries no code of the other.
+// Where a workgroup stands in its XCD's tile list: the group holding the tiles
+// [acc, acc + pe) of the list (this XCD's share of it, or the whole list in the contiguous
+// order) and that group's M-tile count. A workgroup locates its tiles in increasing list
+// order, so the cursor only moves forward: one step per group passed, instead of a walk
+// over all groups from the first for every tile (E steps of dependent scalar loads, with
+// an integer division per step in the contiguous order).
+struct TileCursor {
+  int e;        // group
+  int j;        // contiguous order: list position of group e (jr = j % G, jq = j / G)
+  int jr, jq;
+  int acc;      // list index of group e's first tile
+  int pe;       // group e's tiles in the list
+  int mte;      // group e's M-tiles
+  int plo;      // split order: first of the group's tiles that this XCD takes
+  int G;        // contiguous order: groups per weight matrix
+};
+
+template <int BM, bool CONTIG>
+__device__ __forceinline__ void cursor_load(TileCursor& c, const int32_t* offsets, const TileMap& m) {
+  c.e = CONTIG ? c.jr * m.EW + c.jq : c.e;
+  c.mte = (offsets[c.e + 1] - offsets[c.e] + BM - 1) / BM;
+  if constexpr (CONTIG) {
+    c.pe = c.mte * m.NT;
+  } else if (m.gn > 0) {
+    c.pe = c.mte * m.nx;
+  } else {
+    const long long pe = (long long)c.mte * m.NT;
+    c.plo = (int)((pe * m.xcd) >> 3);
+    c.pe = (int)((pe * (m.xcd + 1)) >> 3) - c.plo;
+  }
+}
+
+template <int BM, bool CONTIG>
+__device__ __forceinline__ TileCursor make_cursor(const int32_t* offsets, const TileMap& m) {
+  TileCursor c;
+  c.e = 0;
+  c.j = c.jr = c.jq = 0;
+  c.acc = 0;
+  c.plo = 0;
+  c.G = m.E / m.EW;
+  cursor_load<BM, CONTIG>(c, offsets, m);
+  return c;
+}
+
+// Tile i of this XCD's share (see TileMap); i at or after the cursor's group, which the
+// call advances. CONTIG = m.contiguous, fixed at compile time so that the split order's
+// stream carries no code of the other.
 template <int BM, bool CONTIG>
 __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, const TileMap& m,
-                                                 int bn_out) {
-  int e = 0, p = 0, mte = 1;
-  if constexpr (!CONTIG) {
-    if (m.gn > 0) {
-      // columns order: this XCD's rectangle of group e is mte row tiles x nx column tiles,
-      // walked block by block (gn columns; only the last block may be narrower)
-      int acc_i = 0;
-      for (;; ++e) {
-        mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-        const int pe = mte * m.nx;
-        if (i < acc_i + pe) break;
-        acc_i += pe;
+                                                 int bn_out, TileCursor& c) {
+  const int gi = CONTIG ? m.base + i : i;
+  // (the bound on the group keeps a cursor that would run past the last group in range)
+  while (gi >= c.acc + c.pe && c.j < m.E - 1) {
+    c.acc += c.pe;
+    ++c.j;
+    if constexpr (CONTIG) {
+      if (++c.jr == c.G) {
+        c.jr = 0;
+        ++c.jq;
       }
-      const int q = i - acc_i;
-      const int g = min(q / (mte * m.gn), (m.nx - 1) / m.gn);
-      const int r = q - g * mte * m.gn;
-      const int wg = min(m.gn, m.nx - g * m.gn);
-      const int mtl = r / wg;
-      TileCoord t;
-      t.e = e;
-      t.row0 = offsets[e] + mtl * BM;
-      t.rows = min(BM, offsets[e + 1] - t.row0);
-      t.n0 = (m.xcd * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
-      return t;
+    } else {
+      c.e = c.j;
     }
-    int acc_i = 0;
-    for (;; ++e) {
-      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      const long long pe = (long long)mte * m.NT;
-      const int plo = (int)((pe * m.xcd) >> 3), phi = (int)((pe * (m.xcd + 1)) >> 3);
-      if (i < acc_i + (phi - plo)) {
-        p = plo + (i - acc_i);
-        break;
-      }
-      acc_i += phi - plo;
-    }
-  } else {
-    // list position j holds group (j mod G) * EW + j / G: the G groups of weight matrix w
-    // (w, w + EW, ...) sit next to each other
-    const int G = m.E / m.EW, gi = m.base + i;
-    int acc_i = 0;
-    for (int j = 0;; ++j) {
-      e = (j % G) * m.EW + j / G;
-      mte = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      const int pe = mte * m.NT;
-      if (gi < acc_i + pe) {
-        p = gi - acc_i;
-        break;
-      }
-      acc_i += pe;
-    }
+    cursor_load<BM, CONTIG>(c, offsets, m);
   }
-  const int nt = p / mte, mtl = p - nt * mte;
+  const int e = c.e, mte = c.mte;
   TileCoord t;
   t.e = e;
+  if (!CONTIG && m.gn > 0) {
+    // columns order: this XCD's rectangle of group e is mte row tiles x nx column tiles,
+    // walked block by block (gn columns; only the last block may be narrower)
+    const int q = gi - c.acc;
+    const int g = min(q / (mte * m.gn), (m.nx - 1) / m.gn);
+    const int r = q - g * mte * m.gn;
+    const int wg = min(m.gn, m.nx - g * m.gn);
+    const int mtl = r / wg;
+    t.row0 = offsets[e] + mtl * BM;
+    t.rows = min(BM, offsets[e + 1] - t.row0);
+    t.n0 = (m.xcd * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
+    return t;
+  }
+  // split: position p of the group's N-tile-major list; contiguous: the same, from the
+  // group's start in the whole list (group at list position j is (j mod G) * EW + j / G:
+  // the G groups of weight matrix w sit next to each other)
+  const int p = CONTIG ? gi - c.acc : c.plo + (gi - c.acc);
+  const int nt = p / mte, mtl = p - nt * mte;
   t.row0 = offsets[e] + mtl * BM;
   t.rows = min(BM, offsets[e + 1] - t.row0);
   t.n0 = nt * bn_out;
@@ -922,7 +949,8 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
   int ln = fresh_lane();
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-  TileCoord t = locate_tile<BM, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT);
+  TileCursor cur_c = make_cursor<BM, CONTIG>(a.offsets, tm);
+  TileCoord t = locate_tile<BM, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT, cur_c);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
   StageLoader<G, SWIGLU, SPLIT> ld =
@@ -949,7 +977,8 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
     // bounds)
     Item nx = cur;
     const bool has_next = next_item(it, sp, slot, nslot, nk, nx);
-    const TileCoord tn = has_next ? locate_tile<BM, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT) : t;
+    const TileCoord tn =
+        has_next ? locate_tile<BM, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT, cur_c) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
@@ -1040,13 +1069,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
       return;
     }
   }
+  TileCursor cur_c = make_cursor<BM, false>(offsets, tm);
+  TileCursor cur_cc = make_cursor<BM, CONTIG_OK>(offsets, tm);
   for (int i = slot; i < my_total; i += nslot) {
     const int ln = fresh_lane();
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
     const TileCoord t = CONTIG_OK && tm.contiguous
-                            ? locate_tile<BM, CONTIG_OK>(i, offsets, tm, G::BN_OUT)
-                            : locate_tile<BM, false>(i, offsets, tm, G::BN_OUT);
+                            ? locate_tile<BM, CONTIG_OK>(i, offsets, tm, G::BN_OUT, cur_cc)
+                            : locate_tile<BM, false>(i, offsets, tm, G::BN_OUT, cur_c);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
     const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, 0, gv);
