@@ -194,3 +194,28 @@ def router_z_loss(x, Wg, b):
         lz = math.log(z)
         acc += lz * lz
     return acc / T
+
+
+def noise_draw_one(t, e, seed, offset=0):
+    """One element of the in-kernel training-noise draw, evaluated with Python
+    integers and the math module: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+    SC 2011) of counter (t, e // 4, low and high 32 bits of offset) under key (low and
+    high 32 bits of seed), the 24-bit uniforms u = (r >> 8 + 1/2) / 2^24 of its four
+    words, and the Box-Muller transform (Box and Muller, 1958) of the pair that
+    expert e falls in: cosine for even e, sine for odd e."""
+    m32 = (1 << 32) - 1
+    c = [t & m32, e // 4, offset & m32, (offset >> 32) & m32]
+    k0, k1 = seed & m32, (seed >> 32) & m32
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + 0x9E3779B9) & m32
+            k1 = (k1 + 0xBB67AE85) & m32
+        a = 0xD2511F53 * c[0]
+        b = 0xCD9E8D57 * c[2]
+        c = [((b >> 32) ^ c[1] ^ k0) & m32, b & m32, ((a >> 32) ^ c[3] ^ k1) & m32, a & m32]
+    j = e % 4
+    pair = j // 2
+    u0 = ((c[2 * pair] >> 8) + 0.5) / float(1 << 24)
+    u1 = ((c[2 * pair + 1] >> 8) + 0.5) / float(1 << 24)
+    r = math.sqrt(-2.0 * math.log(u0))
+    return r * (math.cos(2.0 * math.pi * u1) if j % 2 == 0 else math.sin(2.0 * math.pi * u1))

@@ -40,6 +40,10 @@ Readings where the pages leave a step open or disagree:
     to the logits, bias included, before the softmax; the normal draw eps is an
     input. P5's fixed-scale noise is the same with Wn = None and eps scaled by
     the caller. Token choice only (P3's ``ExpertChoiceGating`` has no noise).
+    The pages draw eps with torch's generator; a draw that both sides can make
+    without passing it is the counter-based one of ``noise_draw`` (Philox4x32-10
+    and the Box-Muller transform, from their published definitions, not from
+    the pages).
   * router z-loss (P3 ``router_z_loss``) is taken on the logits the softmax sees,
     bias included, for every routing mode (it depends on the logits only); with
     no tokens it is 0. P5 prints another quantity under the same name (a mean
@@ -129,6 +133,61 @@ def noisy_logits(x, Wg, b, Wn, eps):
     if Wn is None:
         return s + _f64(eps)
     return s + softplus(_f64(x) @ _f64(Wn)) * _f64(eps)
+
+
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+# as 1, 2, 3", SC 2011): a counter of four 32-bit words and a key of two go through
+# ten rounds; a round multiplies counter words 0 and 2 by two fixed odd constants
+# into 64-bit products and rebuilds the counter from their halves, the two other
+# words and the key; between rounds the key takes a Weyl step (the golden-ratio
+# and sqrt(3) - 1 constants).
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 of arrays of counters: counter uint [..., 4], key (k0, k1).
+    Returns uint64 [..., 4] holding the four 32-bit output words."""
+    c = [np.asarray(counter, dtype=np.uint64)[..., i] & 0xFFFFFFFF for i in range(4)]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    lo32 = np.uint64(0xFFFFFFFF)
+    for rnd in range(10):
+        if rnd > 0:
+            k0 = (k0 + PHILOX_W[0]) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W[1]) & 0xFFFFFFFF
+        prod0 = np.uint64(PHILOX_M[0]) * c[0]   # < 2^64: no wrap
+        prod1 = np.uint64(PHILOX_M[1]) * c[2]
+        hi0, lo0 = prod0 >> np.uint64(32), prod0 & lo32
+        hi1, lo1 = prod1 >> np.uint64(32), prod1 & lo32
+        c = [hi1 ^ c[1] ^ np.uint64(k0), lo1, hi0 ^ c[3] ^ np.uint64(k1), lo0]
+    return np.stack(c, axis=-1)
+
+
+def noise_draw(T, E, seed, offset=0, scale=1.0):
+    """The counter-based normal draw eps [T, E] (float64) that the library makes in
+    its router when no eps is passed: for token t and expert e = 4q + 2h + c,
+    Philox4x32-10 of counter (t, q, offset mod 2^32, offset div 2^32) under key
+    (seed mod 2^32, seed div 2^32) gives words r0..r3; u_i = (floor(r_i / 2^8) +
+    1/2) / 2^24; and the Box-Muller transform (Box and Muller, 1958) of the pair
+    (u_2h, u_2h+1) gives sqrt(-2 ln u_2h) times cos (c = 0) or sin (c = 1) of
+    2 pi u_2h+1. eps = scale * that."""
+    Q = (E + 3) // 4
+    t = np.arange(T, dtype=np.uint64)[:, None]
+    q = np.arange(Q, dtype=np.uint64)[None, :]
+    ctr = np.zeros((T, Q, 4), dtype=np.uint64)
+    ctr[..., 0] = t
+    ctr[..., 1] = q
+    ctr[..., 2] = int(offset) & 0xFFFFFFFF
+    ctr[..., 3] = (int(offset) >> 32) & 0xFFFFFFFF
+    r = philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF))
+    u = ((r >> np.uint64(8)).astype(F64) + 0.5) / float(1 << 24)   # [T, Q, 4], in (0, 1)
+    n = np.empty((T, Q, 4), dtype=F64)
+    for h in range(2):
+        rad = np.sqrt(-2.0 * np.log(u[..., 2 * h]))
+        ang = 2.0 * np.pi * u[..., 2 * h + 1]
+        n[..., 2 * h] = rad * np.cos(ang)
+        n[..., 2 * h + 1] = rad * np.sin(ang)
+    return float(scale) * n.reshape(T, 4 * Q)[:, :E]
 
 
 def route_tc_noisy(x, Wg, b, Wn, eps, k, renormalize=True):

@@ -584,4 +584,57 @@ def pin_noisy_special_cases(O):
     assert np.all(O.route_tc_noisy(c["x"], c["Wg"], c["b"], c["Wn"], spike, 1)[0][:, 0] == 4)
 
 
+def pin_philox_known_answers(O):
+    """Philox4x32-10 reproduces the generator's published known-answer vectors
+    (tests/golden/philox4x32_10_kat.json), one counter at a time and as a batch."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as fh:
+        vec = json.load(fh)["vectors"]
+    ctr = np.array([[int(h, 16) for h in v["counter"]] for v in vec], dtype=np.uint64)
+    for i, v in enumerate(vec):
+        key = tuple(int(h, 16) for h in v["key"])
+        out = O.philox4x32_10(ctr[i], key)
+        assert [int(u) for u in out] == [int(h, 16) for h in v["out"]], v
+
+
+def pin_noise_draw_is_standard_normal(O):
+    """One million draws of the in-kernel noise definition pass as independent
+    standard normals: mean, variance, a Kolmogorov-Smirnov test against N(0, 1), the
+    tail mass beyond 3, and no correlation between a token's neighbouring experts
+    (the cosine and sine of one Box-Muller pair, and the pairs of one Philox call)."""
+    from scipy import stats
+    eps = O.noise_draw(65536, 16, seed=0x5EED5EED1234, offset=3)
+    n = eps.size
+    flat = eps.ravel()
+    assert abs(flat.mean()) < 5.0 / math.sqrt(n)
+    assert abs(flat.var() - 1.0) < 5.0 * math.sqrt(2.0 / n)
+    assert stats.kstest(flat, "norm").pvalue > 1e-4
+    tail = float(np.mean(np.abs(flat) > 3.0))
+    assert abs(tail - 2.0 * stats.norm.sf(3.0)) < 6.0 * math.sqrt(2.0 * stats.norm.sf(3.0) / n)
+    for a, b in ((0, 1), (2, 3), (0, 2), (1, 3), (3, 4)):
+        rho = np.corrcoef(eps[:, a], eps[:, b])[0, 1]
+        assert abs(rho) < 5.0 / math.sqrt(eps.shape[0]), (a, b, rho)
+
+
+def pin_noise_draw_counter_based(O):
+    """The draw of (t, e) depends on (seed, offset, t, e) only: a smaller batch or
+    fewer experts read the same numbers, a new offset or seed draws new ones, scale
+    multiplies, and the vectorised draw equals the scalar evaluation of the
+    definition in pure Python (oracle/brute.py) element by element."""
+    big = O.noise_draw(300, 12, seed=77, offset=5)
+    assert np.array_equal(O.noise_draw(7, 12, seed=77, offset=5), big[:7])
+    assert np.array_equal(O.noise_draw(300, 5, seed=77, offset=5), big[:, :5])
+    other = O.noise_draw(300, 12, seed=77, offset=6)
+    assert np.mean(other == big) < 0.01
+    assert np.mean(O.noise_draw(300, 12, seed=78, offset=5) == big) < 0.01
+    assert np.allclose(O.noise_draw(300, 12, seed=77, offset=5, scale=-2.5), -2.5 * big,
+                       rtol=1e-15, atol=0.0)
+    for t, e in ((0, 0), (1, 3), (17, 6), (299, 11), (123, 9)):
+        ref = B.noise_draw_one(t, e, seed=77, offset=5)
+        assert math.isclose(float(big[t, e]), ref, rel_tol=1e-12, abs_tol=1e-12), (t, e)
+    hi = O.noise_draw(4, 8, seed=(3 << 32) | 9, offset=(5 << 32) | 1)
+    for t, e in ((0, 0), (3, 7), (2, 5)):
+        ref = B.noise_draw_one(t, e, seed=(3 << 32) | 9, offset=(5 << 32) | 1)
+        assert math.isclose(float(hi[t, e]), ref, rel_tol=1e-12, abs_tol=1e-12), (t, e)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

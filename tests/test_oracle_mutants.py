@@ -68,6 +68,18 @@ MUTANTS = {
                                  "g = softmax_rows(router_logits(x, Wg, None))"),
     "dense_mixture_skips_last_expert": ("for e in range(g.shape[1]):",
                                         "for e in range(g.shape[1] - 1):"),
+    "philox_no_key_step": ("            k0 = (k0 + PHILOX_W[0]) & 0xFFFFFFFF\n            k1 = (k1 + PHILOX_W[1]) & 0xFFFFFFFF",
+                           "            pass"),
+    "philox_multipliers_swapped": ("prod0 = np.uint64(PHILOX_M[0]) * c[0]",
+                                   "prod0 = np.uint64(PHILOX_M[1]) * c[0]"),
+    "philox_nine_rounds": ("for rnd in range(10):\n        if rnd > 0:", "for rnd in range(9):\n        if rnd > 0:"),
+    "box_muller_no_minus_two": ("rad = np.sqrt(-2.0 * np.log(u[..., 2 * h]))",
+                                "rad = np.sqrt(-np.log(u[..., 2 * h]))"),
+    "box_muller_angle_from_radius_uniform": ("ang = 2.0 * np.pi * u[..., 2 * h + 1]",
+                                             "ang = 2.0 * np.pi * u[..., 2 * h]"),
+    "box_muller_half_turn": ("ang = 2.0 * np.pi * u[..., 2 * h + 1]", "ang = np.pi * u[..., 2 * h + 1]"),
+    "noise_draw_ignores_offset": ("ctr[..., 2] = int(offset) & 0xFFFFFFFF", "ctr[..., 2] = 0"),
+    "noise_draw_counter_runs_over_experts": ("ctr[..., 1] = q", "ctr[..., 1] = t * Q + q"),
     "tc_capacity_renorm_over_all_slots":("rows = g.sum(axis=1, keepdims=True)",
                                           "rows = np.take_along_axis(p, idx, axis=1).sum(axis=1, keepdims=True)"),
 }
