@@ -11,7 +11,7 @@ per-kernel durations come from a second pass of the same steps in which the libr
 records HIP events around each launch on the stream it launches on.
 
 Options select the other workloads (--workload NAME) and the token-choice variants at a
-workload's shape (--variant capacity | noisy | zloss).
+workload's shape (--variant capacity | noisy | noisy_eps | zloss).
 """
 from __future__ import annotations
 
@@ -35,10 +35,11 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-def stage_work(w, R=None, noisy=False):
+def stage_work(w, R=None, noisy=None):
     """Algorithmic work per stage for one layer call: FLOP for the GEMMs, bytes for the
     streaming stages (minimum each stage must move). R: rows the GEMMs run (the kept
-    rows under an expert capacity); noisy: the router also reads W_noise and the draw."""
+    rows under an expert capacity); noisy: "eps", the router also reads W_noise and the
+    draw; "drawn", it reads W_noise and draws in the kernel."""
     s = 2 if w.dtype == "bf16" else 4
     T, d, f, E = w.T, w.d, w.f, w.E
     R = w.rows if R is None else R
@@ -57,7 +58,7 @@ def stage_work(w, R=None, noisy=False):
     k = w.k
     router = T * d * s + d * E * s + T * k * 8 + T * E * 4
     if noisy:
-        router += d * E * s + T * E * 4
+        router += d * E * s + (T * E * 4 if noisy == "eps" else 0)
     work["router"] = ("bytes", router)
     if w.dtype != "bf16" or T * d >= 2 ** 31:
         # rows copied into expert order (bf16 layers otherwise gather them inside the
@@ -249,9 +250,12 @@ def main():
                     choices=sorted(W.WORKLOADS), help="workload (default: the Mixtral-size layer)")
     ap.add_argument("--cpu-sample", type=int, default=16384,
                     help="tokens the CPU oracle baseline runs (0 = skip)")
-    ap.add_argument("--variant", default="plain", choices=("plain", "capacity", "noisy", "zloss"),
+    ap.add_argument("--variant", default="plain",
+                    choices=("plain", "capacity", "noisy", "noisy_eps", "zloss"),
                     help="token-choice variant: an expert capacity (--cf), training noise "
-                         "softplus(x W_noise) * eps, or the router z-loss as an extra output")
+                         "softplus(x W_noise) * eps with eps drawn in the router kernel (noisy) "
+                         "or passed as a [T, E] input (noisy_eps), or the router z-loss as an "
+                         "extra output")
     ap.add_argument("--cf", type=float, default=1.0, help="capacity factor of --variant capacity")
     ap.add_argument("--reference-gemm", action="store_true",
                     help="after the layer, also time torch's bf16 matmul (hipBLASLt) on the same "
@@ -294,6 +298,9 @@ def main():
     if args.variant == "capacity":
         kw.update(mode="tc_capacity", capacity_factor=args.cf)
     elif args.variant == "noisy":
+        nz = W.make_noise(w, wn_std=0.02)
+        kw.update(W_noise=to_dev(nz["Wn"]), eps=M.NoiseDraw(seed=2024, offset=0))
+    elif args.variant == "noisy_eps":
         nz = W.make_noise(w, wn_std=0.02)
         kw.update(W_noise=to_dev(nz["Wn"]), eps=to_dev(nz["eps"], torch.float32))
     elif args.variant == "zloss":
@@ -343,7 +350,7 @@ def main():
     ms_step = float(np.median(step_ms))
     tokens_s = w.T / (ms_step * 1e-3)
 
-    work = stage_work(w, R_run, noisy=args.variant == "noisy")
+    work = stage_work(w, R_run, noisy={"noisy": "drawn", "noisy_eps": "eps"}.get(args.variant))
     peak_tf = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     st_out = {}
     for name, (tot, n) in stages.items():

@@ -105,14 +105,31 @@ typedef struct moe_shape {
 
 /* Training noise of noisy top-k gating, token choice only (both token-choice modes).
  *   W_noise [d_model, E] dtype, layout of W_g; or NULL for additive noise
- *   eps     [T, E] fp32, the normal draw (one per token and expert), required
+ *   eps     [T, E] fp32, the normal draw (one per token and expert); or NULL to have the
+ *           router kernel draw it: eps[t, e] = scale * n(t, e) below
+ *   seed, offset, scale   the in-kernel draw (ignored when eps is given); a non-finite
+ *           scale returns MOE_ERR_BAD_SHAPE
  * The router's logits become s + softplus(x W_noise) * eps (softplus(z) = log(1 + e^z)),
- * or s + eps without W_noise, with s = x W_g (+ b_g). Everything downstream — softmax,
- * top-k, weights, probs, counts, f, p, loss, z_loss — sees the noisy logits. The draw is
- * an input so that a caller controls its generator (e.g. torch.randn on the stream). */
+ * or s + eps without W_noise, with s = x W_g (+ b_g): the Korean page's TopKGating
+ * (training branch) and 机器学习基础系列——混合专家模型's MoELayer. Everything downstream —
+ * softmax, top-k, weights, probs, counts, f, p, loss, z_loss — sees the noisy logits.
+ * The in-kernel draw is counter-based, so that n(t, e) depends on (seed, offset, t, e)
+ * only, not on the launch:
+ *   (r0, r1, r2, r3) = Philox4x32-10 with counter (t, floor(e / 4), offset mod 2^32,
+ *                      floor(offset / 2^32)) and key (seed mod 2^32, floor(seed / 2^32))
+ *                      (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy
+ *                      as 1, 2, 3", SC 2011)
+ *   u_i = (floor(r_i / 2^8) + 1/2) / 2^24, strictly inside (0, 1)
+ *   n(t, 4q + 2h + c) = sqrt(-2 ln u_{2h}) * (c = 0 ? cos : sin)(2 pi u_{2h+1})
+ *                      (the Box-Muller transform, Box and Muller 1958)
+ * evaluated in fp32 (the uniforms exactly; log, sqrt, cos and sin to about an ulp). A new
+ * draw per training step takes a new offset (or seed). */
 typedef struct moe_noise {
   const void* W_noise;
   const float* eps;
+  uint64_t seed;
+  uint64_t offset;
+  float scale;
 } moe_noise;
 
 /* Human-readable name of a status code. Never NULL; the string is static. */
@@ -164,7 +181,7 @@ moe_status moe_workspace_offset(const moe_shape* shape, int32_t which, size_t* o
  *   W_g    [d_model, E]   dtype (the x @ W layout of MoELayer.__init__)
  *   b_g    [E] fp32 router bias added to the logits, or NULL for none
  *   noise  training noise (moe_noise), or NULL for none; MOE_ERR_UNSUPPORTED in expert
- *          choice, MOE_ERR_NULL_ARG without eps
+ *          choice
  * Token choice outputs:
  *   idx    [T, k] int32   selected experts, descending probability
  *   w      [T, k] fp32    gate weights of the selected experts

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "moe_route", "moe_forward", "moe_forward_noalloc", "moe_aux_loss", "make_shape", "workspace_size", "capacity",
+    "moe_route", "moe_forward", "moe_forward_noalloc", "moe_aux_loss", "NoiseDraw", "make_shape",
+    "workspace_size", "capacity",
     "workspace_offset", "profile_enable", "profile_read", "stage_names", "SparseMoE",
     "MoEError", "load_library", "LIB_PATH",
 ]
@@ -59,7 +60,23 @@ class MoeShape(ctypes.Structure):
 
 
 class MoeNoise(ctypes.Structure):
-    _fields_ = [("W_noise", ctypes.c_void_p), ("eps", ctypes.c_void_p)]
+    _fields_ = [("W_noise", ctypes.c_void_p), ("eps", ctypes.c_void_p), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64), ("scale", ctypes.c_float)]
+
+
+class NoiseDraw:
+    """Pass as ``eps`` to have the router kernel draw the training noise itself:
+    eps[t, e] = scale * n(t, e) with n the counter-based normal draw of (seed, offset)
+    that include/moe.h defines (Philox4x32-10 and the Box-Muller transform). A new draw
+    per training step takes a new offset."""
+
+    def __init__(self, seed: int, offset: int = 0, scale: float = 1.0):
+        if not (0 <= int(seed) < 1 << 64 and 0 <= int(offset) < 1 << 64):
+            raise ValueError("seed and offset must fit in 64 unsigned bits")
+        self.seed, self.offset, self.scale = int(seed), int(offset), float(scale)
+
+    def __repr__(self):
+        return f"NoiseDraw(seed={self.seed}, offset={self.offset}, scale={self.scale})"
 
 
 _lib = None
@@ -186,22 +203,26 @@ def _x_shape(x):
 def _noise_shapes(T, d, E, W_noise, eps):
     if eps is None:
         if W_noise is not None:
-            raise ValueError("W_noise needs eps, the normal draw")
+            raise ValueError("W_noise needs eps, the normal draw (a tensor or a NoiseDraw)")
         return
-    _shape_is(eps, "eps", (T, E))
+    if not isinstance(eps, NoiseDraw):
+        _shape_is(eps, "eps", (T, E))
     _shape_is(W_noise, "W_noise", (d, E))
 
 
 def _noise(x, W_noise, eps, dev):
-    """moe_noise for training noise: eps [T,E] fp32 (required for any noise) and
-    optionally W_noise [d,E] of x's dtype; None when eps is None. Shapes are checked by
-    _noise_shapes first."""
+    """moe_noise for training noise: eps [T,E] fp32 or a NoiseDraw (required for any
+    noise) and optionally W_noise [d,E] of x's dtype; None when eps is None. Shapes are
+    checked by _noise_shapes first."""
     if eps is None:
         return None
-    _need(eps, "eps", torch.float32, dev)
     _need(W_noise, "W_noise", x.dtype, dev)
-    return ctypes.byref(MoeNoise(W_noise=None if W_noise is None else W_noise.data_ptr(),
-                                 eps=eps.data_ptr()))
+    wn = None if W_noise is None else W_noise.data_ptr()
+    if isinstance(eps, NoiseDraw):
+        return ctypes.byref(MoeNoise(W_noise=wn, eps=None, seed=eps.seed, offset=eps.offset,
+                                     scale=eps.scale))
+    _need(eps, "eps", torch.float32, dev)
+    return ctypes.byref(MoeNoise(W_noise=wn, eps=eps.data_ptr()))
 
 
 def _workspace(shape: MoeShape, dev, workspace: Optional[torch.Tensor]) -> torch.Tensor:
@@ -218,7 +239,8 @@ def moe_route(x, W_g, b_g=None, *, k=2, mode="tc", capacity_factor=1.0, renormal
               workspace=None) -> dict:
     """Router only. Token choice (with or without capacity) returns idx/w [T,k];
     expert choice idx/w [E,C]. want_z_loss adds the router z-loss (fp32 [1]); eps
-    (and W_noise) add the training noise of noisy top-k gating."""
+    (and W_noise) add the training noise of noisy top-k gating: eps an fp32 [T,E] draw,
+    or a NoiseDraw for the router kernel to draw it."""
     T, d = _x_shape(x)
     if not isinstance(W_g, torch.Tensor) or W_g.dim() != 2:
         raise ValueError("W_g must be [d_model, E]")
@@ -255,7 +277,8 @@ def moe_forward(x, W_g, b_g, W_gate, W_up, W_down, *, k=2, mode="tc", capacity_f
                 want_z_loss=False, W_noise=None, eps=None, workspace=None, y=None) -> dict:
     """Whole layer forward. Returns y (fp32 [T,d]) and, on request, idx, w, probs,
     counts, (token choice) f, p, loss, and the router z-loss. eps (and W_noise) add
-    the training noise of noisy top-k gating."""
+    the training noise of noisy top-k gating: eps an fp32 [T,E] draw, or a NoiseDraw
+    for the router kernel to draw it."""
     return _forward(x, W_g, b_g, W_gate, W_up, W_down, k, mode, capacity_factor, renormalize,
                     want_routing, want_probs, want_stats, want_z_loss, W_noise, eps, workspace, y,
                     noalloc=False)

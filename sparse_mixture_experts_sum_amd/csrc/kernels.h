@@ -10,9 +10,14 @@ struct RouterArgs {
   const void* Wg;       // [d, E] dtype
   const float* bias;    // [E] or nullptr
   // token choice, optional training noise: logits + softplus(x Wn) * eps, or + eps
-  // when Wn is nullptr; none when eps is nullptr
+  // when Wn is nullptr; eps from the eps array, or drawn in the kernel (draw = 1: the
+  // counter-based normal draw of (seed, offset) times noise_scale); none when eps is
+  // nullptr and draw is 0
   const void* Wn;       // [d, E] dtype or nullptr
   const float* eps;     // [T, E] or nullptr
+  int draw;
+  uint32_t seed_lo, seed_hi, off_lo, off_hi;
+  float noise_scale;
   int T, d, E, k, renorm;
   // token choice outputs
   int32_t* idx;         // [T, k]

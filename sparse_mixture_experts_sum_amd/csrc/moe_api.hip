@@ -153,11 +153,12 @@ Layout make_layout(const moe_shape& s) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Training noise: token choice only; the draw is required, W_noise optional.
+// Training noise: token choice only; the draw given (eps) or drawn in the router kernel
+// (eps null: seed, offset, a finite scale), W_noise optional.
 moe_status check_noise(const moe_shape& s, const moe_noise* noise) {
   if (!noise) return MOE_OK;
   if (!is_tc(s.mode)) return MOE_ERR_UNSUPPORTED;
-  if (s.T > 0 && !noise->eps) return MOE_ERR_NULL_ARG;
+  if (!noise->eps && !isfinite(noise->scale)) return MOE_ERR_BAD_SHAPE;
   if (!aligned16(noise->W_noise) || !aligned16(noise->eps)) return MOE_ERR_MISALIGNED;
   return MOE_OK;
 }
@@ -318,6 +319,14 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
   a.bias = b_g;
   a.Wn = noise ? noise->W_noise : nullptr;
   a.eps = noise ? noise->eps : nullptr;
+  if (noise && !noise->eps) {  // drawn in the router kernel
+    a.draw = 1;
+    a.seed_lo = (uint32_t)noise->seed;
+    a.seed_hi = (uint32_t)(noise->seed >> 32);
+    a.off_lo = (uint32_t)noise->offset;
+    a.off_hi = (uint32_t)(noise->offset >> 32);
+    a.noise_scale = noise->scale;
+  }
   a.T = (int)s.T;
   a.d = (int)s.d_model;
   a.E = s.E;

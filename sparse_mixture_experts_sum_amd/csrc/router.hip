@@ -18,8 +18,10 @@
 // Noisy top-k gating (the Korean page's TopKGating, training branch): the noise
 // projection x W_noise runs as E more MFMA columns over the same x fragments (W_noise
 // staged beside W_g), and each logit becomes s + softplus(x W_noise) * eps before the
-// softmax; eps, the normal draw, is an input. Without W_noise the draw is added as is
-// (the fixed-scale noise of 机器学习基础系列——混合专家模型, MoELayer).
+// softmax. eps, the normal draw, is an input, or is drawn here, per (token, expert), from a
+// counter-based generator (Philox4x32-10 and the Box-Muller transform), so that no draw
+// travels through HBM. Without W_noise the draw is added as is (the fixed-scale noise of
+// 机器学习基础系列——混合专家模型, MoELayer).
 #include <float.h>
 #include <limits.h>
 
@@ -169,7 +171,41 @@ __device__ __forceinline__ float softplus_f(float z) {
   return fmaxf(z, 0.f) + log1pf(expf(-fabsf(z)));
 }
 
-// NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added.
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+// 3", SC 2011): ten rounds of two 32 x 32 -> 64-bit products on the counter, with a Weyl
+// sequence on the key between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0], p1 = (uint64_t)0xCD9E8D57u * c[2];
+    c = u32x4{(uint32_t)(p1 >> 32) ^ c[1] ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c[3] ^ k1,
+              (uint32_t)p0};
+  }
+  return c;
+}
+
+// The in-kernel normal draw n(t, e): Philox4x32-10 of counter (t, e / 4, offset) under key
+// seed gives four words r_0..r_3; u_i = (r_i / 256 (integer part) + 1/2) / 2^24, exact in
+// fp32 and strictly inside (0, 1); the Box-Muller transform (Box and Muller, 1958) of the
+// pair (u_0, u_1) gives experts 4q and 4q + 1 (cosine, sine), of (u_2, u_3) experts 4q + 2
+// and 4q + 3.
+__device__ __forceinline__ float noise_draw(const RouterArgs& a, int t, int e) {
+  const u32x4 r = philox4x32_10(u32x4{(uint32_t)t, (uint32_t)(e >> 2), a.off_lo, a.off_hi},
+                                a.seed_lo, a.seed_hi);
+  const int h = (e >> 1) & 1;
+  const uint32_t r0 = h ? r[2] : r[0], r1 = h ? r[3] : r[1];
+  const float u0 = ((float)(r0 >> 8) + 0.5f) * 0x1p-24f;
+  const float u1 = ((float)(r1 >> 8) + 0.5f) * 0x1p-24f;
+  const float rad = sqrtf(-2.0f * logf(u0));
+  return rad * ((e & 1) ? sinpif(2.0f * u1) : cospif(2.0f * u1));
+}
+
+// NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added; eps from
+// a.eps, or drawn (noise_draw, times a.noise_scale) when a.eps is null.
 // DIRECT (bf16, E a multiple of 8): W_g (and W_noise) staged by stage_wg_direct and read
 // with wg_fragment; otherwise transposed through registers by stage_wg_transposed.
 template <typename TI, int EP, int NOISE, bool DIRECT>
@@ -223,7 +259,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + wave * 16 + 4 * g + r;
-        epsv[nb][r] = (t < T && e < E) ? a.eps[(size_t)t * E + e] : 0.f;
+        epsv[nb][r] = (t < T && e < E)
+                          ? (a.eps ? a.eps[(size_t)t * E + e] : a.noise_scale * noise_draw(a, t, e))
+                          : 0.f;
       }
     }
   }
@@ -609,7 +647,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
 hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s) {
   const int nblk = (a.T + kRT - 1) / kRT;
   const int ep = a.E <= 16 ? 16 : (a.E <= 32 ? 32 : 64);
-  const int noise = a.eps ? (a.Wn ? 2 : 1) : 0;
+  const int noise = (a.eps || a.draw) ? (a.Wn ? 2 : 1) : 0;
   if (noise && ec) return hipErrorInvalidValue;  // noise is a token-choice feature
   dim3 grid(nblk), block(256);
   const bool direct = bf16in && a.E % 8 == 0;

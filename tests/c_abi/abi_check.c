@@ -3,6 +3,7 @@
  * strings, argument errors, profiling with nothing recorded). Needs no GPU: each call
  * below returns before any HIP call. Prints one line per check; exit status 0 when all
  * pass. */
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -85,9 +86,9 @@ int main(void) {
   check(moe_forward(&s, p, p, NULL, NULL, p, p, p, p, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                     NULL, p, need - 1, NULL) == MOE_ERR_WORKSPACE_TOO_SMALL,
         "forward with a small workspace");
-  moe_noise nz = {NULL, NULL};
-  check(moe_route(&s, p, p, NULL, &nz, p, p, NULL, NULL, NULL, p, need, NULL) == MOE_ERR_NULL_ARG,
-        "noise without its draw");
+  moe_noise nz = {NULL, NULL, 1, 0, NAN};
+  check(moe_route(&s, p, p, NULL, &nz, p, p, NULL, NULL, NULL, p, need, NULL) == MOE_ERR_BAD_SHAPE,
+        "noise drawn in the kernel with a non-finite scale");
   moe_shape ecs = shape(64, 128, 256, 8, 1, MOE_EXPERT_CHOICE, 1.0);
   nz.eps = (const float*)p;
   check(moe_route(&ecs, p, p, NULL, &nz, p, p, NULL, NULL, NULL, p, need, NULL) ==

@@ -86,9 +86,12 @@ static void run_all(const moe_shape& s) {
   r = moe_route(&s, kP, kP, nullptr, nullptr, ip, fp, fp, ip, fp, kWs, ws, nullptr);
   check(r == MOE_OK, "route on a valid shape", r);
   if (tc) {
-    moe_noise nz = {kP, fp};
+    moe_noise nz = {kP, fp, 0, 0, 0.f};
     r = moe_route(&s, kP, kP, nullptr, &nz, ip, fp, nullptr, nullptr, nullptr, kWs, ws, nullptr);
     check(r == MOE_OK, "noisy route", r);
+    moe_noise nzd = {kP, nullptr, ~0ull, 1ull << 40, 0.5f};
+    r = moe_route(&s, kP, kP, nullptr, &nzd, ip, fp, nullptr, nullptr, nullptr, kWs, ws, nullptr);
+    check(r == MOE_OK, "noisy route, draw in the kernel", r);
     r = moe_aux_loss(&s, fp, ip, fp, fp, fp, ip, kWs, ws, nullptr);
     check(r == MOE_OK, "aux loss on a valid shape", r);
   }

@@ -197,14 +197,20 @@ def test_forward_argument_errors_before_any_hip_call(M):
                            None, None, None, f, None, None, None, good, n, None) == 3
     assert lib.moe_route(ctypes.byref(s), good, good, None, None, None, good, None, None, None, good,
                          n, None) == 1
-    # training noise: expert choice refuses it, a missing draw is a null argument, and a
-    # misaligned projection is caught
+    # training noise: expert choice refuses it (given or drawn), an in-kernel draw with a
+    # non-finite scale is refused, and a misaligned projection is caught
     ecn = M.make_shape(64, 128, 256, 8, mode="ec", capacity_factor=1.0)
     nz = M.MoeNoise(W_noise=None, eps=8192)
     assert lib.moe_route(ctypes.byref(ecn), good, good, None, ctypes.byref(nz), good, good, None,
                          None, None, good, n * 4, None) == 3
-    assert call(noise=ctypes.byref(M.MoeNoise(W_noise=8192, eps=None))) == 1
+    nzd = M.MoeNoise(W_noise=None, eps=None, seed=1, offset=2, scale=1.0)
+    assert lib.moe_route(ctypes.byref(ecn), good, good, None, ctypes.byref(nzd), good, good, None,
+                         None, None, good, n * 4, None) == 3
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        nzb = M.MoeNoise(W_noise=8192, eps=None, seed=1, offset=2, scale=bad)
+        assert call(noise=ctypes.byref(nzb)) == 2
     assert call(noise=ctypes.byref(M.MoeNoise(W_noise=8196, eps=8192))) == 5
+    assert call(noise=ctypes.byref(M.MoeNoise(W_noise=8196, eps=None, scale=1.0))) == 5
     assert lib.moe_aux_loss(ctypes.byref(ec), good, good, good, good, good, None, good, n, None) == 3
     assert lib.moe_aux_loss(ctypes.byref(s), good, good, None, good, good, None, good, n, None) == 1
 

@@ -89,3 +89,16 @@ def test_right_shapes_on_the_cpu_are_refused_as_host_tensors():
         M.moe_route(t["x"], t["W_g"], t["b_g"], k=k)
     with pytest.raises(TypeError):
         M.moe_aux_loss(torch.zeros(T, E), torch.zeros(T, k, dtype=torch.int32))
+
+
+def test_noise_draw_arguments():
+    # the in-kernel draw: seed and offset are 64-bit unsigned; W_noise still checked
+    with pytest.raises(ValueError):
+        M.NoiseDraw(-1)
+    with pytest.raises(ValueError):
+        M.NoiseDraw(1, offset=1 << 64)
+    t = _layer()
+    with pytest.raises(ValueError):
+        _forward(t, eps=M.NoiseDraw(3), W_noise=torch.zeros(d, E - 1, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):  # right shapes, host tensors
+        _forward(t, eps=M.NoiseDraw(3, 4, 0.5), W_noise=torch.zeros(d, E, dtype=torch.bfloat16))

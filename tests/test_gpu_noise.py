@@ -1,7 +1,9 @@
 """GPU parity of noisy top-k gating (the Korean page's TopKGating, training branch:
 logits + softplus(x W_noise) * eps; additive eps for the fixed-scale form) against
-the fp64 oracle, through the C ABI. The normal draw eps is an input that both sides
-read; routing follows the near-tie rules of the plain token-choice tests.
+the fp64 oracle, through the C ABI. The normal draw eps is either an input that both
+sides read, or drawn by the router kernel from (seed, offset) while the oracle
+evaluates the same counter-based definition (Philox4x32-10 and Box-Muller) in fp64;
+routing follows the near-tie rules of the plain token-choice tests.
 """
 from __future__ import annotations
 
@@ -40,11 +42,19 @@ def _dev_noise(nz, w):
             PR.to_dev(nz["eps"], torch.float32))
 
 
-def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0):
-    _say(w, "noise", "softplus" if nz["Wn"] is not None else "additive", mode)
+def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0, draw=None):
+    """nz: the noise inputs (W_noise, eps). draw = (seed, offset, scale): the router
+    kernel draws eps instead, and the oracle takes its fp64 evaluation of the same
+    definition (nz["eps"] is replaced)."""
+    _say(w, "noise", "softplus" if nz["Wn"] is not None else "additive", mode,
+         "drawn in the kernel %r" % (draw,) if draw else "eps passed")
     inp = W.make_inputs(w)
     dev = PR.device_inputs(inp, w)
     Wn, eps = _dev_noise(nz, w)
+    if draw is not None:
+        seed, offset, scale = draw
+        eps = M.NoiseDraw(seed, offset, scale)
+        nz = dict(nz, eps=O.noise_draw(w.T, w.E, seed, offset, scale))
     out = M.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
                         k=w.k, mode=mode, capacity_factor=cf, renormalize=w.renormalize,
                         want_z_loss=True, W_noise=Wn, eps=eps)
@@ -181,3 +191,77 @@ def test_expert_choice_refuses_noise(moe):
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_route(dev["x"], dev["Wg"], None, mode="ec", eps=eps)
     assert ei.value.status == 3
+
+
+# ---------------------------------------------------------------------------------
+# the training noise drawn in the router kernel (moe_noise with eps = NULL)
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E", [6, 64])
+def test_drawn_noise_seen_through_probs(moe, E):
+    # W_g = 0, no bias, additive noise of scale 1: the logits are the draw itself, so the
+    # probabilities show every element of the kernel's draw against the oracle's fp64
+    # evaluation of the same (seed, offset; t, e) definition. T ragged, seed and offset
+    # with high words set, E = 6 ends inside a group of four experts.
+    T, d = 4097, 64
+    seed, offset = (0xA5A5 << 32) | 0x1234, (7 << 32) | 99
+    _say("drawn noise through probs", T, E, hex(seed), hex(offset))
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    Wg = torch.zeros(d, E, device="cuda", dtype=torch.bfloat16)
+    r = moe.moe_route(x, Wg, None, k=2, eps=moe.NoiseDraw(seed, offset, 1.0))
+    torch.cuda.synchronize()
+    eps_ref = O.noise_draw(T, E, seed, offset)
+    p_ref = O.softmax_rows(eps_ref)
+    np.testing.assert_allclose(_np(r["probs"]), p_ref, rtol=0, atol=2e-6)
+    exempt = PR.check_tc_routing(_np(r["idx"]), _np(r["w"]), p_ref, 2, True)
+    assert exempt.sum() < T // 100
+    # the logits' spread is that of N(0, 1) draws: the largest probability of a token
+    # reaches well above uniform for most tokens
+    assert np.median(p_ref.max(axis=1)) > 2.0 / E
+
+
+def test_drawn_noise_mid_bf16(moe):
+    w = W.MID_BF16
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05), draw=(2024, 1, 1.0))
+
+
+def test_drawn_noise_fine_grained_e64_top4(moe):
+    w = W.custom("drawn_e64_top4", T=2048, d=512, f=256, E=64, k=4, seed=(42, 311))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05), draw=(99, 12345, 1.0))
+
+
+def test_drawn_additive_noise_fp32_ragged(moe):
+    # the fixed-scale form drawn in the kernel: logits + 0.1 * n(t, e)
+    w = W.custom("drawn_additive_fp32", dtype="fp32", T=1000, d=128, f=64, E=8, k=2, x_std=0.5,
+                 wg_std=0.1, renormalize=False, seed=(42, 312))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=None), draw=(7, 0, 0.1))
+
+
+def test_drawn_noise_with_capacity(moe):
+    w = W.custom("drawn_capacity", T=1024, d=256, f=128, E=8, k=2, bias_std=0.5, seed=(42, 313))
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.05), mode="tc_capacity", cf=0.75,
+                   draw=(5, 3, 1.0))
+
+
+def test_drawn_noise_mixtral_layer_full(moe):
+    # every output of the full Mixtral-shaped layer with the draw made in the router
+    w = W.MIXTRAL_LAYER
+    run_noisy_case(moe, w, W.make_noise(w, wn_std=0.02), draw=(0xC0FFEE, 42, 1.0))
+
+
+def test_drawn_noise_is_deterministic_and_moves_with_offset(moe):
+    w = W.custom("drawn_offsets", T=1500, d=256, f=128, E=16, k=2, seed=(42, 314))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    Wn, _ = _dev_noise(W.make_noise(w, wn_std=0.05), w)
+    _say(w, "drawn noise: same (seed, offset) twice, then the next offset")
+    run = lambda off: moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"],
+                                      dev["Wdown"], k=2, want_z_loss=True, W_noise=Wn,
+                                      eps=moe.NoiseDraw(31, off, 1.0))
+    a, b, c = run(8), run(8), run(9)
+    torch.cuda.synchronize()
+    for n in ("y", "idx", "w", "probs", "counts", "f", "p", "loss", "z_loss"):
+        assert torch.equal(a[n], b[n]), n
+    moved = int(torch.any(torch.sort(a["idx"], 1)[0] != torch.sort(c["idx"], 1)[0], 1).sum())
+    assert moved > 0
