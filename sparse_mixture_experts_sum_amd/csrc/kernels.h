@@ -39,10 +39,12 @@ hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
 
 // Expert choice: per expert, softmax over tokens, top-C tokens (ascending token
 // order) and scores. Also writes offsets[g] = g*C for g <= ngroups (E, or 2E when the
-// down projection runs the residual rows as groups of their own) and counts (optional).
+// down projection runs the residual rows as groups of their own), counts (optional),
+// src (optional: the token of each row e*C + c, the same list as idx, for the gate/up
+// GEMM's gather), and clears the stream-K flags (optional).
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int ngroups, int32_t* counts,
-                            hipStream_t s);
+                            int32_t* src, int32_t* sk_flags, hipStream_t s);
 
 // Dispatch prefix sum over per-block counts blk_counts [E, nblk] (expert-major):
 // counts[E] (unclamped), offsets[E+1] (group starts; with an expert capacity cap the

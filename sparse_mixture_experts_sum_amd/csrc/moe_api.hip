@@ -307,10 +307,13 @@ moe_status run_dispatch_tc(const moe_shape& s, const Layout& L, const void* x, i
 // per-block dispatch tables (the dispatch itself follows: run_dispatch_tc); expert choice
 // writes idx/score and the group offsets, and with z_loss leaves the per-block z-loss
 // partials in the workspace for launch_aux_final.
+// select_src / sk_flags (expert choice, or nullptr): the select also writes each row's token
+// and clears the GEMMs' stream-K flags, when no permute follows it.
 moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const void* W_g,
                       const float* b_g, const moe_noise* noise, int32_t* idx, float* w,
                       float* probs, int32_t* user_counts, float* z_loss, void* ws,
-                      hipStream_t stream) {
+                      hipStream_t stream, int32_t* select_src = nullptr,
+                      int32_t* sk_flags = nullptr) {
   const bool want_z = z_loss != nullptr;
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
@@ -346,7 +349,8 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
     MOE_LAUNCH(MOE_STAGE_EC_SELECT,
                launch_ec_select(at<float>(ws, L.logitsT), (int)s.T, s.E, (int)L.C, idx, w, probs,
-                                at<int32_t>(ws, L.offsets), L.ngroups, user_counts, stream));
+                                at<int32_t>(ws, L.offsets), L.ngroups, user_counts,
+                                select_src, sk_flags, stream));
   }
   return MOE_OK;
 }
@@ -487,20 +491,23 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   const int32_t* offsets = at<int32_t>(ws, L.offsets);
   void* h_lo = L.h_lo ? at<void>(ws, L.h_lo) : nullptr;
 
-  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss, ws, stream);
-  if (st != MOE_OK) return st;
   void* x_perm = L.xperm ? at<void>(ws, L.x_perm) : nullptr;  // nullptr: no row copies
-  const int32_t* src = at<int32_t>(ws, L.src);
+  int32_t* src = at<int32_t>(ws, L.src);
   const StreamK sk{L.stream_k ? at<float>(ws, L.sk_partial) : nullptr,
                    L.stream_k ? at<int32_t>(ws, L.sk_flags) : nullptr};
+  // expert choice without row copies: the select writes each row's token and clears the
+  // stream-K flags itself, and no permute runs
+  const bool ec_direct = !is_tc(s.mode) && !x_perm;
+  st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss, ws, stream,
+                  ec_direct ? src : nullptr, ec_direct ? sk.flags : nullptr);
+  if (st != MOE_OK) return st;
   if (is_tc(s.mode)) {
     st = run_dispatch_tc(s, L, x, idx_b, w_b, counts, f, p, loss, z_loss, x_perm, sk.flags, true,
                          ws, stream);
     if (st != MOE_OK) return st;
-  } else {
-    MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b,
-                                                    at<int32_t>(ws, L.src), x_perm, sk.flags,
-                                                    stream));
+  } else if (!ec_direct) {
+    MOE_LAUNCH(MOE_STAGE_PERMUTE, launch_permute_ec(x, eb, d, E, (int)L.C, idx_b, src, x_perm,
+                                                    sk.flags, stream));
   }
   MOE_LAUNCH(MOE_STAGE_GEMM_GATE_UP,
              launch_gemm_gateup(bf, x_perm ? x_perm : x, x_perm ? nullptr : src, W_gate, W_up,

@@ -511,21 +511,29 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 constexpr int kEcThreads = 1024;
 constexpr int kEcWaves = kEcThreads / 64;
 constexpr int kEcLdsTokens = 32768;
+constexpr int kEcCand = kEcThreads;  // keys of the selected value bucket ranked directly
 
 template <bool INLDS>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __restrict__ logitsT,
                                                                int T, int E, int C, int32_t* idx,
                                                                float* score, float* probs,
                                                                int32_t* offsets, int ngroups,
-                                                               int32_t* counts) {
+                                                               int32_t* counts, int32_t* src,
+                                                               int32_t* sk_flags) {
   __shared__ float colsh[INLDS ? kEcLdsTokens : 1];
   __shared__ int whist[kEcWaves][256];
   __shared__ float redf[kEcWaves];
   __shared__ int scan_sh[17];
-  __shared__ int sel_digit, sel_need;
+  __shared__ float redlo[kEcWaves];
+  __shared__ int sel_digit, sel_need, sel_cnt;
+  __shared__ uint32_t cand_key[kEcCand];
+  __shared__ int cand_above[kEcCand];
+  __shared__ int cand_n, cand_sel;
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const float* col = logitsT + (size_t)e * T;
+  if (sk_flags && e == 0)
+    for (int i = tid; i < kStreamKSlots; i += kEcThreads) sk_flags[i] = 0;
   if constexpr (INLDS) {
     for (int t = tid; t < T; t += kEcThreads) colsh[t] = col[t];
     __syncthreads();
@@ -539,13 +547,25 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   const int per = (T + kEcThreads - 1) / kEcThreads;
   const int tb = min(T, tid * per), te = min(T, tb + per);
 
-  float m = -FLT_MAX;
-  for (int t = tb; t < te; ++t) m = fmaxf(m, logit(t));
+  float m = -FLT_MAX, lo = FLT_MAX;
+  for (int t = tb; t < te; ++t) {
+    const float l = logit(t);
+    m = fmaxf(m, l);
+    lo = fminf(lo, l);
+  }
   m = warp_max(m);
-  if (lane == 0) redf[wid] = m;
+  lo = -warp_max(-lo);
+  if (lane == 0) {
+    redf[wid] = m;
+    redlo[wid] = lo;
+  }
   __syncthreads();
   m = redf[0];
-  for (int i = 1; i < kEcWaves; ++i) m = fmaxf(m, redf[i]);
+  lo = redlo[0];
+  for (int i = 1; i < kEcWaves; ++i) {
+    m = fmaxf(m, redf[i]);
+    lo = fminf(lo, redlo[i]);
+  }
   __syncthreads();
   float s = 0.f;
   for (int t = tb; t < te; ++t) s += expf(logit(t) - m);
@@ -556,19 +576,12 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   float sum = 0.f;
   for (int i = 0; i < kEcWaves; ++i) sum += redf[i];
 
-  // radix select of the C-th largest key
-  uint32_t prefix = 0, mask = 0;
-  int need = C;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
-    __builtin_amdgcn_wave_barrier();
-    for (int t = tb; t < te; ++t) {
-      const uint32_t key = float_key(logit(t));
-      if ((key & mask) == prefix) atomicAdd(&whist[wid][(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
+  // The C-th largest key (float_key order), `thr`, and how many keys equal to it are taken,
+  // `need`. Histograms count keys per bucket in per-wave LDS arrays; wave 0 then walks the
+  // 256 buckets from the top (lane l owns buckets 255 - 4l .. 252 - 4l) to the one holding
+  // the need-th largest remaining key.
+  auto find_bucket = [&](int need_in) {
     if (wid == 0) {
-      // lane l owns digits 255 - 4l .. 252 - 4l (descending), summed over the waves
       int c[4], cl = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -578,24 +591,90 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
         c[j] = v;
         cl += v;
       }
-      int incl = cl;  // keys in digits above and at this lane's (inclusive scan)
+      int incl = cl;  // keys in buckets above and at this lane's (inclusive scan)
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int u = __shfl_up(incl, o);
         if (lane >= o) incl += u;
       }
       const int excl = incl - cl;
-      if (excl < need && need <= incl) {  // exactly one lane: the C-th key is here
+      if (excl < need_in && need_in <= incl) {  // exactly one lane: the key is here
         int cum = excl, j = 0;
         for (; j < 3; ++j) {
-          if (cum + c[j] >= need) break;
+          if (cum + c[j] >= need_in) break;
           cum += c[j];
         }
         sel_digit = 255 - 4 * lane - j;
-        sel_need = need - cum;
+        sel_need = need_in - cum;
+        sel_cnt = c[j];
       }
     }
     __syncthreads();
+  };
+  uint32_t prefix = 0;
+  int need = C;
+  bool found = false;
+  // Value buckets: bucket(l) = floor((l - min) * 256 / (max - min)), clamped, is monotone in
+  // l, so the key sits in the bucket where the count from the top reaches C. Its keys (at
+  // most kEcCand) are then ranked among themselves, one per thread. Columns whose span is
+  // not a finite positive number, or whose bucket holds more keys (many equal logits), take
+  // the radix passes below.
+  const float span = m - lo;
+  const float scale = 256.0f / span;
+  if (isfinite(span) && span > 0.f && isfinite(scale)) {
+    auto bucket = [&](float l) { return (int)fminf(fmaxf((l - lo) * scale, 0.f), 255.f); };
+    for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int t = tb; t < te; ++t) atomicAdd(&whist[wid][bucket(logit(t))], 1);
+    __syncthreads();
+    find_bucket(need);
+    const int sb = sel_digit, sneed = sel_need, scnt = sel_cnt;
+    if (scnt <= kEcCand) {
+      if (tid == 0) {
+        cand_n = 0;
+        cand_sel = INT_MAX;
+      }
+      __syncthreads();
+      for (int t = tb; t < te; ++t) {
+        const float l = logit(t);
+        if (bucket(l) == sb) {
+          const int slot = atomicAdd(&cand_n, 1);
+          if (slot < kEcCand) cand_key[slot] = float_key(l);  // (the count is scnt)
+        }
+      }
+      __syncthreads();
+      const int n = min(cand_n, kEcCand);
+      if (tid < n) {
+        const uint32_t kt = cand_key[tid];
+        int above = 0, ateq = 0;
+        for (int j = 0; j < n; ++j) {
+          const uint32_t kj = cand_key[j];
+          above += kj > kt;
+          ateq += kj >= kt;
+        }
+        cand_above[tid] = above;
+        if (above < sneed && sneed <= ateq) atomicMin(&cand_sel, tid);  // equal keys all hit
+      }
+      __syncthreads();
+      const int cs = cand_sel;  // always set when the bucket's keys are all here
+      if (cs < n) {
+        prefix = cand_key[cs];
+        need = sneed - cand_above[cs];
+        found = true;
+      }
+    }
+  }
+  // radix select: 8-bit digits of the key from the top
+  uint32_t mask = 0;
+  for (int shift = 24; shift >= 0 && !found; shift -= 8) {
+    for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int t = tb; t < te; ++t) {
+      const uint32_t key = float_key(logit(t));
+      if ((key & mask) == prefix) atomicAdd(&whist[wid][(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    find_bucket(need);
     prefix |= (uint32_t)sel_digit << shift;
     mask |= 255u << shift;
     need = sel_need;
@@ -628,6 +707,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
       const float sc = expf(l - m) / sum;
       if (take && out < C) {
         idx[(size_t)e * C + out] = t;
+        if (src) src[(size_t)e * C + out] = t;
         score[(size_t)e * C + out] = sc;
         ++out;
       }
@@ -679,13 +759,13 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int ngroups, int32_t* counts,
-                            hipStream_t s) {
+                            int32_t* src, int32_t* sk_flags, hipStream_t s) {
   if (ngroups != E && ngroups != 2 * E) return hipErrorInvalidValue;
   if (T <= kEcLdsTokens)
     ec_select_kernel<true><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                    ngroups, counts);
+                                                    ngroups, counts, src, sk_flags);
   else
     ec_select_kernel<false><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                     ngroups, counts);
+                                                     ngroups, counts, src, sk_flags);
   return hipGetLastError();
 }

@@ -56,10 +56,12 @@ hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t) {
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int ngroups, int32_t* counts,
-                            hipStream_t) {
+                            int32_t* src, int32_t* sk_flags, hipStream_t) {
   ++g_launches;
   inside(logitsT, (size_t)E * T * 4, "select logits");
   inside(idx, (size_t)E * C * 4, "select idx");
+  inside(src, (size_t)E * C * 4, "select src");
+  inside(sk_flags, (size_t)kStreamKSlots * 4, "select stream-K flags");
   inside(score, (size_t)E * C * 4, "select scores");
   inside(offsets, (size_t)(ngroups + 1) * 4, "select offsets");
   (void)probs;
