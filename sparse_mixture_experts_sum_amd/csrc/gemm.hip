@@ -392,17 +392,21 @@ struct TileCoord {
 //  - Split (groups with many tiles, N-tiles not a multiple of 8; tiles listed
 //    N-tile-major): XCD x takes the x-th eighth of each group's list, i.e. mostly its own
 //    slice of the group's weight columns, for all of the group's rows.
-//  - Contiguous (every group small: split would give each XCD under 2 tiles of a group,
-//    or under 6 when the rows are gathered from x): the groups' lists are concatenated,
+//  - Contiguous (every group small: the split order would give each XCD under 4 tiles of a
+//    group, the columns order under 2, or under 6 when the rows are gathered from x): the
+//    groups' lists are concatenated,
 //    groups that share a weight matrix next to each other, and XCD x takes the x-th
 //    eighth of the whole list. The tiles an XCD runs together then come from one or a few
 //    groups and share their weight columns and rows in the XCD's L2; split, they would
 //    come from a different group each. (Measured: contiguous gains where split leaves
-//    an XCD one tile per group, and on gathered rows up to about 6 per group; with plain
-//    rows at 2-3 tiles per group, and beyond 6 with gathered rows, split was faster.)
+//    an XCD up to 2-3 tiles per group (mid-size down projection, A/B in one process:
+//    107.6 -> 102.5 us), and on gathered rows up to about 6 per group; against the columns
+//    order at 2-3 tiles per group (64-expert down projection) it was level, and beyond 6
+//    with gathered rows split was faster.)
 // Both keep the XCDs' tile counts within one of each other.
 constexpr int kXcds = 8;
 constexpr int kContigTiles = 16;        // max tiles per group for contiguous, plain rows
+constexpr int kContigSplitTiles = 32;   // the same where the columns order does not apply
 constexpr int kContigGatherTiles = 48;  // the same, rows gathered from x
 struct TileMap {
   int NT, xcd, E, EW;
@@ -438,7 +442,8 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
   }
   // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
   m.contiguous =
-      CONTIG_OK && maxpe < (gathered ? kContigGatherTiles : kContigTiles) && E % EW == 0;
+      CONTIG_OK && E % EW == 0 &&
+      maxpe < (gathered ? kContigGatherTiles : (gn > 0 ? kContigTiles : kContigSplitTiles));
   if (m.contiguous) m.gn = 0;
   m.base = m.contiguous ? (int)((total * xcd) >> 3) : 0;
   m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base
@@ -1187,7 +1192,8 @@ hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, con
                        const StreamK& sk, hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
-  // only below the threshold
+  // only below the threshold (kernels for wider outputs are built without it; split-order
+  // shapes between kContigTiles and kContigSplitTiles column tiles forgo it)
   const int NT = N / (SWIGLU ? BNL / 2 : BNL);
   const int gn = column_block(NT);
   if (NT < (gather ? kContigGatherTiles : kContigTiles))
