@@ -206,22 +206,27 @@ __global__ __launch_bounds__(256) void permute_ec_kernel(const char* __restrict_
 // are re-read by every block (E * nblk ints each), which is why larger batches take the
 // two-kernel path.
 // ---------------------------------------------------------------------------------
-template <int EB>
-__global__ __launch_bounds__(256) void dispatch_tc_kernel(DispatchArgs a) {
+// NT threads per block: 256 (four waves take 16 experts' counts per round) up to 16 experts,
+// 1024 beyond, so that all 64 experts' counts come in one round and the statistics block
+// has 16 waves (64 experts: 29.7 -> 16.2 us; with 8 experts the larger blocks cost 2 us).
+template <int EB, int NT>
+__global__ __launch_bounds__(NT) void dispatch_tc_kernel(DispatchArgs a) {
+  constexpr int kDispatchWaves = NT / 64;
   __shared__ int pre_sh[64];   // this block's slots of expert e come after pre_sh[e] others
   __shared__ int tot_sh[64];   // assignments per expert (before any capacity)
   __shared__ int gs_sh[64];    // group start of expert e (clamped sizes)
   __shared__ int pos_sh[kRouterTokens * 8];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = a.nblk, E = a.E, k = a.k, T = a.T;
-  // wave w sums experts w, w + 4, ...: four experts' rows at a time, every load of the four
-  // issued before any is added (up to 32 in flight per lane), then a wave reduction each
+  // wave w sums experts w, w + waves, ...: four experts' rows at a time (16 per round at 256
+  // threads, all 64 at 1024), every load of the four issued before any is added (up to 32 in
+  // flight per lane), then a wave reduction each
   constexpr int EPC = 4, LPR = kFusedMaxBlocks / 64;  // experts per round, loads per row
-  for (int e0 = wave; e0 < E; e0 += 4 * EPC) {
+  for (int e0 = wave; e0 < E; e0 += kDispatchWaves * EPC) {
     int c[EPC][LPR];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) {
-      const int e = e0 + 4 * i;
+      const int e = e0 + kDispatchWaves * i;
       const int32_t* row = a.blk_counts + (size_t)min(e, E - 1) * nblk;
 #pragma unroll
       for (int j = 0; j < LPR; ++j) {
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(256) void dispatch_tc_kernel(DispatchArgs a) {
         pre += __shfl_xor(pre, o);
         tot += __shfl_xor(tot, o);
       }
-      const int e = e0 + 4 * i;
+      const int e = e0 + kDispatchWaves * i;
       if (lane == 0 && e < E) {
         pre_sh[e] = pre;
         tot_sh[e] = tot;
@@ -251,7 +256,9 @@ __global__ __launch_bounds__(256) void dispatch_tc_kernel(DispatchArgs a) {
   }
   __syncthreads();
   if (b == nblk) {  // the statistics block
-    aux_stats_block<4>(tot_sh, a.blk_psum, a.blk_zsum, nblk, T, E, k, a.f, a.p, a.loss, a.z_loss);
+    // (items per round: 4 in 64 registers per lane at 256 threads, 2 within 1024 threads' 128)
+    aux_stats_block<NT == 1024 ? 2 : 4>(tot_sh, a.blk_psum, a.blk_zsum, nblk, T, E, k, a.f, a.p,
+                                        a.loss, a.z_loss);
     return;
   }
   if (wave == 0) {  // clamped sizes and their exclusive prefix (E <= 64)
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(256) void dispatch_tc_kernel(DispatchArgs a) {
   // row copies: one wave per token, 16-byte pieces, to each kept slot's row
   const size_t row_bytes = (size_t)a.d * EB;
   const int nch = (int)(row_bytes / 16);
-  for (int tt = wave; tt < ntok; tt += 4) {
+  for (int tt = wave; tt < ntok; tt += kDispatchWaves) {
     const char* xr = a.x + (size_t)(t0 + tt) * row_bytes;
     for (int c = lane; c < nch; c += 64) {
       const u32x4 v = ld16(xr + 16 * (size_t)c);
@@ -330,11 +337,18 @@ hipError_t launch_dispatch_tc(const DispatchArgs& a, hipStream_t s) {
   if (a.E < 1 || a.E > 64 || a.k < 1 || a.k > 8 || a.nblk > kFusedMaxBlocks)
     return hipErrorInvalidValue;
   const bool stats = a.f || a.p || a.loss || a.z_loss;
-  dim3 grid(a.nblk + (stats ? 1 : 0)), block(256);
-  if (a.elt_bytes == 2)
-    dispatch_tc_kernel<2><<<grid, block, 0, s>>>(a);
-  else
-    dispatch_tc_kernel<4><<<grid, block, 0, s>>>(a);
+  dim3 grid(a.nblk + (stats ? 1 : 0));
+  if (a.E > 16) {
+    if (a.elt_bytes == 2)
+      dispatch_tc_kernel<2, 1024><<<grid, 1024, 0, s>>>(a);
+    else
+      dispatch_tc_kernel<4, 1024><<<grid, 1024, 0, s>>>(a);
+  } else {
+    if (a.elt_bytes == 2)
+      dispatch_tc_kernel<2, 256><<<grid, 256, 0, s>>>(a);
+    else
+      dispatch_tc_kernel<4, 256><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
