@@ -498,15 +498,17 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 
 // ---------------------------------------------------------------------------------
 // Expert choice: one workgroup (1024 threads) per expert.
-//   column max and sum of exp over the expert's T logits (fixed-order reductions),
-//   radix select (4 x 8 bits, most significant first) of the C-th largest logit key,
-//   then a stable compaction in token order: every key above the threshold plus the
-//   first (C - above) keys equal to it.
+//   column max, min and sum of exp over the expert's T logits (fixed-order reductions),
+//   the C-th largest logit key: one histogram pass over value buckets (monotone in the
+//   logit) and a direct rank of the chosen bucket's keys, or, for a wide bucket, a radix
+//   select (4 x 8 bits of the key, most significant first); then a stable compaction in
+//   token order: every key above the threshold plus the first (C - above) keys equal to
+//   it.
 // The column is read from HBM once, into LDS (INLDS, T <= kEcLdsTokens); every pass
-// after that reads LDS. Each wave counts digits into its own histogram (the logits of
-// one expert share their leading key bits, so one shared histogram would take
-// thousands of same-address atomics), and wave 0 finds the digit holding the C-th key
-// with a prefix sum across its lanes.
+// after that reads LDS. Each wave counts into its own histogram (the logits of one
+// expert share their leading key bits, so one shared histogram would take thousands of
+// same-address atomics), and wave 0 finds the bucket holding the C-th key with a prefix
+// sum across its lanes.
 // ---------------------------------------------------------------------------------
 constexpr int kEcThreads = 1024;
 constexpr int kEcWaves = kEcThreads / 64;
