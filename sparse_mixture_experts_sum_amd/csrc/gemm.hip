@@ -762,7 +762,7 @@ constexpr int kSkSpinLimit = 1 << 22;    // bound on a head's wait for one parti
 // on the mid-size layer), which only a long tile's saved round repays. Measured (A/B in one
 // process): Mixtral-size down projection (448 stages) 3197 -> 3049 us; the 128-stage
 // (mid-size) and 44-stage (64-expert) down projections ran 30% and 22% slower with it.
-constexpr int kSkMinStages = 256;
+constexpr int kSkMinStages = kStreamKMinStages;
 
 struct SkPlan {
   int dp_tiles;   // XCD list positions [0, dp_tiles) are dealt round-robin as whole tiles

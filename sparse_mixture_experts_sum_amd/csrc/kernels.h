@@ -116,6 +116,9 @@ hipError_t launch_permute_ec(const void* x, int elt_bytes, int d, int E, int C,
 // partial == nullptr: no stream-K (every tile whole).
 constexpr int kStreamKSlots = 256;
 constexpr size_t kStreamKSlotBytes = (size_t)256 * 256 * 4;  // a 256 x 256 fp32 tile
+// Only tiles of at least this many K stages (of 32) are split: the down projection of a layer
+// with d_ff < 32 * kStreamKMinStages never uses the scratch, which is then left out.
+constexpr int kStreamKMinStages = 256;
 struct StreamK {
   float* partial;   // [kStreamKSlots * kStreamKSlotBytes / 4]
   int32_t* flags;   // [kStreamKSlots]

@@ -140,9 +140,10 @@ Layout make_layout(const moe_shape& s) {
   if (resid) L.h_lo = L.h + (size_t)L.R * f * eb;
   L.o = take((size_t)hrows * d * 4);
   if (resid) L.o_lo = L.o + (size_t)L.R * d * 4;
-  // bf16 GEMMs split the tiles of their last partial round along K (stream-K): one fp32
-  // partial slot and one flag per workgroup
-  L.stream_k = s.dtype == MOE_BF16;
+  // the bf16 down projection splits the tiles of its last partial round along K (stream-K)
+  // when they have kStreamKMinStages K stages or more: one fp32 partial slot and one flag
+  // per workgroup
+  L.stream_k = s.dtype == MOE_BF16 && f / 32 >= kStreamKMinStages;
   if (L.stream_k) {
     L.sk_partial = take((size_t)kStreamKSlots * kStreamKSlotBytes);
     L.sk_flags = take((size_t)kStreamKSlots * 4);

@@ -156,15 +156,21 @@ def test_workspace_offsets_are_inside(M):
         off = M.workspace_offset(s32, M.WS_XPERM)
         assert 0 <= off < M.workspace_size(s32) and off % 256 == 0
     # the gathered layout needs no copy buffer: past the shared regions the bf16 workspace
-    # holds no x_perm (its h follows src directly), and bf16 adds the down projection's
-    # stream-K partial slots (256 x 256 KB) and flags
+    # holds no x_perm (its h follows src directly); bf16 adds the down projection's stream-K
+    # partial slots (256 x 256 KB) and flags once d_ff reaches 256 K stages of 32 (8192),
+    # the shortest K the down projection splits
     s16 = M.make_shape(1000, 256, 512, 8, 2)
     s32 = M.make_shape(1000, 256, 512, 8, 2, dtype="fp32")
     R, d = 2000, 256
     assert M.workspace_offset(s32, M.WS_H) - M.workspace_offset(s32, M.WS_SRC) >= R * d * 4
     assert M.workspace_offset(s16, M.WS_H) - M.workspace_offset(s16, M.WS_SRC) < 256 * 64
     sk = 256 * 256 * 256 * 4 + 256 * 4
-    assert M.workspace_size(s16) >= M.workspace_offset(s16, M.WS_O) + R * d * 4 + sk
+    assert M.workspace_offset(s16, M.WS_O) + R * d * 4 <= M.workspace_size(s16)
+    assert M.workspace_size(s16) < M.workspace_offset(s16, M.WS_O) + R * d * 4 + sk
+    for f, with_sk in ((8128, False), (8192, True)):
+        sf = M.make_shape(1000, 256, f, 8, 2)
+        end_o = M.workspace_offset(sf, M.WS_O) + R * d * 4
+        assert (M.workspace_size(sf) >= end_o + sk) == with_sk, f
     with pytest.raises(M.MoEError):
         M.workspace_offset(M.make_shape(1000, 256, 512, 8, 2, mode="ec"), M.WS_POS)
 

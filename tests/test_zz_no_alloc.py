@@ -1,9 +1,9 @@
 """The allocation-free entry point (moe_forward_noalloc, workspace in the library's fixed
 device array) against moe_forward with a caller workspace, through the C ABI: the same
-kernels, so every output must be bitwise equal, and y must meet the oracle's bar. Three
+kernels, so every output must be bitwise equal, and y must meet the oracle's bar. Four
 calls in a row on one GPU, each smaller than the one before (the array keeps the previous
 call's intermediates, which must not leak into the next), then a shape too large for the
-array, which is refused."""
+array, which is refused before anything is launched."""
 from __future__ import annotations
 
 import sys
@@ -69,9 +69,29 @@ def _compare(M, w):
     _say(f"  ok: bitwise equal to moe_forward, y err {err:.3e}")
 
 
-def test_noalloc_three_calls_shrinking(moe):
+def test_noalloc_calls_shrinking(moe):
+    # four calls, each smaller than the one before: the 16-expert expert-choice layer (its
+    # workspace 0.20 GB of the 0.27 GB array), the mid-size layer, a small token-choice one and
+    # an fp32 expert-choice one
+    _compare(moe, W.EXPERT_CHOICE)
     _compare(moe, W.MID_BF16)
     _compare(moe, W.custom("noalloc_small", T=1000, d=256, f=512, E=8, k=2, bias_std=0.5,
                            seed=(42, 620)))
     _compare(moe, W.custom("noalloc_ec_fp32", dtype="fp32", T=300, d=128, f=192, E=6, mode="ec",
                            cf=1.5, k=1, x_std=0.5, wg_std=0.2, seed=(42, 621)))
+
+
+def test_noalloc_refuses_a_layer_larger_than_its_array(moe):
+    # the Mixtral-size layer needs 1.5 GB of workspace: refused on the host (status 4,
+    # MOE_ERR_WORKSPACE_TOO_SMALL), before any launch
+    T, d, f, E = 16384, 4096, 14336, 8
+    assert moe.workspace_size(moe.make_shape(T, d, f, E, 2)) > moe.NOALLOC_SCRATCH_BYTES
+    dev = torch.device("cuda")
+    x = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    Wg = torch.empty(d, E, dtype=torch.bfloat16, device=dev)
+    Wgu = torch.empty(E, d, f, dtype=torch.bfloat16, device=dev)
+    Wd = torch.empty(E, f, d, dtype=torch.bfloat16, device=dev)
+    _say("noalloc refusal", (T, d, f, E))
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_forward_noalloc(x, Wg, None, Wgu, Wgu, Wd, k=2)
+    assert ei.value.status == 4
