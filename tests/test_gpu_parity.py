@@ -212,6 +212,28 @@ def test_expert_choice_long_column(moe):
                               bias_std=0.3, seed=(42, 340)))
 
 
+def test_expert_choice_boundary_ties_in_one_value_bucket(moe):
+    # 2000 tokens repeating 50 rows: every logit value occurs 40 times, and each expert's
+    # 250th largest logit sits inside such a group of 40 equal keys (the 50 distinct values are
+    # 2.3e-3 or more apart, so fp32 and fp64 order them alike). The select's value bucket holds
+    # the group; the lowest 10 token indices of it must be taken, exactly as the oracle's
+    # stable order takes them, and every list must match the oracle's.
+    w = W.custom("ec_ties", T=2000, d=128, f=128, E=8, k=1, mode="ec", cf=1.0, wg_std=0.3,
+                 seed=(42, 713))
+    inp = W.make_inputs(w)
+    inp["x"][:] = inp["x"][np.arange(w.T) % 50]
+    out, _ = run_ec_case(moe, w, inp=inp)
+    ref = O.forward_ec(inp["x"], inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"], inp["Wdown"], w.cf)
+    assert np.array_equal(_np(out["idx"]), ref["idx"])
+
+
+def test_dispatch_17_experts(moe):
+    # just past 16 experts: the 1024-thread dispatch blocks (every expert's counts in one
+    # round), 32 padded experts in the router
+    run_tc_case(moe, W.custom("dispatch_E17", T=3000, d=128, f=128, E=17, k=2, wg_std=0.3,
+                              bias_std=0.5, seed=(42, 343)))
+
+
 def test_dispatch_scan_many_blocks(moe):
     # 313 router blocks x 64 experts = 20032 count entries, summed by every block of the
     # fused dispatch kernel

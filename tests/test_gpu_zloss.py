@@ -94,6 +94,13 @@ def test_zloss_large_logits(moe):
                              bias_std=60.0, seed=(42, 220)), route_only=True)
 
 
+def test_zloss_40_experts_statistics_rounds(moe):
+    # 40 experts: the dispatch's 1024-thread statistics block takes the 41 items (40 experts
+    # and the z-loss) in two rounds of 32, the z-loss item in the second
+    run_z_case(moe, W.custom("z_e40", T=1500, d=256, f=128, E=40, k=3, bias_std=0.5,
+                             seed=(42, 231)))
+
+
 def test_zloss_changes_nothing_else(moe):
     # the same call with and without the z-loss: every other output bitwise equal,
     # and the router-only z-loss equals the layer's
