@@ -160,8 +160,8 @@ moe_status moe_workspace_size(const moe_shape* shape, size_t* bytes);
  *   MOE_WS_H       [R, d_ff]     dtype, silu(x W_gate) * (x W_up) per row
  *   MOE_WS_O       [R, d_model]  fp32, expert output per row (before weighting)
  * Expert choice in bf16 carries h's bf16 rounding residual: the MOE_WS_H region then holds
- * 2R rows (h, then the residual), MOE_WS_O 2R rows (their down projections; the expert output
- * is the sum of rows r and R + r), and MOE_WS_OFFSETS 2E+1 entries (g*C).
+ * 2R rows (h, then the residual), and MOE_WS_O row r is the down projection of row r plus
+ * that of row R + r.
  * R = T*k (token choice) or E*C (expert choice). With an expert capacity only rows
  * [0, offsets[E]) hold kept slots, offsets[E] = sum_e min(counts_e, C). MOE_WS_POS is
  * MOE_ERR_UNSUPPORTED in expert choice. */
@@ -229,8 +229,9 @@ moe_status moe_route(const moe_shape* shape, const void* x, const void* W_g, con
  * and rounded to bf16 for the down projection. In expert choice the bf16 rounding
  * residual of h is carried as a second bf16 term (h ~ h_hi + h_lo): expert-choice scores
  * span a wide range across tokens, and a single rounding of h would cost about 2.5% of
- * the output RMS on the 16-expert workload; the pair costs one extra down-projection
- * pass. */
+ * the output RMS on the 16-expert workload; the pair doubles the down projection's
+ * multiply work (each tile takes 128 tokens' rows and their residual rows, and sums the
+ * two products before storing o). */
 moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, const float* b_g,
                        const moe_noise* noise, const void* W_gate, const void* W_up,
                        const void* W_down, float* y,

@@ -80,7 +80,6 @@ __global__ __launch_bounds__(256) void combine_tc_kernel(const float* __restrict
 
 // one wave per token; lane e < E searches expert e's token list
 __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict__ o,
-                                                         const float* __restrict__ o_lo,
                                                          const int32_t* __restrict__ idx,
                                                          const float* __restrict__ score, int T,
                                                          int d, int E, int C,
@@ -114,9 +113,8 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
       m &= m - 1;
       const int r = __shfl(row, e);
       const float s = __shfl(sc, e);
-      f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c));
-      if (o_lo)
-        v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_lo + (size_t)r * d + 4 * c));
+      const f32x4 v =
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c));
       acc += s * v;
     }
     __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * c));
@@ -188,10 +186,9 @@ hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w,
   return hipGetLastError();
 }
 
-hipError_t launch_combine_ec(const float* o, const float* o_lo, const int32_t* idx,
-                             const float* score, int T, int d, int E, int C, float* y,
-                             hipStream_t s) {
-  combine_ec_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, o_lo, idx, score, T, d, E, C, y);
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
+                             int E, int C, float* y, hipStream_t s) {
+  combine_ec_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, idx, score, T, d, E, C, y);
   return hipGetLastError();
 }
 

@@ -27,8 +27,9 @@
 //     (256 x 128, 256 x 64) use the plain ring (ring_step);
 //   * gate and up tiles share the A tile; the SwiGLU epilogue silu(g) * u runs in
 //     registers and writes h in bf16 (plus its bf16 residual when asked: SPLIT). The
-//     down projection writes o in fp32; group e takes weight matrix e % EW, so that the
-//     residual rows can run as groups of their own against the same weights.
+//     down projection writes o in fp32; with SPLIT it runs h and its residual as pairs:
+//     a 256-row tile holds 128 tokens' main and residual rows, and the epilogue adds the
+//     two products of each token before its single store.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles, 4x4 outputs per thread).
 #include "common.h"
@@ -369,11 +370,12 @@ struct GemmArgs {
   const bf16* B1;        // W_up (SwiGLU)
   const int32_t* offsets;
   int E, K, N;
-  int EW;                // weight matrices: group e uses matrix e % EW
   void* out;             // h (bf16) or o (fp32)
   void* out2;            // h_lo (bf16, SPLIT): the bf16 rounding residual of h
   float* partial;        // stream-K partial sums, one slot per workgroup (nullptr: no stream-K)
   int32_t* flags;        // stream-K: flags[slot] = 1 once that slot's partial is written
+  int lo_rows;           // paired down projection (SPLIT): each main row's residual row sits
+                         // lo_rows rows after it in A
 };
 
 // One output tile: expert e, rows [row0, row0 + rows), output columns from n0.
@@ -394,9 +396,7 @@ struct TileCoord {
 //    slice of the group's weight columns, for all of the group's rows.
 //  - Contiguous (every group small: the split order would give each XCD under 4 tiles of a
 //    group, the columns order under 2, or under 6 when the rows are gathered from x): the
-//    groups' lists are concatenated,
-//    groups that share a weight matrix next to each other, and XCD x takes the x-th
-//    eighth of the whole list. The tiles an XCD runs together then come from one or a few
+//    groups' lists are concatenated and XCD x takes the x-th eighth of the whole list. The tiles an XCD runs together then come from one or a few
 //    groups and share their weight columns and rows in the XCD's L2; split, they would
 //    come from a different group each. (Measured: contiguous gains where split leaves
 //    an XCD up to 2-3 tiles per group (mid-size down projection, A/B in one process:
@@ -409,7 +409,7 @@ constexpr int kContigTiles = 16;        // max tiles per group for contiguous, p
 constexpr int kContigSplitTiles = 32;   // the same where the columns order does not apply
 constexpr int kContigGatherTiles = 48;  // the same, rows gathered from x
 struct TileMap {
-  int NT, xcd, E, EW;
+  int NT, xcd, E;
   bool contiguous;
   int base;      // contiguous: this XCD's first tile in the whole list
   int my_total;  // tiles of this XCD
@@ -419,13 +419,12 @@ struct TileMap {
 // CONTIG_OK: the shape allows the contiguous order (a group of one M-tile has NT tiles,
 // so NT at or above the threshold rules it out; the launch picks the instantiation).
 template <int BM, bool CONTIG_OK>
-__device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int EW, int NT,
-                                                 int xcd, bool gathered, int gn) {
+__device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int NT, int xcd,
+                                                 bool gathered, int gn) {
   TileMap m;
   m.NT = NT;
   m.xcd = xcd;
   m.E = E;
-  m.EW = EW;
   m.nx = NT / kXcds;
   m.gn = gn;
   long long total = 0, maxpe = 0;
@@ -441,9 +440,8 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
     col_total += mte * m.nx;
   }
   // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
-  m.contiguous =
-      CONTIG_OK && E % EW == 0 &&
-      maxpe < (gathered ? kContigGatherTiles : (gn > 0 ? kContigTiles : kContigSplitTiles));
+  m.contiguous = CONTIG_OK && maxpe < (gathered ? kContigGatherTiles
+                                                : (gn > 0 ? kContigTiles : kContigSplitTiles));
   if (m.contiguous) m.gn = 0;
   m.base = m.contiguous ? (int)((total * xcd) >> 3) : 0;
   m.my_total = m.contiguous ? (int)((total * (xcd + 1)) >> 3) - m.base
@@ -459,18 +457,14 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
 // an integer division per step in the contiguous order).
 struct TileCursor {
   int e;        // group
-  int j;        // contiguous order: list position of group e (jr = j % G, jq = j / G)
-  int jr, jq;
   int acc;      // list index of group e's first tile
   int pe;       // group e's tiles in the list
   int mte;      // group e's M-tiles
   int plo;      // split order: first of the group's tiles that this XCD takes
-  int G;        // contiguous order: groups per weight matrix
 };
 
 template <int BM, bool CONTIG>
 __device__ __forceinline__ void cursor_load(TileCursor& c, const int32_t* offsets, const TileMap& m) {
-  c.e = CONTIG ? c.jr * m.EW + c.jq : c.e;
   c.mte = (offsets[c.e + 1] - offsets[c.e] + BM - 1) / BM;
   if constexpr (CONTIG) {
     c.pe = c.mte * m.NT;
@@ -487,10 +481,8 @@ template <int BM, bool CONTIG>
 __device__ __forceinline__ TileCursor make_cursor(const int32_t* offsets, const TileMap& m) {
   TileCursor c;
   c.e = 0;
-  c.j = c.jr = c.jq = 0;
   c.acc = 0;
   c.plo = 0;
-  c.G = m.E / m.EW;
   cursor_load<BM, CONTIG>(c, offsets, m);
   return c;
 }
@@ -503,17 +495,9 @@ __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, 
                                                  int bn_out, TileCursor& c) {
   const int gi = CONTIG ? m.base + i : i;
   // (the bound on the group keeps a cursor that would run past the last group in range)
-  while (gi >= c.acc + c.pe && c.j < m.E - 1) {
+  while (gi >= c.acc + c.pe && c.e < m.E - 1) {
     c.acc += c.pe;
-    ++c.j;
-    if constexpr (CONTIG) {
-      if (++c.jr == c.G) {
-        c.jr = 0;
-        ++c.jq;
-      }
-    } else {
-      c.e = c.j;
-    }
+    ++c.e;
     cursor_load<BM, CONTIG>(c, offsets, m);
   }
   const int e = c.e, mte = c.mte;
@@ -533,8 +517,7 @@ __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, 
     return t;
   }
   // split: position p of the group's N-tile-major list; contiguous: the same, from the
-  // group's start in the whole list (group at list position j is (j mod G) * EW + j / G:
-  // the G groups of weight matrix w sit next to each other)
+  // group's start in the whole list
   const int p = CONTIG ? gi - c.acc : c.plo + (gi - c.acc);
   const int nt = p / mte, mtl = p - nt * mte;
   t.row0 = offsets[e] + mtl * BM;
@@ -608,17 +591,26 @@ __device__ __forceinline__ StageLoader<G, SWIGLU, SPLIT> make_loader(const GemmA
   // elements); contiguous rows: offsets from the tile's first row
   const size_t koff = (size_t)ks0 * G::BK;
   ld.Ab = (a.gather ? a.A : a.A + (size_t)t.row0 * a.K) + koff;
+  if constexpr (!SWIGLU && SPLIT) {
+    // the paired tile's rows 64 .. 127 of each half are residual rows: waves 1 and 3 load
+    // exactly those (64 rows per wave), from lo_rows rows further on
+    static_assert(G::A_PW * G::A_RPI == 64 && G::WM == 128, "paired tile layout");
+    if (wave & 1) ld.Ab += (size_t)a.lo_rows * a.K;
+  }
   ld.nk = nk;
   ld.N = a.N;
   ld.wave = wave;
-  const int ew = t.e < a.EW ? t.e : t.e % a.EW;
-  const bf16* W0 = a.B0 + (size_t)ew * a.K * a.N + koff * a.N;
-  const bf16* W1 = SWIGLU ? a.B1 + (size_t)ew * a.K * a.N + koff * a.N : W0;
+  const bf16* W0 = a.B0 + (size_t)t.e * a.K * a.N + koff * a.N;
+  const bf16* W1 = SWIGLU ? a.B1 + (size_t)t.e * a.K * a.N + koff * a.N : W0;
 #pragma unroll
   for (int j = 0; j < G::A_PW; ++j) {
     const int row = (wave * G::A_PW + j) * G::A_RPI + ln / G::A_CPR;
     const int c = (ln % G::A_CPR) ^ a_swz<G::A_CPR>(row);
-    const int ar = a.gather ? gv[j] : min(row, t.rows - 1);
+    // paired down projection: tile row w * 128 + q (w = wm) holds token w * 64 + q % 64,
+    // its main row for q < 64 and its residual row (wave base above) for q >= 64
+    const int ar = (!SWIGLU && SPLIT) ? min((row >> 7) * 64 + (row & 63), t.rows - 1)
+                   : a.gather         ? gv[j]
+                                      : min(row, t.rows - 1);
     ld.a_src[j] = ar * a.K + c * 8;
   }
 #pragma unroll
@@ -660,13 +652,16 @@ __device__ __forceinline__ u32x4 swap_halves(const u32x2 (&v)[2]) {
 
 // Epilogue: acc[nb][mb][4q + i] = out[row m][col ncol + i], m = lane % 32 of block mb,
 // ncol = 8q + 4 * (lane / 32) inside 32-column block nb. SwiGLU: h = silu(gate) * up in
-// bf16 (and the bf16 residual of h when SPLIT); down projection: o in fp32.
+// bf16 (and the bf16 residual of h when SPLIT); down projection: o in fp32, with SPLIT
+// (paired tile) o = acc[mb] + acc[mb + MB / 2] for token wm * 64 + mb * 32 + lane % 32.
 template <class G, bool SWIGLU, bool SPLIT>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t, int ln, int wm,
                                            int wn, const f32x16 (&acc)[G::NBW][G::MB]) {
+  constexpr bool PAIRED = !SWIGLU && SPLIT;
+  constexpr int MBO = PAIRED ? G::MB / 2 : G::MB;  // row blocks stored per wave
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb) {
-    const int m = wm * G::WM + mb * 32 + (ln & 31);
+  for (int mb = 0; mb < MBO; ++mb) {
+    const int m = wm * (MBO * 32) + mb * 32 + (ln & 31);
     if (m >= t.rows) continue;
     const size_t rowoff = (size_t)(t.row0 + m) * a.N + t.n0;
     if constexpr (SWIGLU) {
@@ -728,9 +723,17 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileCoord& t
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int ncol = wn * G::WNL + nb * 32 + 8 * q + 4 * (ln >> 5);
-          const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
-                           acc[nb][mb][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + rowoff + ncol) = v;
+          float* const dst = static_cast<float*>(a.out) + rowoff + ncol;
+          if constexpr (PAIRED) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[nb][mb][4 * q + i] + acc[nb][mb + MBO][4 * q + i];
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+            const f32x4 v = {acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1],
+                             acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(dst) = v;
+          }
         }
     }
   }
@@ -940,22 +943,24 @@ __device__ __forceinline__ void add_partials(const GemmArgs& a, const TileCoord&
 // multiple of S (whole chunks), so that stage s of every item sits in ring buffer s % S.
 // (The next item's fragments are read after the epilogue: holding them through it would
 // leave too few registers.)
-// (TAG: see k_loop)
-template <class G, bool SWIGLU, bool SPLIT, int BM, int BNL, bool CONTIG, int TAG>
+// (TR: rows of the grouped problem per tile; TAG: see k_loop)
+template <class G, bool SWIGLU, bool SPLIT, int TR, int BNL, bool CONTIG, int TAG>
 __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm, int slot,
                                             int nslot, int wave, int wm, int wn, int nk,
                                             char* const (&ring)[G::STAGES]) {
   constexpr int S = G::STAGES;
   static_assert(S == 4, "the pipelined loop is written out for a ring of 4");
-  const SkPlan sp = make_sk_plan(tm.my_total, slot, nslot, nk, !SWIGLU && a.partial != nullptr);
+  // stream-K: the plain down projection only (paired tiles sum in the epilogue)
+  constexpr bool SK = !SWIGLU && !SPLIT;
+  const SkPlan sp = make_sk_plan(tm.my_total, slot, nslot, nk, SK && a.partial != nullptr);
   ItemIt it{0, sp.c_beg};
   Item cur;
   if (!next_item(it, sp, slot, nslot, nk, cur)) return;
   int ln = fresh_lane();
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-  TileCursor cur_c = make_cursor<BM, CONTIG>(a.offsets, tm);
-  TileCoord t = locate_tile<BM, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT, cur_c);
+  TileCursor cur_c = make_cursor<TR, CONTIG>(a.offsets, tm);
+  TileCoord t = locate_tile<TR, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT, cur_c);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
   StageLoader<G, SWIGLU, SPLIT> ld =
@@ -983,7 +988,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
     Item nx = cur;
     const bool has_next = next_item(it, sp, slot, nslot, nk, nx);
     const TileCoord tn =
-        has_next ? locate_tile<BM, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT, cur_c) : t;
+        has_next ? locate_tile<TR, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT, cur_c) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
@@ -1010,11 +1015,11 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
     PipeStep<G, SWIGLU, SPLIT, 3, false>::run(S - 2, false, true, ldn, 3, ring, a_frag, b_frag,
                                               acc, F1, F0);
     ln = fresh_lane();
-    if (!SWIGLU && cur.role == kPiece) {
+    if (SK && cur.role == kPiece) {
       put_partial<G>(a, (int)blockIdx.x, ln, wm, wn, acc);
     } else {
       store_tile<G, SWIGLU, SPLIT>(a, t, ln, wm, wn, acc);
-      if (!SWIGLU && cur.role == kHead) {
+      if (SK && cur.role == kHead) {
         // the workgroups whose runs cover the rest of this tile
         const int u = cur.tile - sp.dp_tiles;
         add_partials<G>(a, t, (int)blockIdx.x & (kXcds - 1), slot,
@@ -1033,7 +1038,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
-    const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int EW,
+    const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int lo_rows,
     void* __restrict__ out, void* __restrict__ out2, int gn, float* __restrict__ partial,
     int32_t* __restrict__ flags) {
   using G = Geo<BM, BNL, SWIGLU, SPLIT, NW>;
@@ -1052,37 +1057,43 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   // one wave per SIMD on 256 x 256 tiles: the software-pipelined loop
   constexpr bool PIPE = NW == 4 && BM == 256 && BNL == 256;
+  // rows of the grouped problem per tile: BM, or BM / 2 tokens in the paired down projection
+  constexpr bool PAIRED = !SWIGLU && SPLIT;
+  constexpr int TR = PAIRED ? BM / 2 : BM;
 
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
   // this XCD's tiles (the order is described at TileMap)
-  const TileMap tm = make_tile_map<BM, CONTIG_OK>(offsets, E, EW, NT, xcd, gather != nullptr, gn);
+  const TileMap tm = make_tile_map<TR, CONTIG_OK>(offsets, E, NT, xcd, gather != nullptr, gn);
   const int my_total = tm.my_total;
   const int nk = K / G::BK;
   const int nk_total = nk;
 
-  const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, EW, out, out2,
-                      PIPE && gridDim.x <= kSkSlots ? partial : nullptr, flags};
+  // (no stream-K in the paired down projection: a piece's partial sums would need the pair
+  // sum of the epilogue)
+  const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, out, out2,
+                      PIPE && !PAIRED && gridDim.x <= kSkSlots ? partial : nullptr, flags,
+                      lo_rows};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
       if (CONTIG_OK && tm.contiguous)
-        pipe_stream<G, SWIGLU, SPLIT, BM, BNL, CONTIG_OK, CONTIG_OK>(args, tm, slot, nslot, wave,
+        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, CONTIG_OK, CONTIG_OK>(args, tm, slot, nslot, wave,
                                                                      wm, wn, nk, ring);
       else
-        pipe_stream<G, SWIGLU, SPLIT, BM, BNL, false, CONTIG_OK>(args, tm, slot, nslot, wave, wm,
+        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, false, CONTIG_OK>(args, tm, slot, nslot, wave, wm,
                                                                  wn, nk, ring);
       return;
     }
   }
-  TileCursor cur_c = make_cursor<BM, false>(offsets, tm);
-  TileCursor cur_cc = make_cursor<BM, CONTIG_OK>(offsets, tm);
+  TileCursor cur_c = make_cursor<TR, false>(offsets, tm);
+  TileCursor cur_cc = make_cursor<TR, CONTIG_OK>(offsets, tm);
   for (int i = slot; i < my_total; i += nslot) {
     const int ln = fresh_lane();
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
     const TileCoord t = CONTIG_OK && tm.contiguous
-                            ? locate_tile<BM, CONTIG_OK>(i, offsets, tm, G::BN_OUT, cur_cc)
-                            : locate_tile<BM, false>(i, offsets, tm, G::BN_OUT, cur_c);
+                            ? locate_tile<TR, CONTIG_OK>(i, offsets, tm, G::BN_OUT, cur_cc)
+                            : locate_tile<TR, false>(i, offsets, tm, G::BN_OUT, cur_c);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
     const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, 0, gv);
@@ -1188,8 +1199,8 @@ int column_block(int NT) {
 
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, const void* B1,
-                       const int32_t* offsets, int E, int EW, int K, int N, void* out, void* out2,
-                       const StreamK& sk, hipStream_t s) {
+                       const int32_t* offsets, int E, int K, int N, void* out, void* out2,
+                       int lo_rows, const StreamK& sk, hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
   // only below the threshold (kernels for wider outputs are built without it; split-order
@@ -1199,11 +1210,11 @@ hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, con
   if (NT < (gather ? kContigGatherTiles : kContigTiles))
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, true><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn, sk.partial, sk.flags);
+        static_cast<const bf16*>(B1), offsets, E, K, N, lo_rows, out, out2, gn, sk.partial, sk.flags);
   else
     gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, false><<<grid, 64 * NW, 0, s>>>(
         static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, EW, out, out2, gn, sk.partial, sk.flags);
+        static_cast<const bf16*>(B1), offsets, E, K, N, lo_rows, out, out2, gn, sk.partial, sk.flags);
   return hipGetLastError();
 }
 
@@ -1212,22 +1223,24 @@ hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate,
                        const int32_t* offsets, int E, int d, int f, void* h, void* h_lo,
                        const StreamK& sk, hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d,
-                                                         f, h, h_lo, sk, s);
-  return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, E, d, f, h, h_lo,
-                                               sk, s);
+    return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo,
+                                                 0, sk, s);
+  return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo,
+                                               0, sk, s);
 }
 
-hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int EW,
-                     int f, int d, float* o, const StreamK& sk, hipStream_t s) {
+// PAIRED: h's residual rows sit lo_rows rows after their main rows (see store_tile)
+template <bool PAIRED>
+hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int f,
+                     int d, float* o, int lo_rows, const StreamK& sk, hipStream_t s) {
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW,
-                                                          f, d, o, nullptr, sk, s);
+    return launch_bf16<256, 256, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+                                                   o, nullptr, lo_rows, sk, s);
   if (d % 128 == 0)
-    return launch_bf16<256, 128, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d,
-                                                  o, nullptr, sk, s);
-  return launch_bf16<256, 64, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, EW, f, d, o,
-                                               nullptr, sk, s);
+    return launch_bf16<256, 128, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+                                                   o, nullptr, lo_rows, sk, s);
+  return launch_bf16<256, 64, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d, o,
+                                                nullptr, lo_rows, sk, s);
 }
 
 }  // namespace
@@ -1249,10 +1262,13 @@ hipError_t launch_gemm_gateup(int bf16in, const void* xp, const int32_t* gather,
 }
 
 hipError_t launch_gemm_down(int bf16in, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int EW, int R_max, int f, int d, float* o, const StreamK& sk,
-                            hipStream_t s) {
-  if (bf16in) return down_bf16(h, Wdown, offsets, E, EW, f, d, o, sk, s);
-  if (EW != E) return hipErrorInvalidValue;  // the fp32 path runs one matrix per group
+                            int E, int R_max, int f, int d, float* o, int lo_rows,
+                            const StreamK& sk, hipStream_t s) {
+  if (bf16in) {
+    if (lo_rows > 0) return down_bf16<true>(h, Wdown, offsets, E, f, d, o, lo_rows, sk, s);
+    return down_bf16<false>(h, Wdown, offsets, E, f, d, o, 0, sk, s);
+  }
+  if (lo_rows > 0) return hipErrorInvalidValue;  // the fp32 path has no residual rows
   dim3 grid(d / 64, R_max / 64 + E);
   gemm_f32_kernel<false><<<grid, 256, 0, s>>>(static_cast<const float*>(h),
                                               static_cast<const float*>(Wdown), nullptr, offsets,

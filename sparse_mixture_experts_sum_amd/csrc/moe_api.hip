@@ -22,9 +22,8 @@ struct Layout {
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
          offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
-         o_lo = 0, sk_partial = 0, sk_flags = 0, total = 0;
+         sk_partial = 0, sk_flags = 0, total = 0;
   bool stream_k = false;  // bf16: the GEMMs' stream-K partial slots and flags exist
-  int ngroups = 0;  // groups of the down projection: E, or 2E with the residual rows
   bool xperm = false;  // rows copied into x_perm (else the gate/up GEMM gathers them from x)
 };
 
@@ -79,8 +78,8 @@ moe_status check_shape(const moe_shape* s) {
     const int64_t C = ec_capacity(*s);
     if (C < 1 || C > s->T) return MOE_ERR_BAD_SHAPE;
     if (C * (int64_t)s->E >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
-    // bf16 carries h's rounding residual as E * C more rows of the down projection, whose
-    // group offsets are int32 too
+    // bf16 carries h's rounding residual as E * C more rows of h, addressed by int32 row
+    // indices too
     if (s->dtype == MOE_BF16 && 2 * C * (int64_t)s->E >= (int64_t(1) << 31))
       return MOE_ERR_UNSUPPORTED;
   }
@@ -123,12 +122,11 @@ Layout make_layout(const moe_shape& s) {
   }
   L.blk_zsum = take((size_t)L.nblk * 4);
   // expert choice, bf16: h's bf16 rounding residual is carried as rows R .. 2R-1 of the
-  // h region, and the down projection runs them as E more groups (same weights) into
-  // rows R .. 2R-1 of the o region; the combine adds the two halves
+  // h region; the down projection takes each row with its residual row and writes their
+  // products' sum
   const bool resid = s.mode == MOE_EXPERT_CHOICE && s.dtype == MOE_BF16;
   const int64_t hrows = resid ? 2 * L.R : L.R;
-  L.ngroups = resid ? 2 * s.E : s.E;
-  L.offsets = take((size_t)(L.ngroups + 1) * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
   L.counts = take(E * 4);
   L.src = take(L.R * 4);
   // bf16: the gate/up GEMM loads its rows straight from x through src (per-lane addresses of
@@ -138,12 +136,11 @@ Layout make_layout(const moe_shape& s) {
   if (L.xperm) L.x_perm = take((size_t)L.R * d * eb);
   L.h = take((size_t)hrows * f * eb);
   if (resid) L.h_lo = L.h + (size_t)L.R * f * eb;
-  L.o = take((size_t)hrows * d * 4);
-  if (resid) L.o_lo = L.o + (size_t)L.R * d * 4;
+  L.o = take((size_t)L.R * d * 4);
   // the bf16 down projection splits the tiles of its last partial round along K (stream-K)
   // when they have kStreamKMinStages K stages or more: one fp32 partial slot and one flag
-  // per workgroup
-  L.stream_k = s.dtype == MOE_BF16 && f / 32 >= kStreamKMinStages;
+  // per workgroup (not with the residual rows, whose pairs are summed in the epilogue)
+  L.stream_k = s.dtype == MOE_BF16 && !resid && f / 32 >= kStreamKMinStages;
   if (L.stream_k) {
     L.sk_partial = take((size_t)kStreamKSlots * kStreamKSlotBytes);
     L.sk_flags = take((size_t)kStreamKSlots * 4);
@@ -350,8 +347,8 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     MOE_LAUNCH(MOE_STAGE_ROUTER, launch_router(a, bf, 1, stream));
     MOE_LAUNCH(MOE_STAGE_EC_SELECT,
                launch_ec_select(at<float>(ws, L.logitsT), (int)s.T, s.E, (int)L.C, idx, w, probs,
-                                at<int32_t>(ws, L.offsets), L.ngroups, user_counts,
-                                select_src, sk_flags, stream));
+                                at<int32_t>(ws, L.offsets), user_counts, select_src, sk_flags,
+                                stream));
   }
   return MOE_OK;
 }
@@ -514,17 +511,14 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
              launch_gemm_gateup(bf, x_perm ? x_perm : x, x_perm ? nullptr : src, W_gate, W_up,
                                 offsets, E, R, d, ff, at<void>(ws, L.h), h_lo, sk, stream));
   MOE_LAUNCH(MOE_STAGE_GEMM_DOWN,
-             launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, L.ngroups, E,
-                              (int)(L.h_lo ? 2 * L.R : L.R), ff, d, at<float>(ws, L.o), sk,
-                              stream));
+             launch_gemm_down(bf, at<void>(ws, L.h), W_down, offsets, E, R, ff, d,
+                              at<float>(ws, L.o), h_lo ? R : 0, sk, stream));
   if (is_tc(s.mode)) {
     MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_tc(at<float>(ws, L.o), at<int32_t>(ws, L.pos),
                                                     w_b, T, d, s.k, y, stream));
     // (f, p, loss and z_loss came out of the dispatch scan)
   } else {
-    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o),
-                                                    L.o_lo ? at<float>(ws, L.o_lo) : nullptr,
-                                                    idx_b, w_b, T, d, E,
+    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, T, d, E,
                                                     (int)L.C, y, stream));
     if (z_loss)
       MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, T, 0, s.k, nullptr,

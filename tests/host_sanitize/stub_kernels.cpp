@@ -55,15 +55,15 @@ hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t) {
 }
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
-                            float* probs, int32_t* offsets, int ngroups, int32_t* counts,
-                            int32_t* src, int32_t* sk_flags, hipStream_t) {
+                            float* probs, int32_t* offsets, int32_t* counts, int32_t* src,
+                            int32_t* sk_flags, hipStream_t) {
   ++g_launches;
   inside(logitsT, (size_t)E * T * 4, "select logits");
   inside(idx, (size_t)E * C * 4, "select idx");
   inside(src, (size_t)E * C * 4, "select src");
   inside(sk_flags, (size_t)kStreamKSlots * 4, "select stream-K flags");
   inside(score, (size_t)E * C * 4, "select scores");
-  inside(offsets, (size_t)(ngroups + 1) * 4, "select offsets");
+  inside(offsets, (size_t)(E + 1) * 4, "select offsets");
   (void)probs;
   (void)counts;
   return hipSuccess;
@@ -145,16 +145,17 @@ hipError_t launch_gemm_gateup(int bf16, const void* xp, const int32_t* gather, c
 }
 
 hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const int32_t* offsets,
-                            int E, int EW, int R_max, int f, int d, float* o, const StreamK& sk,
-                            hipStream_t) {
+                            int E, int R_max, int f, int d, float* o, int lo_rows,
+                            const StreamK& sk, hipStream_t) {
   ++g_launches;
   const size_t eb = bf16 ? 2 : 4;
-  inside(h, (size_t)R_max * f * eb, "down h");
+  // with residual rows the h rows run to R_max + lo_rows
+  inside(h, (size_t)(R_max + lo_rows) * f * eb, "down h");
   inside(offsets, (size_t)(E + 1) * 4, "down offsets");
   inside(o, (size_t)R_max * d * 4, "down o");
   inside(sk.partial, kStreamKSlots * kStreamKSlotBytes, "stream-K partials");
   inside(sk.flags, kStreamKSlots * 4, "stream-K flags");
-  (void)Wdown, (void)EW;
+  (void)Wdown;
   return hipSuccess;
 }
 
@@ -168,12 +169,10 @@ hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w,
   return hipSuccess;
 }
 
-hipError_t launch_combine_ec(const float* o, const float* o_lo, const int32_t* idx,
-                             const float* score, int T, int d, int E, int C, float* y,
-                             hipStream_t) {
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
+                             int E, int C, float* y, hipStream_t) {
   ++g_launches;
   inside(o, (size_t)E * C * d * 4, "combine o");
-  inside(o_lo, (size_t)E * C * d * 4, "combine o residual");
   inside(idx, (size_t)E * C * 4, "combine idx");
   inside(score, (size_t)E * C * 4, "combine scores");
   (void)T, (void)y;

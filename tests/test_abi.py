@@ -171,6 +171,12 @@ def test_workspace_offsets_are_inside(M):
         sf = M.make_shape(1000, 256, f, 8, 2)
         end_o = M.workspace_offset(sf, M.WS_O) + R * d * 4
         assert (M.workspace_size(sf) >= end_o + sk) == with_sk, f
+    # bf16 expert choice: h holds 2R rows (h, then its bf16 residual), o R rows (each row's
+    # two products summed in the down projection's epilogue), and no stream-K region
+    se = M.make_shape(1000, 256, 8192, 8, 1, mode="ec", capacity_factor=1.0)
+    Re = 8 * 125
+    assert M.workspace_offset(se, M.WS_O) - M.workspace_offset(se, M.WS_H) >= 2 * Re * 8192 * 2
+    assert M.workspace_size(se) - M.workspace_offset(se, M.WS_O) < Re * d * 4 + 4096
     with pytest.raises(M.MoEError):
         M.workspace_offset(M.make_shape(1000, 256, 512, 8, 2, mode="ec"), M.WS_POS)
 

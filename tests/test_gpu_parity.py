@@ -194,10 +194,22 @@ def test_expert_choice_shapes(moe, T, E, cf):
 @pytest.mark.parametrize("d,f", [(64, 128), (192, 320)])
 def test_expert_choice_narrow_tiles_bf16(moe, d, f):
     # d_model 64 / 192: the down projection's 256 x 64 column tiles, which also
-    # run the residual rows of h as groups of their own; d_ff 320 takes the 256 x 128
-    # gate/up tiles
+    # pair each row of h with its residual row (C = 175: a partial second tile of 47
+    # tokens per expert); d_ff 320 takes the 256 x 128 gate/up tiles
     run_ec_case(moe, W.custom(f"ec_d{d}_f{f}", T=700, d=d, f=f, E=6, mode="ec", cf=1.5, k=1,
                               bias_std=0.5, seed=(42, 320 + d)))
+
+
+def test_expert_choice_long_k_bf16(moe):
+    # d_ff 8192: 256 K stages per down tile, the length from which a token-choice layer
+    # splits its last round of tiles along K; the paired expert-choice tiles stay whole
+    # (the workspace holds no stream-K slots for them)
+    w = W.custom("ec_f8192", T=640, d=256, f=8192, E=4, mode="ec", cf=1.0, k=1, bias_std=0.5,
+                 seed=(42, 350))
+    out, _ = run_ec_case(moe, w)
+    R, d = w.E * w.capacity, w.d
+    shape = out["shape"]
+    assert moe.workspace_size(shape) - moe.workspace_offset(shape, moe.WS_O) < R * d * 4 + 4096
 
 
 def test_expert_choice_fp32_bias_ragged(moe):
