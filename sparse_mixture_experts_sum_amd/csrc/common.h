@@ -35,32 +35,33 @@ __device__ __forceinline__ float warp_max(float v) {
   return v;
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x a multiple of 64, at
-// most 1024). `sh` must hold 17 ints. Returns the exclusive prefix; *total gets the
-// sum over the block. All threads must call it.
-__device__ inline int block_exclusive_scan(int v, int* sh, int* total) {
+// Block-wide exclusive scan of one integer (int or long long) per thread (blockDim.x a
+// multiple of 64, at most 1024). `sh` must hold 17 of them. Returns the exclusive prefix;
+// *total gets the sum over the block. All threads must call it.
+template <class V>
+__device__ inline V block_exclusive_scan(V v, V* sh, V* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
+  V incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int u = __shfl_up(incl, o);
+    V u = __shfl_up(incl, o);
     if (lane >= o) incl += u;
   }
   if (lane == 63) sh[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    int s = lane < nw ? sh[lane] : 0;
-    int si = s;
+    V s = lane < nw ? sh[lane] : 0;
+    V si = s;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
-      int u = __shfl_up(si, o);
+      V u = __shfl_up(si, o);
       if (lane >= o) si += u;
     }
     if (lane < nw) sh[lane] = si - s;  // exclusive base of each wave
     if (lane == nw - 1) sh[16] = si;   // block total
   }
   __syncthreads();
-  const int base = sh[wid];
+  const V base = sh[wid];
   *total = sh[16];
   __syncthreads();  // sh may be reused by the caller right after
   return base + incl - v;

@@ -504,29 +504,36 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a, int ec) {
 //   select (4 x 8 bits of the key, most significant first); then a stable compaction in
 //   token order: every key above the threshold plus the first (C - above) keys equal to
 //   it.
-// The column is read from HBM once, into LDS (INLDS, T <= kEcLdsTokens); every pass
-// after that reads LDS. Each wave counts into its own histogram (the logits of one
+// Each thread owns a contiguous run of ceil(T / 1024) tokens and reads their logits from
+// HBM once, into registers (PER > 0 of them: T <= 1024 PER), which every pass after that
+// reuses. Up to 32768 tokens (PER < 0) the column is staged in LDS instead, thread-major
+// (a thread's j-th token at j * 1024 + thread), so that a pass's reads are consecutive
+// across lanes; longer columns read HBM in every pass (PER = 0). (Staged token-major, the
+// reads of a thread's consecutive tokens hit the same LDS banks many times over: 1.3-2.6 us
+// per pass at 8192 tokens.) Each wave counts into its own histogram (the logits of one
 // expert share their leading key bits, so one shared histogram would take thousands of
 // same-address atomics), and wave 0 finds the bucket holding the C-th key with a prefix
 // sum across its lanes.
 // ---------------------------------------------------------------------------------
 constexpr int kEcThreads = 1024;
 constexpr int kEcWaves = kEcThreads / 64;
-constexpr int kEcLdsTokens = 32768;
 constexpr int kEcCand = kEcThreads;  // keys of the selected value bucket ranked directly
+constexpr int kEcLdsTokens = 32768;
 
-template <bool INLDS>
+template <int PER>
 __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __restrict__ logitsT,
                                                                int T, int E, int C, int32_t* idx,
                                                                float* score, float* probs,
                                                                int32_t* offsets, int32_t* counts,
                                                                int32_t* src,
                                                                int32_t* sk_flags) {
+  constexpr bool INLDS = PER < 0;
   __shared__ float colsh[INLDS ? kEcLdsTokens : 1];
   __shared__ int whist[kEcWaves][256];
   __shared__ float redf[kEcWaves];
-  __shared__ int scan_sh[17];
+  __shared__ long long scan_sh[17];
   __shared__ float redlo[kEcWaves];
+  __shared__ float redsum[kEcWaves];
   __shared__ int sel_digit, sel_need, sel_cnt;
   __shared__ uint32_t cand_key[kEcCand];
   __shared__ int cand_above[kEcCand];
@@ -536,30 +543,67 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   const float* col = logitsT + (size_t)e * T;
   if (sk_flags && e == 0)
     for (int i = tid; i < kStreamKSlots; i += kEcThreads) sk_flags[i] = 0;
-  if constexpr (INLDS) {
-    for (int t = tid; t < T; t += kEcThreads) colsh[t] = col[t];
-    __syncthreads();
-  }
-  auto logit = [&](int t) -> float {
-    if constexpr (INLDS) return colsh[t];
-    else return col[t];
-  };
 
   // contiguous token range of this thread
   const int per = (T + kEcThreads - 1) / kEcThreads;
   const int tb = min(T, tid * per), te = min(T, tb + per);
+  const int nt = te - tb;
+  float lv[PER > 0 ? PER : 1];
+  if constexpr (PER > 0) {
+    if (nt == PER && (reinterpret_cast<uintptr_t>(col + tb) & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < PER; j += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(col + tb + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lv[j + i] = v[i];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) lv[j] = j < nt ? col[tb + j] : 0.f;
+    }
+  }
+  if constexpr (INLDS) {
+    for (int t = tid; t < T; t += kEcThreads) {
+      const int owner = t / per;
+      colsh[(t - owner * per) * kEcThreads + owner] = col[t];
+    }
+    __syncthreads();
+  }
+  // f(t, logit) over this thread's tokens, in token order
+  auto each = [&](auto&& f) {
+    if constexpr (PER > 0) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (j < nt) f(tb + j, lv[j]);
+    } else if constexpr (INLDS) {
+      for (int j = 0; j < nt; ++j) f(tb + j, colsh[j * kEcThreads + tid]);
+    } else {
+      for (int t = tb; t < te; ++t) f(t, col[t]);
+    }
+  };
 
+  // column max, min and softmax sum in one pass and one barrier: each thread sums
+  // exp(l - its own max), each wave rescales its lanes' sums to the wave max, and the
+  // wave sums are rescaled to the column max in wave order (a fixed order)
   float m = -FLT_MAX, lo = FLT_MAX;
-  for (int t = tb; t < te; ++t) {
-    const float l = logit(t);
+  each([&](int, float l) {
     m = fmaxf(m, l);
     lo = fminf(lo, l);
+  });
+  float s = 0.f;
+  each([&](int, float l) { s += expf(l - m); });
+  {
+    const float mw = warp_max(m);
+    s *= expf(m - mw);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
+    m = mw;
   }
-  m = warp_max(m);
   lo = -warp_max(-lo);
   if (lane == 0) {
     redf[wid] = m;
     redlo[wid] = lo;
+    redsum[wid] = s;
   }
   __syncthreads();
   m = redf[0];
@@ -568,15 +612,8 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
     m = fmaxf(m, redf[i]);
     lo = fminf(lo, redlo[i]);
   }
-  __syncthreads();
-  float s = 0.f;
-  for (int t = tb; t < te; ++t) s += expf(logit(t) - m);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o);
-  if (lane == 0) redf[wid] = s;
-  __syncthreads();
   float sum = 0.f;
-  for (int i = 0; i < kEcWaves; ++i) sum += redf[i];
+  for (int i = 0; i < kEcWaves; ++i) sum += redsum[i] * expf(redf[i] - m);
 
   // The C-th largest key (float_key order), `thr`, and how many keys equal to it are taken,
   // `need`. Histograms count keys per bucket in per-wave LDS arrays; wave 0 then walks the
@@ -627,7 +664,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
     auto bucket = [&](float l) { return (int)fminf(fmaxf((l - lo) * scale, 0.f), 255.f); };
     for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int t = tb; t < te; ++t) atomicAdd(&whist[wid][bucket(logit(t))], 1);
+    each([&](int, float l) { atomicAdd(&whist[wid][bucket(l)], 1); });
     __syncthreads();
     find_bucket(need);
     const int sb = sel_digit, sneed = sel_need, scnt = sel_cnt;
@@ -637,13 +674,12 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
         cand_sel = INT_MAX;
       }
       __syncthreads();
-      for (int t = tb; t < te; ++t) {
-        const float l = logit(t);
+      each([&](int, float l) {
         if (bucket(l) == sb) {
           const int slot = atomicAdd(&cand_n, 1);
           if (slot < kEcCand) cand_key[slot] = float_key(l);  // (the count is scnt)
         }
-      }
+      });
       __syncthreads();
       const int n = min(cand_n, kEcCand);
       if (tid < n) {
@@ -671,10 +707,10 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   for (int shift = 24; shift >= 0 && !found; shift -= 8) {
     for (int i = lane; i < 256; i += 64) whist[wid][i] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int t = tb; t < te; ++t) {
-      const uint32_t key = float_key(logit(t));
+    each([&](int, float l) {
+      const uint32_t key = float_key(l);
       if ((key & mask) == prefix) atomicAdd(&whist[wid][(key >> shift) & 255u], 1);
-    }
+    });
     __syncthreads();
     find_bucket(need);
     prefix |= (uint32_t)sel_digit << shift;
@@ -684,24 +720,22 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   }
   const uint32_t thr = prefix;  // key of the C-th largest logit
   // `need` = how many keys equal to thr are taken (lowest token indices first)
-  int neq = 0;
-  for (int t = tb; t < te; ++t) neq += float_key(logit(t)) == thr;
-  int tot;
-  int eq_base = block_exclusive_scan(neq, scan_sh, &tot);
-  int ntake = 0;
+  // keys above thr and equal to it before this thread (one scan of both counts): every
+  // key above is taken, and the first `need` equal ones
+  int nabove = 0, neq = 0;
+  each([&](int, float l) {
+    const uint32_t key = float_key(l);
+    nabove += key > thr;
+    neq += key == thr;
+  });
+  long long tot;
+  const long long base2 =
+      block_exclusive_scan<long long>(((long long)nabove << 32) + neq, scan_sh, &tot);
+  const int eq_base = (int)(base2 & 0xffffffffll);
+  int out = (int)(base2 >> 32) + min(eq_base, need);
   {
     int eqr = eq_base;
-    for (int t = tb; t < te; ++t) {
-      const uint32_t key = float_key(logit(t));
-      if (key > thr) ++ntake;
-      else if (key == thr) ntake += (eqr++ < need);
-    }
-  }
-  int out = block_exclusive_scan(ntake, scan_sh, &tot);
-  {
-    int eqr = eq_base;
-    for (int t = tb; t < te; ++t) {
-      const float l = logit(t);
+    each([&](int t, float l) {
       const uint32_t key = float_key(l);
       bool take = false;
       if (key > thr) take = true;
@@ -714,7 +748,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
         ++out;
       }
       if (probs) probs[(size_t)t * E + e] = sc;
-    }
+    });
   }
   if (tid == 0) {
     offsets[e] = e * C;
@@ -761,11 +795,17 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, int32_t* src,
                             int32_t* sk_flags, hipStream_t s) {
-  if (T <= kEcLdsTokens)
-    ec_select_kernel<true><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                    counts, src, sk_flags);
+  if (T <= 8 * kEcThreads)
+    ec_select_kernel<8><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                 counts, src, sk_flags);
+  else if (T <= 16 * kEcThreads)
+    ec_select_kernel<16><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                  counts, src, sk_flags);
+  else if (T <= kEcLdsTokens)
+    ec_select_kernel<-1><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                  counts, src, sk_flags);
   else
-    ec_select_kernel<false><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                     counts, src, sk_flags);
+    ec_select_kernel<0><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
+                                                 counts, src, sk_flags);
   return hipGetLastError();
 }

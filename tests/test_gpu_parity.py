@@ -217,11 +217,13 @@ def test_expert_choice_fp32_bias_ragged(moe):
                               cf=2.0, k=1, x_std=0.5, wg_std=0.2, bias_std=1.0, seed=(42, 330)))
 
 
-def test_expert_choice_long_column(moe):
-    # T = 40000 > 32768: the select kernel reads each logit column from HBM in every pass
-    # instead of staging it in LDS
-    run_ec_case(moe, W.custom("ec_T40000", T=40000, d=64, f=64, E=4, mode="ec", cf=1.0, k=1,
-                              bias_std=0.3, seed=(42, 340)))
+@pytest.mark.parametrize("T", [12000, 20000, 40000])
+def test_expert_choice_long_column(moe, T):
+    # the select kernel holds up to 8 logits per thread in registers (T <= 8192, the other
+    # tests), up to 16 (T = 12000), stages columns of up to 32768 in LDS (T = 20000), and
+    # reads longer ones from HBM in every pass (T = 40000)
+    run_ec_case(moe, W.custom(f"ec_T{T}", T=T, d=64, f=64, E=4, mode="ec", cf=1.0, k=1,
+                              bias_std=0.3, seed=(42, 340 if T == 40000 else 341 + T % 7)))
 
 
 def test_expert_choice_boundary_ties_in_one_value_bucket(moe):
