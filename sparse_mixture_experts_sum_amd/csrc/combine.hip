@@ -105,7 +105,12 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
   const uint64_t found = __ballot(row >= 0);
   const int nch = d / 4;
   float* yr = y + (size_t)t * d;
-  for (int c = lane; c < nch; c += 64) {
+  // every lane runs every round (chunks c0 + lane, the lanes past the row's end idle), so
+  // that the shuffles read their source lanes while those are active: a shuffle from a
+  // lane outside the exec mask reads nothing (d_model < 256 leaves lanes d_model / 4 and
+  // up without a chunk, and expert e's row and score sit in lane e)
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     uint64_t m = found;
     while (m) {
@@ -113,11 +118,13 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
       m &= m - 1;
       const int r = __shfl(row, e);
       const float s = __shfl(sc, e);
-      const f32x4 v =
-          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c));
-      acc += s * v;
+      if (c < nch) {
+        const f32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(o + (size_t)r * d + 4 * c));
+        acc += s * v;
+      }
     }
-    __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * c));
+    if (c < nch) __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(yr + 4 * c));
   }
 }
 

@@ -212,6 +212,15 @@ def test_expert_choice_long_k_bf16(moe):
     assert moe.workspace_size(shape) - moe.workspace_offset(shape, moe.WS_O) < R * d * 4 + 4096
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_expert_choice_more_experts_than_row_chunks(moe, dtype):
+    # d_model 64: a token's output row is 16 chunks of 4 floats, so the combine's lanes 16
+    # and up hold no chunk, while expert e's row and score sit in lane e (E = 40): every
+    # expert's rows must still reach y
+    run_ec_case(moe, W.custom(f"ec_E40_d64_{dtype}", dtype=dtype, T=900, d=64, f=128, E=40,
+                              mode="ec", cf=1.0, k=1, bias_std=0.5, seed=(42, 360)))
+
+
 def test_expert_choice_fp32_bias_ragged(moe):
     run_ec_case(moe, W.custom("ec_fp32", dtype="fp32", T=333, d=128, f=192, E=5, mode="ec",
                               cf=2.0, k=1, x_std=0.5, wg_std=0.2, bias_std=1.0, seed=(42, 330)))
