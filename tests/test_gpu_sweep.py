@@ -53,3 +53,95 @@ def test_random_shape(moe, c):
         run_capacity_case(moe, w, c["cf"])
     else:
         run_ec_case(moe, w)
+
+
+# ---- a second sweep: training noise, routing-only calls and larger layers ------------------
+
+def _cases2(n: int = 24, seed: int = 2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("noisy", "route", "big")[i % 3]
+        dtype = "fp32" if rng.random() < 0.3 else "bf16"
+        E = int(rng.integers(2, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(64, 3000))
+        d = 64 * int(rng.integers(1, 17))
+        f = 64 * int(rng.integers(1, 33))
+        mode = ("tc", "tc", "capacity", "ec")[int(rng.integers(0, 4))]
+        while T * k * d * f > 2e9:  # keep the fp64 oracle to about a second
+            T = max(64, T // 2)
+            f = max(64, f // 128 * 64)  # halved, still a multiple of 64
+        c = dict(i=100 + i, kind=kind, mode=mode, dtype=dtype, T=T, d=d, f=f, E=E, k=k,
+                 bias=0.5 if rng.random() < 0.5 else None, cf=float(np.round(rng.uniform(0.5, 2.0), 3)),
+                 wn=bool(rng.random() < 0.5), draw=bool(rng.random() < 0.5))
+        if kind == "noisy" and mode == "ec":
+            c["mode"] = "tc"  # noise is a token-choice feature
+        if c["mode"] == "ec":
+            c["k"] = 1
+            c["cf"] = max(c["cf"], float(np.ceil(E / T * 1000) / 1000))
+        out.append(c)
+    return out
+
+
+CASES2 = _cases2()
+
+
+def _route_case(M, w, c):
+    """moe_route alone: routing, probabilities, statistics and z-loss against the oracle."""
+    from tests.test_gpu_parity import _np, _say
+    import torch
+    from oracle import moe_oracle as O
+    from tests import parity as PR
+    _say(w, "route only", c["mode"])
+    inp = W.make_inputs(w, experts=False)
+    dev = PR.device_inputs(inp, w)
+    mode = {"tc": "tc", "capacity": "tc_capacity", "ec": "ec"}[c["mode"]]
+    out = M.moe_route(dev["x"], dev["Wg"], dev["b"], k=w.k, mode=mode, capacity_factor=c["cf"],
+                      renormalize=w.renormalize, want_z_loss=True)
+    torch.cuda.synchronize()
+    z_ref = O.router_z_loss(O.router_logits(inp["x"], inp["Wg"], inp["b"]))
+    assert abs(float(_np(out["z_loss"])[0]) - z_ref) <= 1e-5 * abs(z_ref)
+    if mode == "ec":
+        idx_r, score_r, S_r, s_r = O.route_ec(inp["x"], inp["Wg"], inp["b"], c["cf"])
+        ref = {"idx": idx_r, "w": score_r, "probs": S_r, "logits": s_r}
+        PR.check_ec_routing(_np(out["idx"]), _np(out["w"]), ref, w.capacity)
+        assert np.all(_np(out["counts"]) == w.capacity)
+        _say("  ok")
+        return
+    idx, probs = _np(out["idx"]), _np(out["probs"])
+    _, _, p_ref, _ = O.route_tc(inp["x"], inp["Wg"], inp["b"], w.k, w.renormalize)
+    np.testing.assert_allclose(probs, p_ref, rtol=0, atol=1e-5 if w.dtype == "bf16" else 1e-6)
+    exempt = PR.check_tc_routing(idx, None if mode == "tc_capacity" else _np(out["w"]), p_ref,
+                                 w.k, w.renormalize)
+    # the statistics from the standalone entry point, on the device's own routing
+    f_ref, pm_ref, loss_ref, c_ref = O.aux_stats(p_ref, idx.astype(np.int64), w.E, w.k)
+    np.testing.assert_array_equal(_np(out["counts"]), c_ref)
+    st = M.moe_aux_loss(out["probs"], out["idx"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(st["counts"]), c_ref)
+    np.testing.assert_allclose(_np(st["f"]), f_ref, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(_np(st["p"]), pm_ref, rtol=1e-5, atol=1e-7)
+    np.testing.assert_allclose(_np(st["loss"])[0], loss_ref, rtol=1e-5)
+    _say(f"  ok: exempt tokens {int(exempt.sum())}")
+
+
+@pytest.mark.parametrize("c", CASES2, ids=lambda c: f"{c['i']}-{c['kind']}-{c['mode']}-{c['dtype']}")
+def test_random_shape_noise_route_big(moe, c):
+    w = W.custom(f"sweep{c['i']}", dtype=c["dtype"], T=c["T"], d=c["d"], f=c["f"], E=c["E"],
+                 k=c["k"], mode="ec" if c["mode"] == "ec" else "tc", cf=c["cf"],
+                 bias_std=c["bias"], seed=(42, 900 + c["i"]))
+    if c["kind"] == "noisy":
+        from tests.test_gpu_noise import run_noisy_case
+        nz = W.make_noise(w, wn_std=0.02 if c["wn"] else None, eps_scale=1.0)
+        draw = (1000 + c["i"], 7 * c["i"], 1.0) if c["draw"] else None
+        mode = "tc_capacity" if c["mode"] == "capacity" else "tc"
+        run_noisy_case(moe, w, nz, mode=mode, cf=c["cf"], draw=draw)
+    elif c["kind"] == "route":
+        _route_case(moe, w, c)
+    elif c["mode"] == "tc":
+        run_tc_case(moe, w)
+    elif c["mode"] == "capacity":
+        run_capacity_case(moe, w, c["cf"])
+    else:
+        run_ec_case(moe, w)
