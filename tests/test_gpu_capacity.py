@@ -41,8 +41,9 @@ def _ws_i32(M, out, which, n):
     return _np(out["workspace"][off:off + 4 * n].view(torch.int32))
 
 
-def run_capacity_case(M, w: W.Workload, cf: float, inp=None, sample=None):
-    """Returns (device outputs, kept mask the oracle derives from the device's top-k)."""
+def run_capacity_case(M, w: W.Workload, cf: float, inp=None, sample=None, hidden_fallback=False):
+    """Returns (device outputs, kept mask the oracle derives from the device's top-k).
+    hidden_fallback: see parity.check_y."""
     _say(w, "cf", cf)
     if inp is None:
         inp = W.make_inputs(w)
@@ -98,7 +99,9 @@ def run_capacity_case(M, w: W.Workload, cf: float, inp=None, sample=None):
         toks = np.sort(np.random.default_rng(7).choice(T, size=sample, replace=False))
     y_ref = O.mix(inp["x"][toks], idx64[toks], w_use[toks], inp["Wgate"], inp["Wup"], inp["Wdown"])
     y = _np(out["y"])
-    err = PR.check_y(y[toks], y_ref, w.dtype) if T else 0.0
+    hid = (lambda: PR.mix_hidden_bf16(inp["x"][toks], idx64[toks], w_use[toks], inp["Wgate"],
+                                      inp["Wup"], inp["Wdown"])) if hidden_fallback else None
+    err = PR.check_y(y[toks], y_ref, w.dtype, hidden_ref=hid) if T else 0.0
     if not exempt.any() and sample is None and 0 < T <= 4096:
         ref = O.forward_tc_capacity(inp["x"], inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"],
                                     inp["Wdown"], k, cf, w.renormalize)

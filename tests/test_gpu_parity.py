@@ -33,11 +33,11 @@ def _np(t):
     return None if t is None else t.detach().cpu().numpy()
 
 
-def run_tc_case(M, w: W.Workload, inp=None, check_stats=True, sample=None):
+def run_tc_case(M, w: W.Workload, inp=None, check_stats=True, sample=None, hidden_fallback=False):
     """Run the token-choice layer on the device and check it against the oracle.
 
     sample: if given, the number of tokens whose output the oracle evaluates
-    (routing is still checked on every token)."""
+    (routing is still checked on every token). hidden_fallback: see parity.check_y."""
     _say(w)
     if inp is None:
         inp = W.make_inputs(w)
@@ -59,7 +59,9 @@ def run_tc_case(M, w: W.Workload, inp=None, check_stats=True, sample=None):
     if sample is not None and sample < w.T:
         toks = np.sort(np.random.default_rng(7).choice(w.T, size=sample, replace=False))
     y_ref = O.mix(inp["x"][toks], idx_use[toks], w_use[toks], inp["Wgate"], inp["Wup"], inp["Wdown"])
-    err = PR.check_y(y[toks], y_ref, w.dtype)
+    hid = (lambda: PR.mix_hidden_bf16(inp["x"][toks], idx_use[toks], w_use[toks], inp["Wgate"],
+                                      inp["Wup"], inp["Wdown"])) if hidden_fallback else None
+    err = PR.check_y(y[toks], y_ref, w.dtype, hidden_ref=hid)
     if check_stats:
         f_ref, pm_ref, loss_ref, c_ref = O.aux_stats(p_ref, idx_use, w.E, w.k)
         rt = 1e-5

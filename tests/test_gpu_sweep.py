@@ -3,7 +3,10 @@ dtypes), against the fp64 oracle: the fixed cases elsewhere pin the five workloa
 edge cases, this sweep covers combinations nobody picked (odd token counts, expert counts that
 are not powers of two, d_model / d_ff at every multiple of 64 up to 512 / 1024, bias on or off).
 
-The case list is drawn once from a fixed seed, so every run checks the same cases.
+The case list is drawn once from a fixed seed, so every run checks the same cases. Token-choice
+outputs in bf16 are held to the 2e-2 bar, or, where a single bf16 rounding of the hidden
+activation alone misses it (long-tailed outputs at small d_model), to within 10% of that
+rounding's own error (parity.check_y).
 """
 from __future__ import annotations
 
@@ -48,9 +51,9 @@ def test_random_shape(moe, c):
                  k=c["k"], mode="ec" if c["mode"] == "ec" else "tc", cf=c["cf"],
                  bias_std=c["bias"], seed=(42, 900 + c["i"]))
     if c["mode"] == "tc":
-        run_tc_case(moe, w)
+        run_tc_case(moe, w, hidden_fallback=True)
     elif c["mode"] == "capacity":
-        run_capacity_case(moe, w, c["cf"])
+        run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
     else:
         run_ec_case(moe, w)
 
@@ -140,8 +143,49 @@ def test_random_shape_noise_route_big(moe, c):
     elif c["kind"] == "route":
         _route_case(moe, w, c)
     elif c["mode"] == "tc":
-        run_tc_case(moe, w)
+        run_tc_case(moe, w, hidden_fallback=True)
     elif c["mode"] == "capacity":
-        run_capacity_case(moe, w, c["cf"])
+        run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
+    else:
+        run_ec_case(moe, w)
+
+
+# ---- a third sweep: token counts at the edges (a handful of tokens, block boundaries, and
+# batches past the one-launch dispatch and the register-held expert-choice columns) ---------
+
+def _cases3(n: int = 16, seed: int = 2028):
+    rng = np.random.default_rng(seed)
+    Ts = [1, 2, 3, 63, 64, 65, 127, 129, 16385, 20000, 32767, 32769, 40000, 47000, 5, 1000]
+    out = []
+    for i in range(n):
+        T = Ts[i]
+        mode = ("tc", "capacity", "ec", "tc")[i % 4]
+        dtype = "fp32" if rng.random() < 0.25 else "bf16"
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        cf = float(np.round(rng.uniform(0.3, 2.0), 3))
+        if mode == "ec":
+            k = 1
+            cf = max(cf, float(np.ceil(E / T * 1000) / 1000))
+            if np.floor(T * cf / E) > T:
+                cf = float(E)
+        out.append(dict(i=200 + i, mode=mode, dtype=dtype, T=T, d=64 * int(rng.integers(1, 3)),
+                        f=64 * int(rng.integers(1, 3)), E=E, k=k, cf=cf,
+                        bias=0.5 if rng.random() < 0.5 else None))
+    return out
+
+
+CASES3 = _cases3()
+
+
+@pytest.mark.parametrize("c", CASES3, ids=lambda c: f"{c['i']}-T{c['T']}-{c['mode']}-{c['dtype']}")
+def test_random_token_counts(moe, c):
+    w = W.custom(f"sweep{c['i']}", dtype=c["dtype"], T=c["T"], d=c["d"], f=c["f"], E=c["E"],
+                 k=c["k"], mode="ec" if c["mode"] == "ec" else "tc", cf=c["cf"],
+                 bias_std=c["bias"], seed=(42, 900 + c["i"]))
+    if c["mode"] == "tc":
+        run_tc_case(moe, w, hidden_fallback=True)
+    elif c["mode"] == "capacity":
+        run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
     else:
         run_ec_case(moe, w)
