@@ -49,9 +49,8 @@
  * 0 <= T and T * max(k, 1) < 2^31; expert choice needs 1 <= C <= T and E * C < 2^31
  * (outside these: MOE_ERR_BAD_SHAPE). Limits of this implementation, not of the method,
  * return MOE_ERR_UNSUPPORTED: E > 64, k > 8, d_model or d_ff not a multiple of 64 (the
- * kernels run whole 64-column tiles), fp32 layers with more than 64 * (65535 - E)
- * routed rows (T * k, or E * C), and bf16 expert choice with 2 * E * C >= 2^31 (the
- * residual rows of h, below). x, weights, y and the workspace must be 16-byte aligned.
+ * kernels run whole 64-column tiles), and fp32 layers with more than 64 * (65535 - E)
+ * routed rows (T * k, or E * C). x, weights, y and the workspace must be 16-byte aligned.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -78,10 +78,6 @@ moe_status check_shape(const moe_shape* s) {
     const int64_t C = ec_capacity(*s);
     if (C < 1 || C > s->T) return MOE_ERR_BAD_SHAPE;
     if (C * (int64_t)s->E >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
-    // bf16 carries h's rounding residual as E * C more rows of h, addressed by int32 row
-    // indices too
-    if (s->dtype == MOE_BF16 && 2 * C * (int64_t)s->E >= (int64_t(1) << 31))
-      return MOE_ERR_UNSUPPORTED;
   }
   // the fp32 GEMMs launch one grid row per 64 routed rows (plus one per group): the grid's
   // y extent bounds the rows they take

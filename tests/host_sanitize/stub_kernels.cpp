@@ -150,7 +150,7 @@ hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const in
   ++g_launches;
   const size_t eb = bf16 ? 2 : 4;
   // with residual rows the h rows run to R_max + lo_rows
-  inside(h, (size_t)(R_max + lo_rows) * f * eb, "down h");
+  inside(h, ((size_t)R_max + (size_t)lo_rows) * f * eb, "down h");
   inside(offsets, (size_t)(E + 1) * 4, "down offsets");
   inside(o, (size_t)R_max * d * 4, "down o");
   inside(sk.partial, kStreamKSlots * kStreamKSlotBytes, "stream-K partials");

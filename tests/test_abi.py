@@ -141,6 +141,18 @@ def test_token_choice_capacity_host_checks(M):
         M.make_shape(64, 64, 64, 8, 2, mode="capacity")
 
 
+def test_expert_choice_bf16_near_the_row_limit_is_sized(M):
+    # bf16 expert choice carries h's residual as E * C more rows; only E * C itself must stay
+    # below 2^31 (the residual rows are addressed from their own base, not by row index)
+    T = (1 << 31) - 2
+    s = M.make_shape(T, 64, 64, 2, 1, mode="ec", capacity_factor=1.0)
+    R = 2 * (T // 2)
+    assert M.workspace_size(s) >= 2 * R * 64 * 2 + R * 64 * 4  # h and its residual, o
+    with pytest.raises(M.MoEError) as ei:  # C = T = 2^30 + 2, E * C = 2^31 + 4: out of range
+        M.workspace_size(M.make_shape((1 << 30) + 2, 64, 64, 2, 1, mode="ec", capacity_factor=2.0))
+    assert ei.value.status == 2
+
+
 def test_workspace_offsets_are_inside(M):
     for mode in ("tc", "ec"):
         s = M.make_shape(1000, 256, 512, 8, 2, mode=mode)
