@@ -189,19 +189,33 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 }
 
 // The in-kernel normal draw n(t, e): Philox4x32-10 of counter (t, e / 4, offset) under key
-// seed gives four words r_0..r_3; u_i = (r_i / 256 (integer part) + 1/2) / 2^24, exact in
-// fp32 and strictly inside (0, 1); the Box-Muller transform (Box and Muller, 1958) of the
-// pair (u_0, u_1) gives experts 4q and 4q + 1 (cosine, sine), of (u_2, u_3) experts 4q + 2
-// and 4q + 3.
+// seed gives four words r_0..r_3; u_i = (j_i + 1/2) / 2^24 with j_i = r_i / 256 (integer
+// part), strictly inside (0, 1); the Box-Muller transform (Box and Muller, 1958) of the pair
+// (u_0, u_1), sqrt(-2 ln u_0) times cos or sin of 2 pi u_1, gives experts 4q and 4q + 1
+// (cosine, sine), of (u_2, u_3) experts 4q + 2 and 4q + 3.
+// u_i takes 25 significant bits once j_i >= 2^23, so it is not an fp32 value there; its
+// complement 1 - u_i = (2^24 - j_i - 1/2) / 2^24 is, and so ln u_0 = log1p(-(1 - u_0)) is
+// evaluated from it, and the angle through cos(pi (2 - a)) = cos(pi a), sin(pi (2 - a)) =
+// -sin(pi a) with 2 - a = 2 (1 - u_1) half turns. Every argument is then exact, and the
+// draw differs from its definition only by the fp32 math functions' own rounding.
 __device__ __forceinline__ float noise_draw(const RouterArgs& a, int t, int e) {
   const u32x4 r = philox4x32_10(u32x4{(uint32_t)t, (uint32_t)(e >> 2), a.off_lo, a.off_hi},
                                 a.seed_lo, a.seed_hi);
   const int h = (e >> 1) & 1;
-  const uint32_t r0 = h ? r[2] : r[0], r1 = h ? r[3] : r[1];
-  const float u0 = ((float)(r0 >> 8) + 0.5f) * 0x1p-24f;
-  const float u1 = ((float)(r1 >> 8) + 0.5f) * 0x1p-24f;
-  const float rad = sqrtf(-2.0f * logf(u0));
-  return rad * ((e & 1) ? sinpif(2.0f * u1) : cospif(2.0f * u1));
+  const uint32_t j0 = (h ? r[2] : r[0]) >> 8, j1 = (h ? r[3] : r[1]) >> 8;
+  constexpr uint32_t kHalf = 1u << 23;
+  // exact: (j + 1/2) below 2^23, (2^24 - j - 1/2) from 2^23 on, both at most 24 bits
+  const float lnu0 = j0 < kHalf ? logf(((float)j0 + 0.5f) * 0x1p-24f)
+                                : log1pf(-(((float)((1u << 24) - j0) - 0.5f) * 0x1p-24f));
+  const bool up = j1 >= kHalf;
+  const float turns = up ? ((float)((1u << 24) - j1) - 0.5f) * 0x1p-23f  // 2 - 2 u_1
+                         : ((float)j1 + 0.5f) * 0x1p-23f;                // 2 u_1
+  const float rad = sqrtf(-2.0f * lnu0);
+  if (e & 1) {
+    const float sv = sinpif(turns);
+    return rad * (up ? -sv : sv);
+  }
+  return rad * cospif(turns);
 }
 
 // NOISE: 0 none, 1 eps added to the logits, 2 softplus(x W_noise) * eps added; eps from

@@ -105,7 +105,7 @@ def run_capacity_case(M, w: W.Workload, cf: float, inp=None, sample=None, hidden
     if not exempt.any() and sample is None and 0 < T <= 4096:
         ref = O.forward_tc_capacity(inp["x"], inp["Wg"], inp["b"], inp["Wgate"], inp["Wup"],
                                     inp["Wdown"], k, cf, w.renormalize)
-        PR.check_y(y, ref["y"], w.dtype)
+        PR.check_y(y, ref["y"], w.dtype, hidden_ref=hid)
     # statistics before any drop
     f_ref, pm_ref, loss_ref, _ = O.aux_stats(p_ref, idx64, E, k)
     np.testing.assert_allclose(_np(out["f"]), f_ref, rtol=1e-6, atol=0)

@@ -42,10 +42,10 @@ def _dev_noise(nz, w):
             PR.to_dev(nz["eps"], torch.float32))
 
 
-def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0, draw=None):
+def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0, draw=None, hidden_fallback=False):
     """nz: the noise inputs (W_noise, eps). draw = (seed, offset, scale): the router
     kernel draws eps instead, and the oracle takes its fp64 evaluation of the same
-    definition (nz["eps"] is replaced)."""
+    definition (nz["eps"] is replaced). hidden_fallback: see parity.check_y."""
     _say(w, "noise", "softplus" if nz["Wn"] is not None else "additive", mode,
          "drawn in the kernel %r" % (draw,) if draw else "eps passed")
     inp = W.make_inputs(w)
@@ -77,7 +77,9 @@ def run_noisy_case(M, w, nz, sample=None, mode="tc", cf=1.0, draw=None):
     if sample is not None and sample < w.T:
         toks = np.sort(np.random.default_rng(7).choice(w.T, size=sample, replace=False))
     y_ref = O.mix(inp["x"][toks], idx64[toks], w_use[toks], inp["Wgate"], inp["Wup"], inp["Wdown"])
-    err = PR.check_y(_np(out["y"])[toks], y_ref, w.dtype)
+    hid = (lambda: PR.mix_hidden_bf16(inp["x"][toks], idx64[toks], w_use[toks], inp["Wgate"],
+                                      inp["Wup"], inp["Wdown"])) if hidden_fallback else None
+    err = PR.check_y(_np(out["y"])[toks], y_ref, w.dtype, hidden_ref=hid)
     f_ref, pm_ref, loss_ref, _ = O.aux_stats(p_ref, idx64, w.E, w.k)
     np.testing.assert_allclose(_np(out["f"]), f_ref, rtol=1e-6, atol=0)
     np.testing.assert_allclose(_np(out["p"]), pm_ref, rtol=1e-5, atol=1e-7)
@@ -219,6 +221,30 @@ def test_drawn_noise_seen_through_probs(moe, E):
     # the logits' spread is that of N(0, 1) draws: the largest probability of a token
     # reaches well above uniform for most tokens
     assert np.median(p_ref.max(axis=1)) > 2.0 / E
+
+
+def test_drawn_noise_matches_its_definition_to_fp32_rounding(moe):
+    # The same setting as above, read back sharper: with W_g = 0 the logits are the draw, so
+    # ln p_e differs from eps_e by one constant per token; what is left after removing it is
+    # the draw's own error (plus about 2.4e-7 from the fp32 probabilities). Half of the u
+    # values need 25 significant bits ((j + 1/2) / 2^24 with j >= 2^23) and are not fp32
+    # numbers; computing ln u or the angle from such a rounded u is off by up to 7e-6 near
+    # u = 1 on this draw, far outside the bound, which allows a few fp32 roundings of |eps|.
+    T, d, E = 4097, 64, 64
+    seed, offset = (0xA5A5 << 32) | 0x1234, (7 << 32) | 99
+    _say("drawn noise against its definition", T, E)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(T, d, device="cuda", generator=g).to(torch.bfloat16)
+    Wg = torch.zeros(d, E, device="cuda", dtype=torch.bfloat16)
+    r = moe.moe_route(x, Wg, None, k=2, eps=moe.NoiseDraw(seed, offset, 1.0))
+    torch.cuda.synchronize()
+    eps_ref = O.noise_draw(T, E, seed, offset)
+    D = np.log(_np(r["probs"]).astype(np.float64)) - eps_ref
+    D -= np.median(D, axis=1, keepdims=True)
+    tol = 5e-7 + 2.0 ** -21 * np.abs(eps_ref)
+    bad = np.abs(D) > tol
+    assert not bad.any(), (f"{int(bad.sum())} draws off by up to {np.abs(D).max():.3g}; "
+                           f"worst at {np.unravel_index(np.argmax(np.abs(D) / tol), D.shape)}")
 
 
 def test_drawn_noise_mid_bf16(moe):

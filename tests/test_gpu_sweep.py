@@ -139,7 +139,7 @@ def test_random_shape_noise_route_big(moe, c):
         nz = W.make_noise(w, wn_std=0.02 if c["wn"] else None, eps_scale=1.0)
         draw = (1000 + c["i"], 7 * c["i"], 1.0) if c["draw"] else None
         mode = "tc_capacity" if c["mode"] == "capacity" else "tc"
-        run_noisy_case(moe, w, nz, mode=mode, cf=c["cf"], draw=draw)
+        run_noisy_case(moe, w, nz, mode=mode, cf=c["cf"], draw=draw, hidden_fallback=True)
     elif c["kind"] == "route":
         _route_case(moe, w, c)
     elif c["mode"] == "tc":
