@@ -360,6 +360,25 @@ def test_dispatch_permutation_is_stable_bijection(moe, dtype):
             moe.workspace_offset(shape, moe.WS_XPERM)
 
 
+@pytest.mark.parametrize("mode", ["tc", "tc_capacity", "ec"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_optional_outputs_do_not_change_y(moe, mode, dtype):
+    # routing, probabilities and statistics not requested (NULL pointers through the C ABI:
+    # the library keeps idx and w in its workspace instead): the same y, bit for bit
+    w = W.custom(f"optional_{mode}_{dtype}", dtype=dtype, T=777, d=128, f=192, E=12, k=3 if
+                 mode != "ec" else 1, bias_std=0.5, seed=(42, 370))
+    inp = W.make_inputs(w)
+    dev = PR.device_inputs(inp, w)
+    args = (dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"])
+    kw = dict(k=w.k, mode=mode, capacity_factor=1.25)
+    _say(w, mode, "all outputs, then y alone")
+    full = moe.moe_forward(*args, want_stats=mode != "ec", want_z_loss=True, **kw)
+    bare = moe.moe_forward(*args, want_routing=False, want_probs=False, want_stats=False, **kw)
+    torch.cuda.synchronize()
+    assert bare["idx"] is None and bare["probs"] is None
+    assert torch.equal(full["y"], bare["y"])
+
+
 def test_layer_module_batch_seq_input(moe):
     # the layer object on [batch, seq, d_model] input: the same bits as moe_forward on the
     # flattened tokens, for three calls of different token counts sharing its workspace
