@@ -269,7 +269,7 @@ def main():
                     help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               f"(the layer is benchmarked on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 

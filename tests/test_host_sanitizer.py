@@ -5,7 +5,7 @@ against host-only stand-ins of the kernel launchers (tests/host_sanitize/stub_ke
 which also check that every workspace buffer handed to a launcher fits inside the
 workspace), and driven through every error path and a sweep of about 600k extreme shapes
 (tests/host_sanitize/host_checks.cpp). No GPU, no HIP compiler: the device kernels are not
-part of this build."""
+compiled for this test."""
 import os
 import shutil
 import subprocess
