@@ -189,3 +189,36 @@ def test_random_token_counts(moe, c):
         run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
     else:
         run_ec_case(moe, w)
+
+
+# ---- a fourth sweep: d_ff of 8192 and more, where the down projection splits the K range of
+# its last partial round of tiles across workgroups (stream-K, partial sums in a fixed order)
+
+def _cases4(n: int = 8, seed: int = 2029):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f = 64 * int(rng.integers(128, 257))  # 8192 .. 16384
+        d = 64 * int(rng.integers(1, 9))
+        E = int(rng.integers(1, 17))
+        k = int(rng.integers(1, min(E, 2) + 1))
+        T = int(rng.integers(50, 4000))
+        while T * k * d * f > 2e9:  # keep the fp64 oracle to about a second
+            T = max(50, T // 2)
+        out.append(dict(i=300 + i, T=T, d=d, f=f, E=E, k=k, cap=bool(rng.random() < 0.3),
+                        cf=float(np.round(rng.uniform(0.5, 1.5), 3)),
+                        bias=0.5 if rng.random() < 0.5 else None))
+    return out
+
+
+CASES4 = _cases4()
+
+
+@pytest.mark.parametrize("c", CASES4, ids=lambda c: f"{c['i']}-f{c['f']}-{'cap' if c['cap'] else 'tc'}")
+def test_random_stream_k_shapes(moe, c):
+    w = W.custom(f"sweep{c['i']}", dtype="bf16", T=c["T"], d=c["d"], f=c["f"], E=c["E"], k=c["k"],
+                 bias_std=c["bias"], seed=(42, 900 + c["i"]))
+    if c["cap"]:
+        run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
+    else:
+        run_tc_case(moe, w, hidden_fallback=True)
