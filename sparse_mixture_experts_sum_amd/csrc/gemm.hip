@@ -833,11 +833,11 @@ __device__ __forceinline__ bool next_item(ItemIt& it, const SkPlan& p, int slot,
 }
 
 // A partial slot holds one piece's fp32 accumulators as a row-major [BM, BNL] array. Only the
-// down projection splits tiles: its output is the accumulator itself, so the owner stores its
-// own piece to o like any tile and then adds the other pieces to o in workgroup order
-// (o = head + p1 + p2 + ...), with the accumulators no longer live. (The gate/up GEMM's SwiGLU
-// epilogue would need the sum before it, and a second epilogue path in those kernels costs
-// registers they do not have.)
+// down projection splits tiles: its output is the accumulator itself, so the owner, its own
+// piece still in the accumulators, waits for the other pieces and stores
+// o = head + p1 + p2 + ... in workgroup order, once. (The gate/up GEMM's SwiGLU epilogue would
+// need the sum before it, and a second epilogue path in those kernels costs registers they do
+// not have.)
 //
 // Where the partials travel: a piece and its owner always run on one XCD (their workgroup
 // ids differ by a multiple of 8, and workgroups are dealt round-robin over a partition's 8,
@@ -880,13 +880,17 @@ __device__ __forceinline__ void put_partial(const GemmArgs& a, int bid, int ln, 
     __hip_atomic_store(a.flags + bid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The owner of a split tile, after storing its own piece to o: for each later workgroup w of
-// this XCD whose run covers part of the tile (w = slot + 1 .. w_last) wait for its flag and
-// clear it; then o += p_{slot+1} + p_{slot+2} + ... element by element, in that order, each
-// lane over the elements it stored (store_tile's order, rows of the tile only).
+// The owner of a split tile, with its own piece still in the accumulators: wait for the
+// pieces of the later workgroups of this XCD whose runs cover the rest of the tile
+// (w = slot + 1 .. w_last; thread 0 waits for each flag and clears it), then store
+// o = head + p_{slot+1} + p_{slot+2} + ... element by element, in that order: one store of
+// o and one read of each partial. (Storing the head first and adding the partials to o after
+// it wrote o twice and read it back, 1 MB per tile split in two against 512 KB here; the same
+// additions in the same order, so the same bits.)
 template <class G>
-__device__ __forceinline__ void add_partials(const GemmArgs& a, const TileCoord& t, int xcd,
-                                             int slot, int w_last, int wm, int wn) {
+__device__ __forceinline__ void store_tile_sum(const GemmArgs& a, const TileCoord& t, int xcd,
+                                               int slot, int w_last, int ln, int wm, int wn,
+                                               const f32x16 (&acc)[G::NBW][G::MB]) {
   constexpr int BNL = G::WNL * G::WGN;
   if (threadIdx.x == 0) {
     for (int w = slot + 1; w <= w_last; ++w) {
@@ -898,40 +902,47 @@ __device__ __forceinline__ void add_partials(const GemmArgs& a, const TileCoord&
       __hip_atomic_store(a.flags + wb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  wait_vmcnt<0>();  // this thread's own o stores have completed
   __syncthreads();
-  const int ln = fresh_lane();
   float* o = static_cast<float*>(a.out);
-  // per 32-row block: all 16 of the lane's o chunks, then each partial's 16 chunks, are
-  // loaded before they are added
-  constexpr int NQ = G::NBW * 4;
+  // per 32-row block and quarter of its columns: 8 chunks of each partial are loaded before
+  // they are added (a running sum and one partial in flight: 64 VGPRs)
+  constexpr int NQ = G::NBW * 4, NH = 4, HQ = NQ / NH;
+#pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
     const int m = wm * G::WM + mb * 32 + (ln & 31);
     const bool row_ok = m < t.rows;
     const size_t rowoff = (size_t)(t.row0 + (row_ok ? m : 0)) * a.N + t.n0;
-    f32x4 v[NQ];
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
-      v[i] = row_ok ? *reinterpret_cast<const f32x4*>(o + rowoff + ncol) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int w = slot + 1; w <= w_last; ++w) {
-      const __amdgpu_buffer_rsrc_t r = partial_rsrc(a, w * kXcds + xcd);
-      f32x4 p[NQ];
+    for (int hh = 0; hh < NH; ++hh) {
+      f32x4 v[HQ];
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
-        p[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (m * BNL + ncol) * 4, 0, kCpolSc0);
+      for (int ii = 0; ii < HQ; ++ii) {
+        const int i = hh * HQ + ii, nb = i / 4, q = i % 4;
+        v[ii] = f32x4{acc[nb][mb][4 * q + 0], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2],
+                      acc[nb][mb][4 * q + 3]};
       }
+      for (int w = slot + 1; w <= w_last; ++w) {
+        const __amdgpu_buffer_rsrc_t r = partial_rsrc(a, w * kXcds + xcd);
+        f32x4 p[HQ];
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) v[i] += p[i];
-    }
-    if (row_ok) {
+        for (int ii = 0; ii < HQ; ++ii) {
+          const int i = hh * HQ + ii;
+          const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
+          p[ii] = __builtin_amdgcn_raw_buffer_load_b128(r, (m * BNL + ncol) * 4, 0, kCpolSc0);
+        }
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
-        *reinterpret_cast<f32x4*>(o + rowoff + ncol) = v[i];
+        for (int ii = 0; ii < HQ; ++ii) v[ii] += p[ii];
       }
+      if (row_ok) {
+#pragma unroll
+        for (int ii = 0; ii < HQ; ++ii) {
+          const int i = hh * HQ + ii;
+          const int ncol = wn * G::WNL + (i / 4) * 32 + 8 * (i % 4) + 4 * (ln >> 5);
+          *reinterpret_cast<f32x4*>(o + rowoff + ncol) = v[ii];
+        }
+      }
+      // one batch at a time: keeps the accumulator copies from piling up in VGPRs
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -1017,14 +1028,13 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
     ln = fresh_lane();
     if (SK && cur.role == kPiece) {
       put_partial<G>(a, (int)blockIdx.x, ln, wm, wn, acc);
+    } else if (SK && cur.role == kHead) {
+      // the workgroups whose runs cover the rest of this tile
+      const int u = cur.tile - sp.dp_tiles;
+      store_tile_sum<G>(a, t, (int)blockIdx.x & (kXcds - 1), slot,
+                        ((u + 1) * sp.nkc - 1) / sp.per, ln, wm, wn, acc);
     } else {
       store_tile<G, SWIGLU, SPLIT>(a, t, ln, wm, wn, acc);
-      if (SK && cur.role == kHead) {
-        // the workgroups whose runs cover the rest of this tile
-        const int u = cur.tile - sp.dp_tiles;
-        add_partials<G>(a, t, (int)blockIdx.x & (kXcds - 1), slot,
-                        ((u + 1) * sp.nkc - 1) / sp.per, wm, wn);
-      }
     }
     if (!has_next) break;
     t = tn;
