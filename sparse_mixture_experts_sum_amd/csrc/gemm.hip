@@ -123,6 +123,7 @@ struct Geo {
   static constexpr int SUB = BK / 16;                // 16-deep MFMA substeps per stage
   static constexpr int A_CPR = BK / 8;               // 16-byte chunks per A row
   static constexpr int A_RPI = 1024 / (BK * 2);      // A rows per DMA instruction
+  static constexpr bool GATHERS = SWIGLU;             // A rows may be gathered (gate/up)
   static constexpr int WGN = NW / 2;                 // waves: 2 along M x WGN along N
   static constexpr int WM = BM / 2, WNL = BNL / WGN; // per wave
   static constexpr int MB = WM / 32, NBW = WNL / 32; // 32x32 blocks per wave
@@ -293,8 +294,7 @@ static __device__ __forceinline__ void run(int n_after, bool more_, bool refill_
   constexpr int NM = G::SUB * G::NBW * G::MB;                // MFMAs per stage
   constexpr int NR = G::SUB * G::MB + 2 * G::SUB * G::NBW;   // LDS reads per stage
   constexpr int NG = G::LPS;                                 // groups: one load each
-  static_assert(NM % NG == 0 && NR % NG == 0, "MFMA / read / load groups");
-  constexpr int MPG = NM / NG, RPG = NR / NG;
+  static_assert(NM >= NG && NR >= NG, "MFMA / read / load groups");
   __builtin_amdgcn_sched_barrier(0);
   // own loads of stage kt + 1 (kt + 1 .. kt + S - 1 may be in flight)
   if constexpr (FULL) wait_vmcnt<(S - 2) * G::LPS>();
@@ -305,13 +305,16 @@ static __device__ __forceinline__ void run(int n_after, bool more_, bool refill_
   const bool refill = FULL || refill_;
   const char* src = ring[(J + 1) % S];
   char* const dst = ring[J];
+  // group g: MFMAs [NM g / NG, NM (g + 1) / NG), reads likewise, then one load (equal
+  // groups when the counts divide)
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
 #pragma unroll
-    for (int m = 0; m < MPG; ++m) mfma_frag<G>(g * MPG + m, Fc, acc);
+    for (int m = NM * g / NG; m < NM * (g + 1) / NG; ++m) mfma_frag<G>(m, Fc, acc);
     if (more) {
 #pragma unroll
-      for (int r = 0; r < RPG; ++r) read_frag<G>(g * RPG + r, src, a_frag, b_frag, Fn);
+      for (int r = NR * g / NG; r < NR * (g + 1) / NG; ++r)
+        read_frag<G>(r, src, a_frag, b_frag, Fn);
     }
     if (refill) rl.issue_one(g, rstage, dst);
     __builtin_amdgcn_sched_barrier(0);
@@ -569,7 +572,8 @@ __device__ __forceinline__ void frag_offsets(int ln, int wm, int wn, int (&a_fra
 // use), and each load's lanes take their rows' indices from those lanes (gather_rows).
 template <class G>
 __device__ __forceinline__ int gather_fetch(const GemmArgs& a, const TileCoord& t, int ln, int wave) {
-  static_assert(G::A_PW * G::A_RPI == 64, "a wave's A loads cover 64 rows");
+  // (only the gate/up GEMM gathers; other kernels compile the call on a path never taken)
+  static_assert(!G::GATHERS || G::A_PW * G::A_RPI == 64, "a wave's A loads cover 64 rows");
   return a.gather[t.row0 + min(64 * wave + ln, t.rows - 1)];
 }
 template <class G>
@@ -1065,8 +1069,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // the wave index is uniform: keep it scalar so LDS destinations stay plain offsets
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
-  // one wave per SIMD on 256 x 256 tiles: the software-pipelined loop
-  constexpr bool PIPE = NW == 4 && BM == 256 && BNL == 256;
+  // one wave per SIMD on 256 (or 192) x 256 tiles: the software-pipelined loop
+  constexpr bool PIPE = NW == 4 && (BM == 256 || BM == 192) && BNL == 256;
   // rows of the grouped problem per tile: BM, or BM / 2 tokens in the paired down projection
   constexpr bool PAIRED = !SWIGLU && SPLIT;
   constexpr int TR = PAIRED ? BM / 2 : BM;
@@ -1082,7 +1086,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // (no stream-K in the paired down projection: a piece's partial sums would need the pair
   // sum of the epilogue)
   const GemmArgs args{A, gather, B0, B1, offsets, E, K, N, out, out2,
-                      PIPE && !PAIRED && gridDim.x <= kSkSlots ? partial : nullptr, flags,
+                      PIPE && BM == 256 && !PAIRED && gridDim.x <= kSkSlots ? partial : nullptr,
+                      flags,
                       lo_rows};
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
@@ -1239,10 +1244,23 @@ hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate,
                                                0, sk, s);
 }
 
+// Whether the down projection of up to R_max rows in E groups fits one round of the
+// workgroups in 192-row tiles (at most R_max / 192 + E row tiles). A layer whose 256-row
+// tiles already fit one round, or nearly, then finishes when its slowest tile does, and a
+// 192-row tile is three quarters of the work: the mid-size layer (8192 rows, 8 experts,
+// d_model 1024) runs 140 tiles of 256 rows on 256 CUs, or about 190 of 192.
+bool down_fits_192(long long R_max, int E, int d) {
+  const long long tiles = (R_max / 192 + E) * (long long)(d / 256);
+  return tiles <= ((device_cu_count() + 7) / 8) * 8;
+}
+
 // PAIRED: h's residual rows sit lo_rows rows after their main rows (see store_tile)
 template <bool PAIRED>
-hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int f,
-                     int d, float* o, int lo_rows, const StreamK& sk, hipStream_t s) {
+hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int R_max,
+                     int f, int d, float* o, int lo_rows, const StreamK& sk, hipStream_t s) {
+  if (!PAIRED && d % 256 == 0 && down_fits_192(R_max, E, d))
+    return launch_bf16<192, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+                                                  o, nullptr, 0, sk, s);
   if (d % 256 == 0)
     return launch_bf16<256, 256, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
                                                    o, nullptr, lo_rows, sk, s);
@@ -1275,8 +1293,8 @@ hipError_t launch_gemm_down(int bf16in, const void* h, const void* Wdown, const 
                             int E, int R_max, int f, int d, float* o, int lo_rows,
                             const StreamK& sk, hipStream_t s) {
   if (bf16in) {
-    if (lo_rows > 0) return down_bf16<true>(h, Wdown, offsets, E, f, d, o, lo_rows, sk, s);
-    return down_bf16<false>(h, Wdown, offsets, E, f, d, o, 0, sk, s);
+    if (lo_rows > 0) return down_bf16<true>(h, Wdown, offsets, E, R_max, f, d, o, lo_rows, sk, s);
+    return down_bf16<false>(h, Wdown, offsets, E, R_max, f, d, o, 0, sk, s);
   }
   if (lo_rows > 0) return hipErrorInvalidValue;  // the fp32 path has no residual rows
   dim3 grid(d / 64, R_max / 64 + E);
