@@ -222,3 +222,27 @@ def test_random_stream_k_shapes(moe, c):
         run_capacity_case(moe, w, c["cf"], hidden_fallback=True)
     else:
         run_tc_case(moe, w, hidden_fallback=True)
+
+
+# ---- the down projection's tile height ------------------------------------------------------
+# The host runs the down projection in 192-row tiles when at most (R / 192 + E) row tiles times
+# d_model / 256 column tiles fit one round of the 256 workgroups, and in 256-row tiles
+# otherwise. The cases below sit on both sides of that rule, with groups skewed by a router
+# bias so that some are empty or shorter than one tile and most end in a partial tile.
+
+TILE_CASES = [
+    # (T, d_model, d_ff, E, k, bias std): rows R = T k
+    (3000, 256, 512, 8, 2, 2.0),    # 6000 rows: 39 + 8 row tiles of 192, one column tile
+    (2500, 512, 384, 5, 2, 1.0),    # 5000 rows: (26 + 5) x 2 column tiles of 192 rows
+    (4096, 768, 256, 8, 2, None),   # 8192 rows: (42 + 8) x 3 = 150 tiles of 192 rows
+    (24000, 256, 512, 8, 2, 1.0),   # 48000 rows: 250 + 8 > 256: 256-row tiles
+    (9000, 1024, 256, 8, 2, 0.5),   # 18000 rows: (93 + 8) x 4 > 256: 256-row tiles
+]
+
+
+@pytest.mark.parametrize("c", TILE_CASES, ids=lambda c: f"T{c[0]}-d{c[1]}-E{c[3]}")
+def test_down_projection_tile_height(moe, c):
+    T, d, f, E, k, bias = c
+    w = W.custom(f"tiles-T{T}-d{d}", dtype="bf16", T=T, d=d, f=f, E=E, k=k, bias_std=bias,
+                 seed=(42, 700 + T % 97))
+    run_tc_case(moe, w, hidden_fallback=True)
