@@ -5,8 +5,8 @@
 // Expert outputs o sit in expert-contiguous rows; token t reads its k rows through
 // pos[t, :] and sums them in slot order in fp32, so the result does not depend on
 // scheduling. Expert choice (the Korean page's ExpertChoiceGating dispatch mask):
-// token t finds, per expert, whether that expert chose it by binary search in the
-// expert's ascending token list, and sums the chosen rows in ascending expert order.
+// token t takes, per expert, the row the expert gave it (if any) from the expert's
+// ascending token list, and sums the chosen rows in ascending expert order.
 //
 // Statistics ("Mixture of Experts（MoE）の理論と実装", load_balancing_loss; the Korean
 // page's compute_load_balancing_loss): f_e = count_e / T, p_e = mean_t probs[t, e],
@@ -128,6 +128,107 @@ __global__ __launch_bounds__(256) void combine_ec_kernel(const float* __restrict
   }
 }
 
+// Expert choice, a workgroup per block of kEcCombineTokens consecutive tokens (d_model >= 512).
+// The experts' token lists are ascending, so the block's entries in expert e's list are one
+// run, whose ends the select kernel wrote into the run table (runs[e][b], runs[e][b + 1]): no
+// search. The entries are laid out by (token, expert), and every thread walks that list for
+// its 16-byte column chunks: per token, acc = 0, then acc += score * o[row] in ascending expert
+// order (the same operations, in the same order, as combine_ec_kernel), eight rows' loads
+// issued before they are added. Tokens no expert took get zeros.
+constexpr int kEcTok = kEcCombineTokens;
+
+__global__ __launch_bounds__(256) void combine_ec_block_kernel(const float* __restrict__ o,
+                                                               const int32_t* __restrict__ idx,
+                                                               const float* __restrict__ score,
+                                                               const int32_t* __restrict__ runs,
+                                                               int T, int d, int E, int C,
+                                                               float* __restrict__ y) {
+  __shared__ int run_lo[64], run_hi[64];
+  __shared__ int tab[kEcTok][64];       // row of (token, expert), or -1
+  __shared__ int ftok[kEcTok * 64];     // the block's entries in (token, expert) order
+  __shared__ int frow[kEcTok * 64];
+  __shared__ float fsc[kEcTok * 64];
+  __shared__ int empty_tok[kEcTok];
+  __shared__ int nflat;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kEcTok;
+  const int ntok = min(kEcTok, T - t0);
+
+  // 1. each expert's run of entries in [t0, t0 + ntok), from the select's run table
+  if (tid < E) {
+    const int32_t* r = runs + (size_t)tid * ec_run_stride(T) + blockIdx.x;
+    run_lo[tid] = r[0];
+    run_hi[tid] = r[1];
+  }
+  for (int i = tid; i < kEcTok * 64; i += 256) tab[i >> 6][i & 63] = -1;
+  __syncthreads();
+  // 2. the (token, expert) table: at most ntok entries per expert
+  for (int i = tid; i < E * kEcTok; i += 256) {
+    const int e = i / kEcTok, j = run_lo[e] + i % kEcTok;
+    if (j < run_hi[e]) {
+      const int tl = idx[(size_t)e * C + j] - t0;  // in [0, ntok) by the run table
+      if (tl >= 0 && tl < ntok) tab[tl][e] = e * C + j;
+    }
+  }
+  __syncthreads();
+  // 3. wave 0 compacts the table in (token, expert) order; wave 1 marks the empty tokens
+  if (wave == 0) {
+    int base = 0;
+    const int n = ntok * E;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int tl = i / E, e = i - tl * E;
+      const int r = i < n ? tab[tl][e] : -1;
+      const uint64_t m = __ballot(r >= 0);
+      if (r >= 0) {
+        const int at = base + __popcll(m & ((1ull << lane) - 1ull));
+        ftok[at] = tl;
+        frow[at] = r;
+        fsc[at] = score[r];
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) nflat = base;
+  } else if (wave == 1 && lane < ntok) {
+    int any = 0;
+    for (int e = 0; e < E; ++e) any |= tab[lane][e] >= 0;
+    empty_tok[lane] = !any;
+  }
+  __syncthreads();
+  const int n = nflat, nch = d / 4;
+  for (int c = tid; c < nch; c += 256) {
+    for (int tl = 0; tl < ntok; ++tl)
+      if (empty_tok[tl])
+        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f},
+                                    reinterpret_cast<f32x4*>(y + (size_t)(t0 + tl) * d + 4 * c));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    int cur = -1;
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = j0 + u < n ? __builtin_nontemporal_load(
+                                reinterpret_cast<const f32x4*>(o + (size_t)frow[j0 + u] * d + 4 * c))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= n) break;
+        const int tl = ftok[j0 + u];
+        if (tl != cur) {
+          if (cur >= 0)
+            __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(y + (size_t)(t0 + cur) * d + 4 * c));
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          cur = tl;
+        }
+        const float sc = fsc[j0 + u];
+        acc += sc * v[u];
+      }
+    }
+    if (cur >= 0)
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(y + (size_t)(t0 + cur) * d + 4 * c));
+  }
+}
+
 // per block of kRouterTokens tokens: slot counts per expert and probability sums
 __global__ __launch_bounds__(256) void aux_partials_kernel(const float* __restrict__ probs,
                                                            const int32_t* __restrict__ idx, int T,
@@ -193,9 +294,15 @@ hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w,
   return hipGetLastError();
 }
 
-hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
-                             int E, int C, float* y, hipStream_t s) {
-  combine_ec_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, idx, score, T, d, E, C, y);
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score,
+                             const int32_t* runs, int T, int d, int E, int C, float* y,
+                             hipStream_t s) {
+  // (narrower rows leave most of a block's threads without a column chunk)
+  if (runs && d >= 512)
+    combine_ec_block_kernel<<<ec_run_stride(T) - 1, 256, 0, s>>>(o, idx, score, runs, T, d, E, C,
+                                                                 y);
+  else
+    combine_ec_kernel<<<(T + 3) / 4, 256, 0, s>>>(o, idx, score, T, d, E, C, y);
   return hipGetLastError();
 }
 

@@ -37,13 +37,23 @@ struct RouterArgs {
 // either mode, when blk_zsum is set, the per-block z-loss partials.
 hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t s);
 
+// Tokens per workgroup of the expert-choice combine, and the granularity of the run table
+// the select writes for it.
+constexpr int kEcCombineTokens = 16;
+// Entries per expert of that table: one per block of kEcCombineTokens tokens, plus the end.
+__host__ __device__ inline int ec_run_stride(int T) {
+  return T / kEcCombineTokens + (T % kEcCombineTokens != 0) + 1;  // (no T + 15: T may be 2^31 - 1)
+}
+
 // Expert choice: per expert, softmax over tokens, top-C tokens (ascending token
 // order) and scores. Also writes offsets[e] = e*C for e <= E, counts (optional),
 // src (optional: the token of each row e*C + c, the same list as idx, for the gate/up
-// GEMM's gather), and clears the stream-K flags (optional).
+// GEMM's gather), clears the stream-K flags (optional), and (optional) the run table
+// runs [E, ec_run_stride(T)]: runs[e][b] = entries of expert e's list with token below
+// b * kEcCombineTokens (the last entry, C).
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, int32_t* src,
-                            int32_t* sk_flags, hipStream_t s);
+                            int32_t* sk_flags, int32_t* runs, hipStream_t s);
 
 // Dispatch prefix sum over per-block counts blk_counts [E, nblk] (expert-major):
 // counts[E] (unclamped), offsets[E+1] (group starts; with an expert capacity cap the
@@ -143,8 +153,10 @@ hipError_t launch_gemm_down(int bf16, const void* h, const void* Wdown, const in
 hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w, int T, int d,
                              int k, float* y, hipStream_t s);
 // y[t] = sum over experts e (ascending) that chose t of score[e,c] * o[e*C + c]; else 0.
-hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
-                             int E, int C, float* y, hipStream_t s);
+// runs: the select's run table (nullptr: each token searches the lists itself).
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score,
+                             const int32_t* runs, int T, int d, int E, int C, float* y,
+                             hipStream_t s);
 
 // Per-block counts ([E, nblk]) and probability sums from router outputs (standalone aux loss).
 hipError_t launch_aux_partials(const float* probs, const int32_t* idx, int T, int E, int k,

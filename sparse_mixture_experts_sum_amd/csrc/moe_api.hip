@@ -22,7 +22,7 @@ struct Layout {
   int nblk = 0;
   size_t idx = 0, w = 0, lrank = 0, pos = 0, src = 0, blk_counts = 0, blk_psum = 0, base = 0,
          offsets = 0, counts = 0, logitsT = 0, blk_zsum = 0, x_perm = 0, h = 0, h_lo = 0, o = 0,
-         sk_partial = 0, sk_flags = 0, total = 0;
+         sk_partial = 0, sk_flags = 0, ec_runs = 0, total = 0;
   bool stream_k = false;  // bf16: the GEMMs' stream-K partial slots and flags exist
   bool xperm = false;  // rows copied into x_perm (else the gate/up GEMM gathers them from x)
 };
@@ -141,6 +141,10 @@ Layout make_layout(const moe_shape& s) {
     L.sk_partial = take((size_t)kStreamKSlots * kStreamKSlotBytes);
     L.sk_flags = take((size_t)kStreamKSlots * 4);
   }
+  // expert choice: the select's run table for the combine (entries of each expert's list
+  // before each block of kEcCombineTokens tokens); last, so that the buffers above keep the
+  // offsets they have without it
+  if (!is_tc(s.mode)) L.ec_runs = take((size_t)E * ec_run_stride((int)T) * 4);
   L.total = cur;
   return L;
 }
@@ -307,7 +311,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
                       const float* b_g, const moe_noise* noise, int32_t* idx, float* w,
                       float* probs, int32_t* user_counts, float* z_loss, void* ws,
                       hipStream_t stream, int32_t* select_src = nullptr,
-                      int32_t* sk_flags = nullptr) {
+                      int32_t* sk_flags = nullptr, int32_t* ec_runs = nullptr) {
   const bool want_z = z_loss != nullptr;
   const int bf = s.dtype == MOE_BF16;
   RouterArgs a{};
@@ -344,7 +348,7 @@ moe_status run_router(const moe_shape& s, const Layout& L, const void* x, const 
     MOE_LAUNCH(MOE_STAGE_EC_SELECT,
                launch_ec_select(at<float>(ws, L.logitsT), (int)s.T, s.E, (int)L.C, idx, w, probs,
                                 at<int32_t>(ws, L.offsets), user_counts, select_src, sk_flags,
-                                stream));
+                                ec_runs, stream));
   }
   return MOE_OK;
 }
@@ -492,8 +496,9 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
   // expert choice without row copies: the select writes each row's token and clears the
   // stream-K flags itself, and no permute runs
   const bool ec_direct = !is_tc(s.mode) && !x_perm;
+  int32_t* ec_runs = is_tc(s.mode) ? nullptr : at<int32_t>(ws, L.ec_runs);
   st = run_router(s, L, x, W_g, b_g, noise, idx_b, w_b, probs, counts, z_loss, ws, stream,
-                  ec_direct ? src : nullptr, ec_direct ? sk.flags : nullptr);
+                  ec_direct ? src : nullptr, ec_direct ? sk.flags : nullptr, ec_runs);
   if (st != MOE_OK) return st;
   if (is_tc(s.mode)) {
     st = run_dispatch_tc(s, L, x, idx_b, w_b, counts, f, p, loss, z_loss, x_perm, sk.flags, true,
@@ -514,7 +519,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const void* W_g, c
                                                     w_b, T, d, s.k, y, stream));
     // (f, p, loss and z_loss came out of the dispatch scan)
   } else {
-    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, T, d, E,
+    MOE_LAUNCH(MOE_STAGE_COMBINE, launch_combine_ec(at<float>(ws, L.o), idx_b, w_b, ec_runs, T, d, E,
                                                     (int)L.C, y, stream));
     if (z_loss)
       MOE_LAUNCH(MOE_STAGE_AUX, launch_aux_final(nullptr, nullptr, L.nblk, T, 0, s.k, nullptr,

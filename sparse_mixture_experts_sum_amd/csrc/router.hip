@@ -540,7 +540,8 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
                                                                float* score, float* probs,
                                                                int32_t* offsets, int32_t* counts,
                                                                int32_t* src,
-                                                               int32_t* sk_flags) {
+                                                               int32_t* sk_flags,
+                                                               int32_t* runs) {
   constexpr bool INLDS = PER < 0;
   __shared__ float colsh[INLDS ? kEcLdsTokens : 1];
   __shared__ int whist[kEcWaves][256];
@@ -749,7 +750,11 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
   int out = (int)(base2 >> 32) + min(eq_base, need);
   {
     int eqr = eq_base;
+    const int rstride = ec_run_stride(T);
     each([&](int t, float l) {
+      // entries before token t: the run table's boundary when t starts a combine block
+      if (runs && t % kEcCombineTokens == 0)
+        runs[(size_t)e * rstride + t / kEcCombineTokens] = out;
       const uint32_t key = float_key(l);
       bool take = false;
       if (key > thr) take = true;
@@ -765,6 +770,7 @@ __global__ __launch_bounds__(kEcThreads) void ec_select_kernel(const float* __re
     });
   }
   if (tid == 0) {
+    if (runs) runs[(size_t)e * ec_run_stride(T) + ec_run_stride(T) - 1] = C;
     offsets[e] = e * C;
     if (e == E - 1) offsets[E] = E * C;
     if (counts) counts[e] = C;
@@ -808,18 +814,18 @@ hipError_t launch_router(const RouterArgs& a, int bf16in, int ec, hipStream_t s)
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, int32_t* src,
-                            int32_t* sk_flags, hipStream_t s) {
+                            int32_t* sk_flags, int32_t* runs, hipStream_t s) {
   if (T <= 8 * kEcThreads)
     ec_select_kernel<8><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                 counts, src, sk_flags);
+                                                 counts, src, sk_flags, runs);
   else if (T <= 16 * kEcThreads)
     ec_select_kernel<16><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                  counts, src, sk_flags);
+                                                  counts, src, sk_flags, runs);
   else if (T <= kEcLdsTokens)
     ec_select_kernel<-1><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                  counts, src, sk_flags);
+                                                  counts, src, sk_flags, runs);
   else
     ec_select_kernel<0><<<E, kEcThreads, 0, s>>>(logitsT, T, E, C, idx, score, probs, offsets,
-                                                 counts, src, sk_flags);
+                                                 counts, src, sk_flags, runs);
   return hipGetLastError();
 }

@@ -56,9 +56,10 @@ hipError_t launch_router(const RouterArgs& a, int bf16, int ec, hipStream_t) {
 
 hipError_t launch_ec_select(const float* logitsT, int T, int E, int C, int32_t* idx, float* score,
                             float* probs, int32_t* offsets, int32_t* counts, int32_t* src,
-                            int32_t* sk_flags, hipStream_t) {
+                            int32_t* sk_flags, int32_t* runs, hipStream_t) {
   ++g_launches;
   inside(logitsT, (size_t)E * T * 4, "select logits");
+  inside(runs, (size_t)E * ec_run_stride(T) * 4, "select run table");
   inside(idx, (size_t)E * C * 4, "select idx");
   inside(src, (size_t)E * C * 4, "select src");
   inside(sk_flags, (size_t)kStreamKSlots * 4, "select stream-K flags");
@@ -169,9 +170,11 @@ hipError_t launch_combine_tc(const float* o, const int32_t* pos, const float* w,
   return hipSuccess;
 }
 
-hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score, int T, int d,
-                             int E, int C, float* y, hipStream_t) {
+hipError_t launch_combine_ec(const float* o, const int32_t* idx, const float* score,
+                             const int32_t* runs, int T, int d, int E, int C, float* y,
+                             hipStream_t) {
   ++g_launches;
+  inside(runs, (size_t)E * ec_run_stride(T) * 4, "combine run table");
   inside(o, (size_t)E * C * d * 4, "combine o");
   inside(idx, (size_t)E * C * 4, "combine idx");
   inside(score, (size_t)E * C * 4, "combine scores");

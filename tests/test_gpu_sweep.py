@@ -246,3 +246,27 @@ def test_down_projection_tile_height(moe, c):
     w = W.custom(f"tiles-T{T}-d{d}", dtype="bf16", T=T, d=d, f=f, E=E, k=k, bias_std=bias,
                  seed=(42, 700 + T % 97))
     run_tc_case(moe, w, hidden_fallback=True)
+
+
+# ---- the expert-choice combine by token blocks ----------------------------------------------
+# From d_model 512 on, the expert-choice combine takes 16 consecutive tokens per workgroup and
+# finds each expert's run of them in its token list; the cases cover a partial last block, a
+# single block, experts whose lists skip a block entirely, many experts, and (d_model 256) the
+# per-token kernel below that width.
+
+EC_BLOCK_CASES = [
+    # (T, d_model, d_ff, E, capacity factor, bias std)
+    (1000, 768, 256, 12, 1.3, None),   # 63 blocks, the last one of 8 tokens
+    (17, 512, 128, 3, 2.0, None),      # one full block and one of a single token
+    (2048, 512, 192, 64, 0.5, 1.0),    # 64 experts of 16 tokens: most blocks absent from a list
+    (777, 1024, 128, 5, 4.0, 0.5),     # C = 621 of 777 tokens: most tokens in several lists
+    (300, 256, 128, 6, 1.0, None),     # d_model 256: one wave per token
+]
+
+
+@pytest.mark.parametrize("c", EC_BLOCK_CASES, ids=lambda c: f"T{c[0]}-d{c[1]}-E{c[3]}")
+def test_expert_choice_combine_blocks(moe, c):
+    T, d, f, E, cf, bias = c
+    w = W.custom(f"ecblk-T{T}-d{d}", dtype="bf16", T=T, d=d, f=f, E=E, k=1, mode="ec", cf=cf,
+                 bias_std=bias, seed=(42, 800 + T % 89))
+    run_ec_case(moe, w)
