@@ -270,3 +270,33 @@ def test_expert_choice_combine_blocks(moe, c):
     w = W.custom(f"ecblk-T{T}-d{d}", dtype="bf16", T=T, d=d, f=f, E=E, k=1, mode="ec", cf=cf,
                  bias_std=bias, seed=(42, 800 + T % 89))
     run_ec_case(moe, w)
+
+
+# ---- repeated calls and a reused workspace on the two paths above ---------------------------
+# A second call gives the same bits, and a call that reuses the workspace of a larger call
+# (whose run table, rows and tiles are still there) gives the bits of a call with a fresh one.
+
+def _layer(moe, dev, w, **kw):
+    return moe.moe_forward(dev["x"], dev["Wg"], dev["b"], dev["Wgate"], dev["Wup"], dev["Wdown"],
+                           **kw)
+
+
+@pytest.mark.parametrize("mode", ["ec", "tc"])
+def test_block_combine_and_192_tiles_repeat_and_reuse_workspace(moe, mode):
+    import torch
+    from tests import parity as PR
+    kw = dict(mode="ec", capacity_factor=1.3, want_stats=False) if mode == "ec" else dict(k=2)
+    big = W.custom(f"reuse-big-{mode}", dtype="bf16", T=1000, d=768, f=256, E=12,
+                   k=1 if mode == "ec" else 2, mode=mode, cf=1.3, seed=(42, 611))
+    small = W.custom(f"reuse-small-{mode}", dtype="bf16", T=333, d=768, f=256, E=12,
+                     k=1 if mode == "ec" else 2, mode=mode, cf=1.3, bias_std=0.7, seed=(42, 612))
+    dev_b = PR.device_inputs(W.make_inputs(big), big)
+    dev_s = PR.device_inputs(W.make_inputs(small), small)
+    first = _layer(moe, dev_b, big, **kw)
+    again = _layer(moe, dev_b, big, workspace=first["workspace"], **kw)
+    fresh = _layer(moe, dev_s, small, **kw)
+    reused = _layer(moe, dev_s, small, workspace=first["workspace"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(first["y"], again["y"])
+    assert torch.equal(fresh["y"], reused["y"])
+    assert torch.equal(fresh["idx"], reused["idx"])
