@@ -241,6 +241,61 @@ def reference_gemm(torch, w, group_rows, steps, warmup, gu_ms, dn_ms):
     return res
 
 
+def one_expert_gemm(torch, M, w, steps, warmup, rows=4096):
+    """The grouped GEMMs on a regular problem, against torch's bf16 matmul (hipBLASLt) on
+    operands of the same sizes: a layer with one expert and `rows` tokens at the workload's
+    d_model and d_ff (every token routed to it), its gate/up and down stages timed with the
+    library's per-stage events; torch: x [rows, d] times [W_gate | W_up] [d, 2 d_ff] (no SwiGLU
+    epilogue) and h [rows, d_ff] times W_down [d_ff, d]. Medians over the steps."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(0)
+    T, d, f = rows, w.d, w.f
+    x = torch.randn(T, d, device=dev, generator=g).to(torch.bfloat16)
+    Wg = torch.zeros(d, 1, device=dev, dtype=torch.bfloat16)
+    Wgate = (torch.randn(1, d, f, device=dev, generator=g) * 0.01).to(torch.bfloat16)
+    Wup = (torch.randn(1, d, f, device=dev, generator=g) * 0.01).to(torch.bfloat16)
+    Wdown = (torch.randn(1, f, d, device=dev, generator=g) * 0.01).to(torch.bfloat16)
+    out = M.moe_forward(x, Wg, None, Wgate, Wup, Wdown, k=1, want_stats=False)
+    ws, y = out["workspace"], out["y"]
+    for _ in range(warmup):
+        M.moe_forward(x, Wg, None, Wgate, Wup, Wdown, k=1, y=y, workspace=ws, want_stats=False)
+    torch.cuda.synchronize()
+    M.profile_enable(True)
+    M.profile_read()
+    for _ in range(steps):
+        M.moe_forward(x, Wg, None, Wgate, Wup, Wdown, k=1, y=y, workspace=ws, want_stats=False)
+    torch.cuda.synchronize()
+    st = M.profile_read()
+    M.profile_enable(False)
+    res = {"rows": T, "d_model": d, "d_ff": f}
+    h = torch.randn(T, f, device=dev, generator=g).to(torch.bfloat16)
+    Wgu = torch.cat([Wgate[0], Wup[0]], 1).contiguous()
+    o1 = torch.empty(T, 2 * f, device=dev, dtype=torch.bfloat16)
+    o2 = torch.empty(T, d, device=dev, dtype=torch.bfloat16)
+    for name, stage, fn, flop in (
+            ("gate_up", "gemm_gate_up", lambda: torch.matmul(x, Wgu, out=o1), 4.0 * d * f * T),
+            ("down", "gemm_down", lambda: torch.matmul(h, Wdown[0], out=o2), 2.0 * f * d * T)):
+        ours = st[stage][0] / max(st[stage][1], 1)
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, z in ev:
+            a.record()
+            fn()
+            z.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(z) for a, z in ev]))
+        res[name] = {"ours_us": round(ours * 1e3, 1),
+                     "ours_tflops": round(flop / (ours * 1e-3) / 1e12, 1),
+                     "torch_us": round(ms * 1e3, 1),
+                     "torch_tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    res["what"] = ("one expert, every token routed to it; ours: per-stage events (mean over the "
+                   "steps), torch.matmul bf16: median; gate/up without the SwiGLU epilogue in torch")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +320,9 @@ def main():
                     help="after the layer, time a plain streaming read of x (torch.sum over its "
                          "bf16 values, fp32 result) placed where the router runs: right after a "
                          "layer call, repeated; the read rate x allows in that cache state")
+    ap.add_argument("--one-expert-gemm", action="store_true",
+                    help="also time the GEMMs on a one-expert layer of 4096 tokens against "
+                         "torch's bf16 matmul on operands of the same sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB read + 256 MiB write kernel (for HBM counter scaling)")
     args = ap.parse_args()
@@ -425,6 +483,8 @@ def main():
         line["reference_gemm"] = reference_gemm(torch, w, counts if w.mode != "ec" else
                                                 np.full(w.E, w.capacity), args.steps, args.warmup,
                                                 gu_ms, dn_ms)
+    if args.one_expert_gemm and w.dtype == "bf16":
+        line["one_expert_gemm"] = one_expert_gemm(torch, M, w, args.steps, args.warmup)
     if args.variant != "plain":
         line["config"]["variant"] = args.variant
         if args.variant == "capacity":
