@@ -388,12 +388,16 @@ struct TileCoord {
 
 // How the tiles are dealt to the eight XCDs (each XCD runs 32 at a time, one per CU).
 //  - Columns (groups with many tiles, N-tiles a multiple of 8): the groups are processed one
-//    after another by all XCDs together; XCD x owns the x-th eighth of each group's output
-//    columns (NX = NT / 8 N-tiles) for all of the group's rows, and walks that rectangle in
-//    column blocks of GN N-tiles, rows outer and the block's columns inner. The 32 tiles an
-//    XCD runs together then cover about 32 / GN row tiles x GN column tiles, so they share
-//    both their rows and their weight columns in the XCD's L2 (about 32 / GN + GN tile
-//    operands fetched per 32 tiles, against 33 for one column of 32 row tiles).
+//    after another by all XCDs together. The XCDs form RP row groups x 8 / RP column groups
+//    (RP = 1 or 2): XCD x owns the (x % (8 / RP))-th column group's share of each group's
+//    output columns (NX = NT * RP / 8 N-tiles) for the row tiles r of the group with
+//    r % RP = (x / (8 / RP) + e) % RP, and walks that rectangle in column blocks of GN
+//    N-tiles, rows outer and the block's columns inner. The 32 tiles an XCD runs together
+//    then cover about 32 / GN row tiles x GN column tiles, so they share both their rows and
+//    their weight columns in the XCD's L2 (about 32 / GN + GN tile operands fetched per 32
+//    tiles, against 33 for one column of 32 row tiles). Over the whole launch every row tile
+//    is fetched by the 8 / RP XCDs of its row group and every weight column by RP XCDs: the
+//    launch picks RP = 2 where that fetches less (rows and weights of about the same size).
 //  - Split (groups with many tiles, N-tiles not a multiple of 8; tiles listed
 //    N-tile-major): XCD x takes the x-th eighth of each group's list, i.e. mostly its own
 //    slice of the group's weight columns, for all of the group's rows.
@@ -419,16 +423,22 @@ struct TileMap {
   int nx, gn;    // columns order: N-tiles per XCD and per column block (gn = 0: split order)
 };
 
+// Row tiles r < mte with r % rp = s: this XCD's share of a group in the columns order.
+__device__ __forceinline__ int row_share(int mte, int rp, int s) {
+  return mte > s ? (mte - 1 - s) / rp + 1 : 0;
+}
+
 // CONTIG_OK: the shape allows the contiguous order (a group of one M-tile has NT tiles,
 // so NT at or above the threshold rules it out; the launch picks the instantiation).
-template <int BM, bool CONTIG_OK>
+template <int BM, bool CONTIG_OK, int RP>
 __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, int NT, int xcd,
                                                  bool gathered, int gn) {
+  constexpr int rp = RP;
   TileMap m;
   m.NT = NT;
   m.xcd = xcd;
   m.E = E;
-  m.nx = NT / kXcds;
+  m.nx = NT / (kXcds / rp);
   m.gn = gn;
   long long total = 0, maxpe = 0;
   int split_total = 0, col_total = 0;
@@ -440,7 +450,8 @@ __device__ __forceinline__ TileMap make_tile_map(const int32_t* offsets, int E, 
       maxpe = pe > maxpe ? pe : maxpe;
     }
     split_total += (int)((pe * (xcd + 1)) >> 3) - (int)((pe * xcd) >> 3);
-    col_total += mte * m.nx;
+    if constexpr (RP == 1) col_total += mte * m.nx;
+    else col_total += row_share(mte, RP, (xcd / (kXcds / RP) + e) % RP) * m.nx;
   }
   // (contiguous: every group has fewer than 48 tiles, so the whole list fits an int)
   m.contiguous = CONTIG_OK && maxpe < (gathered ? kContigGatherTiles
@@ -466,12 +477,15 @@ struct TileCursor {
   int plo;      // split order: first of the group's tiles that this XCD takes
 };
 
-template <int BM, bool CONTIG>
+// RP: row groups of the columns order (see TileMap)
+template <int BM, bool CONTIG, int RP>
 __device__ __forceinline__ void cursor_load(TileCursor& c, const int32_t* offsets, const TileMap& m) {
   c.mte = (offsets[c.e + 1] - offsets[c.e] + BM - 1) / BM;
   if constexpr (CONTIG) {
     c.pe = c.mte * m.NT;
   } else if (m.gn > 0) {
+    if constexpr (RP > 1)  // this XCD's row tiles of the group
+      c.mte = row_share(c.mte, RP, (m.xcd / (kXcds / RP) + c.e) % RP);
     c.pe = c.mte * m.nx;
   } else {
     const long long pe = (long long)c.mte * m.NT;
@@ -480,20 +494,20 @@ __device__ __forceinline__ void cursor_load(TileCursor& c, const int32_t* offset
   }
 }
 
-template <int BM, bool CONTIG>
+template <int BM, bool CONTIG, int RP>
 __device__ __forceinline__ TileCursor make_cursor(const int32_t* offsets, const TileMap& m) {
   TileCursor c;
   c.e = 0;
   c.acc = 0;
   c.plo = 0;
-  cursor_load<BM, CONTIG>(c, offsets, m);
+  cursor_load<BM, CONTIG, RP>(c, offsets, m);
   return c;
 }
 
 // Tile i of this XCD's share (see TileMap); i at or after the cursor's group, which the
 // call advances. CONTIG = m.contiguous, fixed at compile time so that the split order's
 // stream carries no code of the other.
-template <int BM, bool CONTIG>
+template <int BM, bool CONTIG, int RP>
 __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, const TileMap& m,
                                                  int bn_out, TileCursor& c) {
   const int gi = CONTIG ? m.base + i : i;
@@ -501,7 +515,7 @@ __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, 
   while (gi >= c.acc + c.pe && c.e < m.E - 1) {
     c.acc += c.pe;
     ++c.e;
-    cursor_load<BM, CONTIG>(c, offsets, m);
+    cursor_load<BM, CONTIG, RP>(c, offsets, m);
   }
   const int e = c.e, mte = c.mte;
   TileCoord t;
@@ -514,9 +528,16 @@ __device__ __forceinline__ TileCoord locate_tile(int i, const int32_t* offsets, 
     const int r = q - g * mte * m.gn;
     const int wg = min(m.gn, m.nx - g * m.gn);
     const int mtl = r / wg;
-    t.row0 = offsets[e] + mtl * BM;
-    t.rows = min(BM, offsets[e + 1] - t.row0);
-    t.n0 = (m.xcd * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
+    if constexpr (RP == 1) {
+      t.row0 = offsets[e] + mtl * BM;
+      t.rows = min(BM, offsets[e + 1] - t.row0);
+      t.n0 = (m.xcd * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
+    } else {
+      const int rg = m.xcd / (kXcds / RP), cg = m.xcd % (kXcds / RP);
+      t.row0 = offsets[e] + (mtl * RP + (rg + e) % RP) * BM;
+      t.rows = min(BM, offsets[e + 1] - t.row0);
+      t.n0 = (cg * m.nx + g * m.gn + (r - mtl * wg)) * bn_out;
+    }
     return t;
   }
   // split: position p of the group's N-tile-major list; contiguous: the same, from the
@@ -959,7 +980,7 @@ __device__ __forceinline__ void store_tile_sum(const GemmArgs& a, const TileCoor
 // (The next item's fragments are read after the epilogue: holding them through it would
 // leave too few registers.)
 // (TR: rows of the grouped problem per tile; TAG: see k_loop)
-template <class G, bool SWIGLU, bool SPLIT, int TR, int BNL, bool CONTIG, int TAG>
+template <class G, bool SWIGLU, bool SPLIT, int TR, int BNL, bool CONTIG, int RP, int TAG>
 __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm, int slot,
                                             int nslot, int wave, int wm, int wn, int nk,
                                             char* const (&ring)[G::STAGES]) {
@@ -974,8 +995,8 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
   int ln = fresh_lane();
   int a_frag[G::MB], b_frag[G::NBW];
   frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
-  TileCursor cur_c = make_cursor<TR, CONTIG>(a.offsets, tm);
-  TileCoord t = locate_tile<TR, CONTIG>(cur.tile, a.offsets, tm, G::BN_OUT, cur_c);
+  TileCursor cur_c = make_cursor<TR, CONTIG, RP>(a.offsets, tm);
+  TileCoord t = locate_tile<TR, CONTIG, RP>(cur.tile, a.offsets, tm, G::BN_OUT, cur_c);
   int gv[G::A_PW] = {};
   if (SWIGLU && a.gather) gather_rows<G>(gather_fetch<G>(a, t, ln, wave), ln, gv);
   StageLoader<G, SWIGLU, SPLIT> ld =
@@ -1003,7 +1024,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
     Item nx = cur;
     const bool has_next = next_item(it, sp, slot, nslot, nk, nx);
     const TileCoord tn =
-        has_next ? locate_tile<TR, CONTIG>(nx.tile, a.offsets, tm, G::BN_OUT, cur_c) : t;
+        has_next ? locate_tile<TR, CONTIG, RP>(nx.tile, a.offsets, tm, G::BN_OUT, cur_c) : t;
     // gathered rows: the next tile's row indices, fetched now so that the load is long
     // complete when they are needed (a vector load completes in order with the ring's
     // loads; one issued just before its use would wait for all of them)
@@ -1049,7 +1070,7 @@ __device__ __forceinline__ void pipe_stream(const GemmArgs& a, const TileMap& tm
   wait_vmcnt<0>();
 }
 
-template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK>
+template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW, bool CONTIG_OK, int RP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void gemm_bf16_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ gather, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, const int32_t* __restrict__ offsets, int E, int K, int N, int lo_rows,
@@ -1078,7 +1099,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int NT = N / G::BN_OUT;
   const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
   // this XCD's tiles (the order is described at TileMap)
-  const TileMap tm = make_tile_map<TR, CONTIG_OK>(offsets, E, NT, xcd, gather != nullptr, gn);
+  const TileMap tm = make_tile_map<TR, CONTIG_OK, RP>(offsets, E, NT, xcd, gather != nullptr, gn);
+  // (one instantiation of the shared helpers per kernel: see k_loop)
+  constexpr int TAG = (CONTIG_OK ? 1 : 0) + 2 * (RP - 1);
   const int my_total = tm.my_total;
   const int nk = K / G::BK;
   const int nk_total = nk;
@@ -1092,23 +1115,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   if constexpr (PIPE) {
     if (nk_total % G::STAGES == 0 && nk_total >= 2 * G::STAGES) {
       if (CONTIG_OK && tm.contiguous)
-        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, CONTIG_OK, CONTIG_OK>(args, tm, slot, nslot, wave,
-                                                                     wm, wn, nk, ring);
+        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, CONTIG_OK, RP, TAG>(args, tm, slot, nslot, wave,
+                                                                   wm, wn, nk, ring);
       else
-        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, false, CONTIG_OK>(args, tm, slot, nslot, wave, wm,
-                                                                 wn, nk, ring);
+        pipe_stream<G, SWIGLU, SPLIT, TR, BNL, false, RP, TAG>(args, tm, slot, nslot, wave, wm,
+                                                               wn, nk, ring);
       return;
     }
   }
-  TileCursor cur_c = make_cursor<TR, false>(offsets, tm);
-  TileCursor cur_cc = make_cursor<TR, CONTIG_OK>(offsets, tm);
+  TileCursor cur_c = make_cursor<TR, false, RP>(offsets, tm);
+  TileCursor cur_cc = make_cursor<TR, CONTIG_OK, RP>(offsets, tm);
   for (int i = slot; i < my_total; i += nslot) {
     const int ln = fresh_lane();
     int a_frag[G::MB], b_frag[G::NBW];
     frag_offsets<G, SWIGLU, BNL>(ln, wm, wn, a_frag, b_frag);
     const TileCoord t = CONTIG_OK && tm.contiguous
-                            ? locate_tile<TR, CONTIG_OK>(i, offsets, tm, G::BN_OUT, cur_cc)
-                            : locate_tile<TR, false>(i, offsets, tm, G::BN_OUT, cur_c);
+                            ? locate_tile<TR, CONTIG_OK, RP>(i, offsets, tm, G::BN_OUT, cur_cc)
+                            : locate_tile<TR, false, RP>(i, offsets, tm, G::BN_OUT, cur_c);
     int gv[G::A_PW] = {};
     if (SWIGLU && args.gather) gather_rows<G>(gather_fetch<G>(args, t, ln, wave), ln, gv);
     const StageLoader<G, SWIGLU, SPLIT> ld = make_loader<G, SWIGLU, SPLIT, BNL>(args, t, ln, wave, nk, 0, gv);
@@ -1116,7 +1139,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     zero_acc<G>(acc);
 
     // (the pipelined layout falls back to the plain ring when its stream does not apply)
-    k_loop<G, SWIGLU, SPLIT, CONTIG_OK>(nk_total, ring, ld, a_frag, b_frag, acc);
+    k_loop<G, SWIGLU, SPLIT, TAG>(nk_total, ring, ld, a_frag, b_frag, acc);
 
     store_tile<G, SWIGLU, SPLIT>(args, t, ln, wm, wn, acc);
     // stores retired and every wave past its last stage read before the next tile's
@@ -1205,43 +1228,63 @@ int device_cu_count() {
 // A/B in one process): widths 3 to 7 within 1% of each other, 4 the best, all 4-5% faster
 // than the split order; NX = 2 (its down projection): width 2 is 2% faster than 1 or split.
 // NX columns are cut into round(NX / 4) blocks.
-int column_block(int NT) {
+int column_block(int NT, int rp) {
   if (NT % kXcds != 0) return 0;
-  const int nx = NT / kXcds;
+  const int nx = NT * rp / kXcds;
   const int nblocks = nx < 6 ? 1 : (nx + 2) / 4;
   return (nx + nblocks - 1) / nblocks;
 }
 
+// Row groups of the columns order (1 or 2). Every row tile is fetched by the 8 / RP XCDs of its
+// row group and every weight column by RP XCDs, so about RP * W + (8 / RP) * A elements move
+// beyond L2 (A: the rows, rows x K; W: the weights, E x K x N); two row groups fetch less when
+// W < 4 A. Measured on a one-expert down projection of 4096 rows, K = 14336, N = 4096 (rows
+// and weights alike): one row group fetched 9 times the rows' bytes, which the model gives.
+int row_groups(int NT, long long rows, int K, int N, int E) {
+  if (NT % kXcds != 0) return 1;
+  const double A = (double)rows * K, W = (double)E * K * N;
+  return W < 4.0 * A ? 2 : 1;
+}
+
+// rows: the grouped problem's rows (at most), for the choice of row groups
 template <int BM, int BNL, bool SWIGLU, bool SPLIT, int NW>
 hipError_t launch_bf16(const void* A, const int32_t* gather, const void* B0, const void* B1,
-                       const int32_t* offsets, int E, int K, int N, void* out, void* out2,
-                       int lo_rows, const StreamK& sk, hipStream_t s) {
+                       const int32_t* offsets, int E, long long rows, int K, int N, void* out,
+                       void* out2, int lo_rows, const StreamK& sk, hipStream_t s) {
   const int grid = ((device_cu_count() + 7) / 8) * 8;
   // a non-empty group has at least N / BN_OUT tiles: the contiguous order is possible
   // only below the threshold (kernels for wider outputs are built without it; split-order
   // shapes between kContigTiles and kContigSplitTiles column tiles forgo it)
   const int NT = N / (SWIGLU ? BNL / 2 : BNL);
-  const int gn = column_block(NT);
-  if (NT < (gather ? kContigGatherTiles : kContigTiles))
-    gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, true><<<grid, 64 * NW, 0, s>>>(
-        static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, lo_rows, out, out2, gn, sk.partial, sk.flags);
-  else
-    gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, false><<<grid, 64 * NW, 0, s>>>(
-        static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),
-        static_cast<const bf16*>(B1), offsets, E, K, N, lo_rows, out, out2, gn, sk.partial, sk.flags);
+  // (two row groups only for plain-row down projections too wide for the contiguous order:
+  // the only kernels built with them)
+  const int rp = !SWIGLU && !SPLIT && NT >= kContigTiles ? row_groups(NT, rows, K, N, E) : 1;
+  const int gn = column_block(NT, rp);
+#define MOE_GEMM_BF16(CONTIG, RPV)                                                              \
+  gemm_bf16_kernel<BM, BNL, SWIGLU, SPLIT, NW, CONTIG, RPV><<<grid, 64 * NW, 0, s>>>(             \
+      static_cast<const bf16*>(A), gather, static_cast<const bf16*>(B0),                          \
+      static_cast<const bf16*>(B1), offsets, E, K, N, lo_rows, out, out2, gn, sk.partial, sk.flags)
+  if (NT < (gather ? kContigGatherTiles : kContigTiles)) {
+    MOE_GEMM_BF16(true, 1);
+  } else if constexpr (!SWIGLU && !SPLIT) {
+    if (rp == 2) MOE_GEMM_BF16(false, 2);
+    else MOE_GEMM_BF16(false, 1);
+  } else {
+    MOE_GEMM_BF16(false, 1);
+  }
+#undef MOE_GEMM_BF16
   return hipGetLastError();
 }
 
 template <bool SPLIT>
 hipError_t gateup_bf16(const void* xp, const int32_t* gather, const void* Wgate, const void* Wup,
-                       const int32_t* offsets, int E, int d, int f, void* h, void* h_lo,
-                       const StreamK& sk, hipStream_t s) {
+                       const int32_t* offsets, int E, int R_max, int d, int f, void* h,
+                       void* h_lo, const StreamK& sk, hipStream_t s) {
   if (f % 128 == 0)
-    return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo,
-                                                 0, sk, s);
-  return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo,
-                                               0, sk, s);
+    return launch_bf16<256, 256, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, R_max, d, f, h,
+                                                 h_lo, 0, sk, s);
+  return launch_bf16<256, 128, true, SPLIT, 4>(xp, gather, Wgate, Wup, offsets, E, R_max, d, f, h,
+                                               h_lo, 0, sk, s);
 }
 
 // Whether the down projection of up to R_max rows in E groups fits one round of the
@@ -1258,16 +1301,18 @@ bool down_fits_192(long long R_max, int E, int d) {
 template <bool PAIRED>
 hipError_t down_bf16(const void* h, const void* Wdown, const int32_t* offsets, int E, int R_max,
                      int f, int d, float* o, int lo_rows, const StreamK& sk, hipStream_t s) {
+  // (the paired tiles read each row and its residual row)
+  const long long rows = PAIRED ? 2LL * R_max : R_max;
   if (!PAIRED && d % 256 == 0 && down_fits_192(R_max, E, d))
-    return launch_bf16<192, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+    return launch_bf16<192, 256, false, false, 4>(h, nullptr, Wdown, nullptr, offsets, E, rows, f, d,
                                                   o, nullptr, 0, sk, s);
   if (d % 256 == 0)
-    return launch_bf16<256, 256, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+    return launch_bf16<256, 256, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, rows, f, d,
                                                    o, nullptr, lo_rows, sk, s);
   if (d % 128 == 0)
-    return launch_bf16<256, 128, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d,
+    return launch_bf16<256, 128, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, rows, f, d,
                                                    o, nullptr, lo_rows, sk, s);
-  return launch_bf16<256, 64, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, f, d, o,
+  return launch_bf16<256, 64, false, PAIRED, 4>(h, nullptr, Wdown, nullptr, offsets, E, rows, f, d, o,
                                                 nullptr, lo_rows, sk, s);
 }
 
@@ -1277,8 +1322,9 @@ hipError_t launch_gemm_gateup(int bf16in, const void* xp, const int32_t* gather,
                               const void* Wup, const int32_t* offsets, int E, int R_max, int d,
                               int f, void* h, void* h_lo, const StreamK& sk, hipStream_t s) {
   if (bf16in) {
-    if (h_lo) return gateup_bf16<true>(xp, gather, Wgate, Wup, offsets, E, d, f, h, h_lo, sk, s);
-    return gateup_bf16<false>(xp, gather, Wgate, Wup, offsets, E, d, f, h, nullptr, sk, s);
+    if (h_lo)
+      return gateup_bf16<true>(xp, gather, Wgate, Wup, offsets, E, R_max, d, f, h, h_lo, sk, s);
+    return gateup_bf16<false>(xp, gather, Wgate, Wup, offsets, E, R_max, d, f, h, nullptr, sk, s);
   }
   if (gather) return hipErrorInvalidValue;  // the fp32 path reads copied rows
   dim3 grid(f / 64, R_max / 64 + E);

@@ -300,3 +300,25 @@ def test_block_combine_and_192_tiles_repeat_and_reuse_workspace(moe, mode):
     assert torch.equal(first["y"], again["y"])
     assert torch.equal(fresh["y"], reused["y"])
     assert torch.equal(fresh["idx"], reused["idx"])
+
+
+# ---- two row groups in the down projection's columns order ---------------------------------
+# With 16 or more output column tiles (d_model >= 4096) and weights smaller than four times
+# the rows (E * d_model < 4 * rows), the down projection's XCDs split a group's row tiles in
+# two and its columns in four. Cases: 256-row tiles, 192-row tiles (one round), and 256-row
+# tiles whose last round is split along K (d_ff 8192: stream-K).
+
+ROW_GROUP_CASES = [
+    # (T, d_model, d_ff, E, k, bias std)
+    (1500, 4096, 256, 2, 2, 0.5),    # 3000 rows: 17 x 16 tiles of 256 rows
+    (2400, 4096, 256, 2, 1, None),   # 2400 rows: 14 x 16 tiles of 192 rows, one round
+    (1500, 4096, 8192, 2, 2, 0.5),   # stream-K in the last round
+]
+
+
+@pytest.mark.parametrize("c", ROW_GROUP_CASES, ids=lambda c: f"T{c[0]}-f{c[2]}-k{c[4]}")
+def test_down_projection_two_row_groups(moe, c):
+    T, d, f, E, k, bias = c
+    w = W.custom(f"rowgroups-T{T}-f{f}", dtype="bf16", T=T, d=d, f=f, E=E, k=k, bias_std=bias,
+                 seed=(42, 650 + T % 83))
+    run_tc_case(moe, w, hidden_fallback=True)
