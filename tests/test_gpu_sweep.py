@@ -322,3 +322,29 @@ def test_down_projection_two_row_groups(moe, c):
     w = W.custom(f"rowgroups-T{T}-f{f}", dtype="bf16", T=T, d=d, f=f, E=E, k=k, bias_std=bias,
                  seed=(42, 650 + T % 83))
     run_tc_case(moe, w, hidden_fallback=True)
+
+
+# Groups whose rows run just past a whole number of 256-row tiles (the last row tile holds 1,
+# 64 or 65 rows). With E = 2 and k = 2 every token goes to both experts, so each group has
+# exactly T rows. Cases: gate/up and the 192-row down projection of small layers, the down
+# projection in 256-row tiles (d_model 4096) with and without stream-K, and a skewed
+# 16-expert mix.
+BOUNDARY_CASES = [
+    # (T, d_model, d_ff, E, k, bias std)
+    (257, 256, 512, 2, 2, None),
+    (320, 1024, 512, 2, 2, None),
+    (321, 1024, 512, 2, 2, None),
+    (576, 512, 1024, 2, 2, None),
+    (1537, 4096, 256, 2, 2, None),
+    (1600, 4096, 256, 2, 2, None),
+    (1600, 4096, 8192, 2, 2, None),
+    (3000, 1024, 1408, 16, 2, 0.3),
+]
+
+
+@pytest.mark.parametrize("c", BOUNDARY_CASES, ids=lambda c: f"T{c[0]}-d{c[1]}-f{c[2]}-E{c[3]}")
+def test_groups_just_past_a_tile_boundary(moe, c):
+    T, d, f, E, k, bias = c
+    w = W.custom(f"boundary-T{T}-d{d}-f{f}-E{E}", dtype="bf16", T=T, d=d, f=f, E=E, k=k,
+                 bias_std=bias, seed=(42, 700 + T % 97))
+    run_tc_case(moe, w, hidden_fallback=True)
